@@ -1,0 +1,290 @@
+"""Decode driver of the oracle: batch intake, ubatches, KV cells, layer loop.
+
+TEST INFRASTRUCTURE: imported only by tests, smoke() and bench.py's
+cpu_baseline leg.
+
+What one ``decode(batch)`` call does, in the pages' order:
+
+1. Validate the batch and fill absent fields (llama.cpp walkthrough,
+   "Step 10: forming the batch for one call"): every token id in
+   [0, n_vocab); absent sequence ids mean sequence 0; absent positions
+   continue each sequence from ``seq_pos_max(s) + 1`` in batch order; absent
+   output flags select the last token only, or every token when
+   ``output_all``.
+2. Split the batch into consecutive ubatches of at most ``n_ubatch`` tokens,
+   processed in order ("Steps 11-12: running the batch through the model").
+3. Place each ubatch's tokens in KV cells and record (position, sequences)
+   per cell (Ollama engine page, "KV Cache: memory for causal attention":
+   find contiguous cache slots, store K/V, build the mask).
+4. Run the forward pass over the ubatch (Ollama engine page, "Deep dive: the
+   Llama forward pass in Go"): embedding, then per layer attention RMSNorm,
+   Q/K/V, RoPE, attention over the cached cells, output projection and
+   residual; in the last layer keep only the rows whose logits are wanted
+   before the MLP; MLP RMSNorm, SwiGLU, down projection and residual; then
+   output RMSNorm and the LM head.
+5. Collect one logits row per flagged token in batch order ("Steps 14-15:
+   logits in the buffer and choosing the next token"), and the greedy token
+   (temperature 0 -> argmax; Ollama engine page, "Token sampling pipeline").
+
+Readings where the pages are silent or inconsistent:
+* Return codes: 0 success; 1 the batch could not be placed (fewer free cells
+  than tokens), nothing changed; -1 invalid input, nothing changed.
+* ``n_batch = min(n_ctx, n_batch)``, ``n_ubatch = min(n_batch, n_ubatch)``
+  ("Step 7: creating the inference context"); a batch larger than n_batch is
+  invalid.  At most 64 sequences (one bit each in a cell's sequence mask).
+* Explicit positions must be >= 0 and greater than every earlier position of
+  each of the token's sequences (cache and batch), so no two live cells share
+  (sequence, position) and each sequence's cells are position-ordered.
+* Cell placement: the first run of T consecutive free cells scanning from
+  cell 0; if there is none, the T lowest-index free cells.  Token i of the
+  ubatch goes to the i-th chosen cell.
+* A token attends to the occupied cells whose sequence set holds the token's
+  first sequence id and whose position is <= the token's position; this
+  includes itself and earlier tokens of its own ubatch.  Cached K is stored
+  after RoPE.
+* Logits: one row per flagged token, in batch order, accumulated over the
+  ubatches of the call.  Greedy ties go to the lowest index.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+from .model import OracleModel, widen
+from .ops import attend, rms_norm, rope, swiglu_mlp
+
+OK, NO_SLOT, INVALID = 0, 1, -1
+MAX_SEQ = 64
+
+
+@dataclass
+class DecodeResult:
+    status: int
+    positions: List[int] = field(default_factory=list)
+    seq_ids: List[List[int]] = field(default_factory=list)
+    output_flags: List[bool] = field(default_factory=list)
+    ubatches: List[range] = field(default_factory=list)
+    slots: List[int] = field(default_factory=list)      # cell of each token, batch order
+    out_index: List[int] = field(default_factory=list)  # batch indices that have logits
+    logits: Optional[np.ndarray] = None                 # [n_out, n_vocab] float64
+    tokens: Optional[np.ndarray] = None                 # greedy id per output row
+
+    def logits_ith(self, i: int) -> Optional[np.ndarray]:
+        if self.logits is None or i not in self.out_index:
+            return None
+        return self.logits[self.out_index.index(i)]
+
+
+def _round_storage(a: np.ndarray, dtype: Optional[str]) -> np.ndarray:
+    """Optional diagnosis switch: round stored K/V to the cache's type."""
+    if dtype is None or dtype == "f64":
+        return a
+    if dtype == "f32":
+        return a.astype(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return a.astype(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        f = a.astype(np.float32)
+        u = f.view(np.uint32)
+        u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+        return u.view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+class OracleContext:
+    def __init__(self, model: Optional[OracleModel], n_ctx: int, n_batch: Optional[int] = None,
+                 n_ubatch: int = 512, n_seq_max: int = 1, output_all: bool = False,
+                 compute: bool = True, kv_round: Optional[str] = None):
+        if n_ctx <= 0 or n_seq_max < 1 or n_seq_max > MAX_SEQ:
+            raise ValueError("invalid context parameters")
+        self.model = model
+        self.hp = model.hp if model is not None else None
+        self.n_ctx = int(n_ctx)
+        nb = self.n_ctx if n_batch is None else int(n_batch)
+        self.n_batch = min(self.n_ctx, nb)
+        self.n_ubatch = min(self.n_batch, int(n_ubatch))
+        if self.n_batch <= 0 or self.n_ubatch <= 0:
+            raise ValueError("invalid batch sizes")
+        self.n_seq_max = int(n_seq_max)
+        self.output_all = bool(output_all)
+        self.compute = compute and model is not None
+        self.kv_round = kv_round
+        self.cell_pos = np.full(self.n_ctx, -1, dtype=np.int64)   # -1 = free
+        self.cell_seq = np.zeros(self.n_ctx, dtype=np.uint64)     # bit s = belongs to seq s
+        self.k_cache: dict = {}
+        self.v_cache: dict = {}
+
+    # ---- bookkeeping ------------------------------------------------------
+
+    def clear(self) -> None:
+        self.cell_pos[:] = -1
+        self.cell_seq[:] = 0
+        self.k_cache.clear()
+        self.v_cache.clear()
+
+    def seq_pos_max(self, s: int) -> int:
+        """Largest position held by sequence s, or -1 if it has no cell."""
+        m = (self.cell_seq >> np.uint64(s)) & np.uint64(1)
+        sel = self.cell_pos[m.astype(bool)]
+        return int(sel.max()) if sel.size else -1
+
+    def n_free(self) -> int:
+        return int(np.count_nonzero(self.cell_pos < 0))
+
+    def find_slots(self, n: int) -> Optional[np.ndarray]:
+        """First run of n consecutive free cells from cell 0, else the n
+        lowest-index free cells, else None."""
+        free = np.flatnonzero(self.cell_pos < 0)
+        if free.size < n:
+            return None
+        span = free[n - 1:] - free[: free.size - n + 1]
+        hit = np.flatnonzero(span == n - 1)
+        if hit.size:
+            start = int(free[hit[0]])
+            return np.arange(start, start + n, dtype=np.int64)
+        return free[:n].astype(np.int64)
+
+    def _intake(self, tokens, pos, seq_ids, logits):
+        """Validation and defaults; returns (status, positions, seqs, flags)."""
+        n = len(tokens) if tokens is not None else 0
+        if n <= 0 or n > self.n_batch:
+            return INVALID, None, None, None
+        V = self.hp["n_vocab"] if self.hp is not None else None
+        toks = [int(t) for t in tokens]
+        if V is not None and any(t < 0 or t >= V for t in toks):
+            return INVALID, None, None, None
+        if seq_ids is None:
+            seqs = [[0] for _ in range(n)]
+        else:
+            if len(seq_ids) != n:
+                return INVALID, None, None, None
+            seqs = [list(map(int, s)) for s in seq_ids]
+            for s in seqs:
+                if len(s) < 1 or len(set(s)) != len(s) or any(x < 0 or x >= self.n_seq_max for x in s):
+                    return INVALID, None, None, None
+        # running last position per sequence (cache, then this batch)
+        last = {s: self.seq_pos_max(s) for s in range(self.n_seq_max)}
+        out_pos = []
+        for i in range(n):
+            p = last[seqs[i][0]] + 1 if pos is None else int(pos[i])
+            if p < 0 or any(p <= last[s] for s in seqs[i]):
+                return INVALID, None, None, None
+            for s in seqs[i]:
+                last[s] = p
+            out_pos.append(p)
+        if logits is None:
+            flags = [True] * n if self.output_all else [False] * (n - 1) + [True]
+        else:
+            if len(logits) != n:
+                return INVALID, None, None, None
+            flags = [bool(f) for f in logits]
+        return OK, out_pos, seqs, flags
+
+    # ---- decode -----------------------------------------------------------
+
+    def decode(self, tokens: Sequence[int], pos: Optional[Sequence[int]] = None,
+               seq_ids: Optional[Sequence[Sequence[int]]] = None,
+               logits: Optional[Sequence[bool]] = None) -> DecodeResult:
+        st, positions, seqs, flags = self._intake(tokens, pos, seq_ids, logits)
+        if st != OK:
+            return DecodeResult(status=st)
+        n = len(tokens)
+        if self.n_free() < n:
+            return DecodeResult(status=NO_SLOT)
+        res = DecodeResult(status=OK, positions=positions, seq_ids=seqs, output_flags=flags)
+        toks = np.asarray(tokens, dtype=np.int64)
+        rows = []
+        for u0 in range(0, n, self.n_ubatch):
+            ub = range(u0, min(n, u0 + self.n_ubatch))
+            res.ubatches.append(ub)
+            cells = self.find_slots(len(ub))
+            assert cells is not None  # total free space was checked above
+            for i, t in enumerate(ub):
+                self.cell_pos[cells[i]] = positions[t]
+                m = 0
+                for s in seqs[t]:
+                    m |= 1 << s
+                self.cell_seq[cells[i]] = np.uint64(m)
+            res.slots.extend(int(c) for c in cells)
+            sel = [i for i, t in enumerate(ub) if flags[t]]
+            res.out_index.extend(ub[i] for i in sel)
+            if self.compute:
+                out = self._forward(toks[ub.start:ub.stop], np.asarray([positions[t] for t in ub]),
+                                    [seqs[t][0] for t in ub], cells, sel)
+                if out is not None:
+                    rows.append(out)
+        if self.compute:
+            V = self.hp["n_vocab"]
+            res.logits = np.concatenate(rows, axis=0) if rows else np.zeros((0, V))
+            res.tokens = np.argmax(res.logits, axis=1) if rows else np.zeros(0, dtype=np.int64)
+        return res
+
+    def kv_import(self, seq: int, pos0: int, pos1: int, k_layers, v_layers) -> int:
+        """Place positions [pos0, pos1) of sequence ``seq`` in cells (one chunk,
+        same placement rule as a ubatch) holding the given post-RoPE K and V.
+        ``k_layers[l]`` / ``v_layers[l]`` are [pos1-pos0, n_head_kv, head_dim]
+        stored values (float32 or bf16 bits), or callables l -> such arrays."""
+        n = pos1 - pos0
+        if n <= 0 or seq < 0 or seq >= self.n_seq_max or pos0 <= self.seq_pos_max(seq):
+            return INVALID
+        cells = self.find_slots(n)
+        if cells is None:
+            return NO_SLOT
+        self.cell_pos[cells] = np.arange(pos0, pos1)
+        self.cell_seq[cells] = np.uint64(1 << seq)
+        if self.compute:
+            for l in range(self.hp["n_layer"]):
+                kl = k_layers(l) if callable(k_layers) else k_layers[l]
+                vl = v_layers(l) if callable(v_layers) else v_layers[l]
+                self._layer_cache(l)[0][cells] = widen(kl)
+                self._layer_cache(l)[1][cells] = widen(vl)
+        self.last_import_cells = cells
+        return OK
+
+    # ---- numerics ---------------------------------------------------------
+
+    def _layer_cache(self, l: int):
+        if l not in self.k_cache:
+            shape = (self.n_ctx, self.hp["n_head_kv"], self.hp["head_dim"])
+            self.k_cache[l] = np.zeros(shape, dtype=np.float64)
+            self.v_cache[l] = np.zeros(shape, dtype=np.float64)
+        return self.k_cache[l], self.v_cache[l]
+
+    def _forward(self, toks, pos, seq0, cells, sel) -> Optional[np.ndarray]:
+        hp, m = self.hp, self.model
+        H, Hkv, hd = hp["n_head"], hp["n_head_kv"], hp["head_dim"]
+        L, eps, theta = hp["n_layer"], hp["rms_eps"], hp["rope_theta"]
+        T = len(toks)
+        # visible cells per token: same (first) sequence, position <= own
+        visible = []
+        for t in range(T):
+            inseq = ((self.cell_seq >> np.uint64(seq0[t])) & np.uint64(1)).astype(bool)
+            visible.append(np.flatnonzero(inseq & (self.cell_pos >= 0) & (self.cell_pos <= pos[t])))
+        x = m.embed_rows(toks)
+        for l in range(L):
+            p = f"blk.{l}."
+            h = rms_norm(x, m.w(p + "attn_norm.weight"), eps)
+            q = (h @ m.w(p + "attn_q.weight").T).reshape(T, H, hd)
+            k = (h @ m.w(p + "attn_k.weight").T).reshape(T, Hkv, hd)
+            v = (h @ m.w(p + "attn_v.weight").T).reshape(T, Hkv, hd)
+            q = rope(q, pos, theta)
+            k = rope(k, pos, theta)
+            kc, vc = self._layer_cache(l)
+            kc[cells] = _round_storage(k, self.kv_round)
+            vc[cells] = _round_storage(v, self.kv_round)
+            o = np.stack([attend(q[t], kc[visible[t]], vc[visible[t]]) for t in range(T)])
+            x = x + o.reshape(T, H * hd) @ m.w(p + "attn_output.weight").T
+            if l == L - 1:
+                if not sel:
+                    return None
+                x = x[sel]
+            h2 = rms_norm(x, m.w(p + "ffn_norm.weight"), eps)
+            x = x + swiglu_mlp(h2, m.w(p + "ffn_gate.weight"), m.w(p + "ffn_up.weight"),
+                               m.w(p + "ffn_down.weight"))
+        if L == 0:
+            if not sel:
+                return None
+            x = x[sel]
+        return rms_norm(x, m.w("output_norm.weight"), eps) @ m.output_weight().T
