@@ -1,0 +1,230 @@
+"""Benchmark of the decoder forward pass on one MI355X.
+
+Workload (8B-class Llama shape, bf16 weights N(0, 0.02), bf16 KV cache of
+8192 cells): a 2048-token uniform-random prompt decoded in ubatches of 512
+with logits for the last position only (prefill), then greedy decode steps of
+one token each, every step feeding back the GPU's own argmax.
+
+A timed "step" is one decode call: the whole forward pass for one token
+(embedding, 32 layers, output norm, LM head, device argmax, 4-byte token
+readback).  ``value`` is decode tokens/s; the prefill rate of the same model
+is reported beside it.  ``roofline`` covers the dominant decode kernel (the
+fused gate/up GEMV) and ``roofline_prefill`` the dominant prefill kernel (the
+gate/up MFMA GEMM); both take their average launch duration from HIP events
+recorded on the library's stream during a profiled repeat of the workload.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def build_model(cfg):
+    import tdf_synth
+    import transformer_decode_forward_amd as tdf
+    from transformer_decode_forward_amd.device import to_device
+    host, dev = {}, {}
+    names = list(tdf_synth.tensor_shapes(cfg).items())
+    for l in range(cfg["n_layer"]):
+        names += list(tdf_synth.tensor_shapes(cfg, l).items())
+    t0 = time.time()
+    for i, (name, shape) in enumerate(names):
+        a = tdf_synth.make_tensor(cfg, name, shape)
+        host[name] = a
+        dev[name] = to_device(a)
+        if i % 36 == 0:
+            log(f"weights {i}/{len(names)} ({time.time() - t0:.0f}s)")
+    return tdf.Model(tdf_synth.hparams(cfg), dev), host
+
+
+def decode_bytes(cfg, ctx_len):
+    """Algorithmic HBM bytes of one single-token decode step at context ctx_len:
+    every weight once, K/V of the visible cells, the new K/V, the logits."""
+    d, H, Hkv, hd, F, V, L = (cfg[k] for k in ("n_embd", "n_head", "n_head_kv", "head_dim", "n_ff",
+                                             "n_vocab", "n_layer"))
+    p_layer = d * H * hd + 2 * d * Hkv * hd + H * hd * d + 3 * d * F
+    weights = 2 * (L * p_layer + V * d)
+    kv_cell = L * 2 * Hkv * hd * 2
+    return weights + kv_cell * ctx_len + kv_cell + 4 * V
+
+
+def prefill_flops(cfg, n_tok, n_ubatch, n_out_last=1):
+    """Algorithmic FLOPs of the prompt: projections and MLP of every token
+    (last layer's MLP only for output rows), causal attention pairs, LM head."""
+    d, H, Hkv, hd, F, V, L = (cfg[k] for k in ("n_embd", "n_head", "n_head_kv", "head_dim", "n_ff",
+                                             "n_vocab", "n_layer"))
+    p_attn = d * H * hd + 2 * d * Hkv * hd + H * hd * d
+    p_mlp = 3 * d * F
+    fl = 2 * n_tok * L * (p_attn + p_mlp) - 2 * (n_tok - n_out_last) * p_mlp
+    fl += 4 * H * hd * L * sum(p + 1 for p in range(n_tok))
+    fl += 2 * n_out_last * V * d
+    return fl
+
+
+def cpu_baseline(cfg, host_weights, ctx_len):
+    """The oracle, as it stands, on a bounded sample: one decode step of the
+    same model at context ctx_len (the cache restored from synthetic
+    post-RoPE K/V, since replaying the prompt on the CPU would take hours)."""
+    import tdf_synth
+    from oracle import OracleContext, OracleModel
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    m = OracleModel(tdf_synth.hparams(cfg), host_weights, cache=False)
+    oc = OracleContext(m, n_ctx=ctx_len + 8)
+    L = cfg["n_layer"]
+    rc = oc.kv_import(0, 0, ctx_len, lambda l: tdf_synth.kv_fill(cfg, l, "k", 0, ctx_len, "bf16"),
+                      lambda l: tdf_synth.kv_fill(cfg, l, "v", 0, ctx_len, "bf16"))
+    assert rc == 0
+    tok = int(tdf_synth.prompt(cfg, 7, 1)[0])
+    t0 = time.perf_counter()
+    r = oc.decode([tok])
+    dt = time.perf_counter() - t0
+    assert r.status == 0 and r.logits.shape == (1, cfg["n_vocab"])
+    return {"value": 1.0 / dt, "unit": "decode tok/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"1 decode step of the {L}-layer model at context {ctx_len} (cache restored "
+                      f"from synthetic K/V), float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--prefill-reps", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--config", default="llama8b")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tdf_synth
+    import transformer_decode_forward_amd as tdf
+    assert torch.cuda.is_available(), "no GPU"
+    cfg = dict(tdf_synth.CONFIGS[args.config])
+    P, U, n_ctx = cfg["prompt_len"], cfg["n_ubatch"], cfg["n_ctx"]
+    assert P + args.warmup + args.steps < n_ctx, "steps exceed the KV capacity"
+
+    log(f"generating and uploading {args.config} weights")
+    model, host = build_model(cfg)
+    prompt = tdf_synth.prompt(cfg, 0, P)
+
+    def run(ctx, steps, warm):
+        # prefill: repeated on a cleared cache, the last repetition timed
+        for _ in range(args.prefill_reps + 1):
+            ctx.kv_clear()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            assert ctx.decode(prompt) == 0, tdf.tdf_last_error()
+            t_pre = time.perf_counter() - t0
+        tok = ctx.argmax_ith(P - 1)
+        for _ in range(warm):
+            assert ctx.decode([tok]) == 0, tdf.tdf_last_error()
+            tok = ctx.argmax_ith(0)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            assert ctx.decode([tok]) == 0, tdf.tdf_last_error()
+            tok = ctx.argmax_ith(0)
+        torch.cuda.synchronize()
+        return t_pre, time.perf_counter() - t0
+
+    log("timed run")
+    ctx = tdf.Context(model, n_ctx=n_ctx, n_ubatch=U, kv_dtype=cfg["kv_dtype"])
+    t_pre, t_dec = run(ctx, args.steps, args.warmup)
+    ctx.close()
+    ms_step = 1000.0 * t_dec / args.steps
+    decode_tps = args.steps / t_dec
+    prefill_tps = P / t_pre
+    mean_ctx = P + args.warmup + (args.steps + 1) / 2.0
+    step_bytes = decode_bytes(cfg, mean_ctx)
+    pre_flops = prefill_flops(cfg, P, U)
+    log(f"prefill {prefill_tps:.0f} tok/s, decode {decode_tps:.1f} tok/s ({ms_step:.3f} ms/step)")
+
+    log("profiled run (HIP events per launch)")
+    pctx = tdf.Context(model, n_ctx=n_ctx, n_ubatch=U, kv_dtype=cfg["kv_dtype"], profile=True)
+    run(pctx, args.steps, args.warmup)
+    prof = pctx.profile()
+    pctx.close()
+    d, F = cfg["n_embd"], cfg["n_ff"]
+    n_gu, ms_gu = prof[("gate_up", "decode")]
+    # per decode launch: the gate and up matrices once, the normed input, the output
+    gu_bytes = 2 * F * d * 2 + d * 4 + F * 4
+    gu_ms = ms_gu / n_gu
+    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+    n_gg, ms_gg = prof[("gate_up", "mfma")]
+    gg_flops = 2.0 * U * (2 * F) * d
+    gg_ms = ms_gg / n_gg
+    gg_tfs = gg_flops / (gg_ms * 1e-3) / 1e12
+    breakdown = {f"{k[0]}/{k[1]}": {"launches": v[0], "avg_us": round(1000.0 * v[1] / v[0], 2)}
+                 for k, v in sorted(prof.items())}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(cfg, host, P)
+
+    out = {
+        "metric": "decode tok/s (% HBM peak) + prefill tok/s (% MFMA peak), 8B-shape bf16",
+        "value": round(decode_tps, 3),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: batch 1, {P}-token prompt in ubatches of {U} "
+                               f"(last-position logits), then greedy decode steps; KV bf16 {n_ctx} cells",
+                   "d_model": d, "n_layer": cfg["n_layer"], "n_ff": F, "n_vocab": cfg["n_vocab"]},
+        "decode": {"tok_s": round(decode_tps, 3), "mean_ctx": mean_ctx,
+                   "algorithmic_bytes_per_step": int(step_bytes),
+                   "achieved_GBs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+                   "frac_hbm_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "prefill": {"tok_s": round(prefill_tps, 1), "ms": round(1000 * t_pre, 3),
+                    "algorithmic_tflop": round(pre_flops / 1e12, 4),
+                    "achieved_TFLOPs": round(pre_flops / t_pre / 1e12, 2),
+                    "frac_mfma_peak": round(pre_flops / t_pre / 1e12 / MFMA_BF16_PEAK_TFS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "gate/up GEMV + SwiGLU (decode)",
+                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(1000 * gu_ms, 2), "bytes_per_launch": gu_bytes},
+        "roofline_prefill": {"bound": "mfma", "kernel": "gate/up GEMM + SwiGLU (prefill ubatch 512)",
+                             "achieved": round(gg_tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                             "frac": round(gg_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                             "avg_launch_us": round(1000 * gg_ms, 2), "flops_per_launch": gg_flops},
+        "kernels": breakdown,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,204 @@
+/*
+ * tdf.h -- C ABI of the MI355X (gfx950) Llama-style decoder forward pass.
+ *
+ * The calls follow the problem statement of the pages:
+ *  - a model made from hyper-parameters plus named weight tensors
+ *    (Ollama engine page "Inside the inference engine: model architectures
+ *    and the forward pass", sections on the model registry and reflection
+ *    based initialisation; llama.cpp walkthrough "Step 4: loading
+ *    hyper-parameters");
+ *  - a context owning the KV cache (llama.cpp walkthrough "Step 7: creating
+ *    the inference context"; Ollama page "KV Cache: memory for causal
+ *    attention");
+ *  - decode(batch of tokens, positions, sequence ids, output flags)
+ *    (llama.cpp walkthrough "Step 10: forming the batch for one call" and
+ *    "Steps 11-12: running the batch through the model"), logits per
+ *    flagged row ("Steps 14-15") and the greedy token (Ollama page "Token
+ *    sampling pipeline": temperature 0 is argmax).
+ *
+ * Conventions
+ *  - All functions are callable from any host thread, one call per context
+ *    at a time.  Errors are reported by the return value; a human-readable
+ *    message for the calling thread is available from tdf_last_error().
+ *  - "device" pointers are HIP device addresses on the current device;
+ *    "host" pointers are ordinary process memory.
+ *  - Matrices are row-major [out][in] in the model's weight dtype; norm
+ *    gains are float32.
+ */
+#ifndef TDF_H
+#define TDF_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TDF_F32 = 0, TDF_F16 = 1, TDF_BF16 = 2 } tdf_dtype;
+
+/* Return codes of tdf_decode / tdf_kv_import (llama.cpp walkthrough,
+ * "Steps 11-12": 0 success, 1 non-fatal, negative error). */
+enum {
+  TDF_OK = 0,
+  TDF_NO_SLOT = 1,        /* not enough free KV cells: nothing was changed */
+  TDF_E_INVALID = -1,     /* invalid argument or batch: nothing was changed */
+  TDF_E_ALLOC = -2,       /* device allocation failed */
+  TDF_E_DEVICE = -3       /* launch or device failure: clear the context */
+};
+
+/* Context flags. */
+enum {
+  TDF_CTX_DRY_RUN = 1,    /* bookkeeping only: validate, place cells, commit;
+                             no device memory, no kernels, no logits; the
+                             model's weight pointers are never read */
+  TDF_CTX_PROFILE = 2     /* time every kernel launch with HIP events on the
+                             context's stream (see tdf_profile_read) */
+};
+
+/* Operation classes timed by TDF_CTX_PROFILE. */
+enum {
+  TDF_OP_EMBED = 0,   /* embedding gather and cell-list update */
+  TDF_OP_NORM = 1,    /* RMSNorm and output-row gather */
+  TDF_OP_QKV = 2,     /* Q/K/V projection + RoPE + KV write */
+  TDF_OP_ATTN = 3,    /* attention (split + merge) */
+  TDF_OP_WO = 4,      /* output projection + residual */
+  TDF_OP_GATE_UP = 5, /* gate/up projection + SwiGLU */
+  TDF_OP_DOWN = 6,    /* down projection + residual */
+  TDF_OP_LM_HEAD = 7, /* LM head */
+  TDF_OP_ARGMAX = 8,  /* greedy argmax */
+  TDF_OP_COUNT = 9
+};
+
+/* Hyper-parameters (llama.cpp walkthrough, "Step 4": n_vocab, n_embd,
+ * n_layer, n_head, n_head_kv, n_ff, rope base).  head_dim is given
+ * explicitly; rope frequency scale is 1 and RMSNorm eps sits inside the
+ * square root. weight_dtype is TDF_F32 or TDF_BF16. */
+typedef struct {
+  int32_t n_vocab, n_embd, n_layer, n_head, n_head_kv, head_dim, n_ff;
+  float rms_eps, rope_theta;
+  int32_t weight_dtype;
+} tdf_hparams;
+
+/* Device pointers of one layer (GGUF names blk.<i>.*): attn_norm, attn_q
+ * [n_head*head_dim][n_embd], attn_k / attn_v [n_head_kv*head_dim][n_embd],
+ * attn_output [n_embd][n_head*head_dim], ffn_norm, ffn_gate / ffn_up
+ * [n_ff][n_embd], ffn_down [n_embd][n_ff]. */
+typedef struct {
+  const void *attn_norm, *wq, *wk, *wv, *wo, *ffn_norm, *w_gate, *w_up, *w_down;
+} tdf_layer_weights;
+
+/* token_embd [n_vocab][n_embd]; output_norm [n_embd] f32; output
+ * [n_vocab][n_embd] or NULL to reuse token_embd (tied embeddings, the
+ * "alt:token_embd" fallback of the Ollama model struct).  `layers` is a
+ * HOST array of n_layer entries; it is copied by tdf_model_create. */
+typedef struct {
+  const void *token_embd, *output_norm, *output;
+  const tdf_layer_weights *layers;
+} tdf_weights;
+
+/* n_ctx = KV cells; n_batch = largest batch per decode (clamped to n_ctx);
+ * n_ubatch = tokens per forward chunk (clamped to n_batch); n_seq_max <= 64;
+ * kv_dtype = TDF_F32, TDF_F16 or TDF_BF16; output_all = default output flag
+ * of every token instead of the last; stream = hipStream_t to run on (NULL:
+ * the context creates its own). */
+typedef struct {
+  int32_t n_ctx, n_batch, n_ubatch, n_seq_max;
+  int32_t kv_dtype;
+  int32_t output_all;
+  int32_t flags;
+  void *stream;
+} tdf_context_params;
+
+/* One decode call (llama.cpp walkthrough, "Step 10": struct llama_batch
+ * without the embedding input).  HOST arrays of n_tokens entries, read only
+ * during tdf_decode.  pos == NULL: each sequence continues at
+ * seq_pos_max(s)+1 in batch order.  n_seq_id/seq_id == NULL: sequence 0.
+ * logits == NULL: only the last token (or all, with output_all). */
+typedef struct {
+  int32_t n_tokens;
+  const int32_t *token;
+  const int32_t *pos;
+  const int32_t *n_seq_id;
+  const int32_t *const *seq_id;
+  const int8_t *logits;
+} tdf_batch;
+
+typedef struct tdf_model tdf_model;
+typedef struct tdf_context tdf_context;
+
+/* Model from hparams and DEVICE weight pointers.  The weights are NOT
+ * copied or owned: they must stay valid until tdf_model_free.  NULL on
+ * error (invalid hparams, missing pointer). */
+tdf_model *tdf_model_create(const tdf_hparams *hp, const tdf_weights *w);
+void tdf_model_free(tdf_model *m);
+
+/* Context (KV cache, scratch, logits) for a model; the model must outlive
+ * it.  NULL on error (invalid parameters, allocation failure). */
+tdf_context *tdf_context_create(const tdf_model *m, const tdf_context_params *p);
+void tdf_context_free(tdf_context *c);
+
+/* Run the batch: validate and fill defaults, split into ubatches of at most
+ * n_ubatch tokens in order, place each ubatch's tokens in KV cells, run the
+ * forward pass, keep the logits of flagged rows and their greedy tokens.
+ * Returns TDF_OK, TDF_NO_SLOT (nothing changed), TDF_E_INVALID (nothing
+ * changed), TDF_E_ALLOC or TDF_E_DEVICE.  Synchronises the context's stream
+ * before returning. */
+int32_t tdf_decode(tdf_context *c, const tdf_batch *b);
+
+/* Rows with logits after the last successful tdf_decode. */
+int32_t tdf_n_outputs(const tdf_context *c);
+
+/* Batch indices (batch order) of those rows into out[n_outputs]; returns
+ * n_outputs. */
+int32_t tdf_output_ids(const tdf_context *c, int32_t *out);
+
+/* HOST pointer to the n_vocab float32 logits of batch index i of the last
+ * decode, or NULL if i was not flagged.  Valid until the next tdf_decode,
+ * tdf_kv_clear or tdf_context_free (copied from the device on first use). */
+const float *tdf_get_logits_ith(tdf_context *c, int32_t i);
+
+/* DEVICE pointer to the [n_outputs][n_vocab] float32 logits. */
+const float *tdf_get_logits_device(tdf_context *c);
+
+/* Greedy token (argmax, lowest index on ties) of batch index i, or
+ * TDF_E_INVALID if i was not flagged. */
+int32_t tdf_argmax_ith(const tdf_context *c, int32_t i);
+
+/* Largest position held by sequence s, -1 if none (llama.cpp walkthrough,
+ * "KV-cache and the Prefill / Decode stages"); TDF_E_INVALID for a bad s. */
+int32_t tdf_seq_pos_max(const tdf_context *c, int32_t s);
+
+/* Free every cell (the cache contents become unreachable). */
+int32_t tdf_kv_clear(tdf_context *c);
+
+/* Inspection: position (-1 if free) and sequence bit mask of a cell. */
+int32_t tdf_kv_cell(const tdf_context *c, int32_t cell, int32_t *pos, uint64_t *seq_mask);
+
+/* Cells given to the tokens of the last successful decode (batch order) into
+ * slots[n_tokens]; returns n_tokens. */
+int32_t tdf_last_slots(const tdf_context *c, int32_t *slots);
+
+/* Place positions [pos0, pos0+n) of sequence s in cells (one chunk, the
+ * ubatch placement rule) and fill them with given post-RoPE keys and values:
+ * k_layers[l] / v_layers[l] are DEVICE pointers to [n][n_head_kv][head_dim]
+ * arrays in the context's kv dtype (HOST array of n_layer pointers).  Used
+ * to restore a cache state.  Returns TDF_OK, TDF_NO_SLOT, TDF_E_INVALID (pos0
+ * must exceed seq_pos_max(s)) or TDF_E_DEVICE. */
+int32_t tdf_kv_import(tdf_context *c, int32_t s, int32_t pos0, int32_t n,
+                      const void *const *k_layers, const void *const *v_layers);
+
+/* Accumulated launches and GPU time (ms, HIP events) of operation class op
+ * since the last reset, for the matrix-core path (mfma = 1: ubatches above
+ * 32 tokens) or the decode path (mfma = 0).  Only for TDF_CTX_PROFILE
+ * contexts; TDF_E_INVALID otherwise. */
+int32_t tdf_profile_read(const tdf_context *c, int32_t op, int32_t mfma, int64_t *launches, double *ms);
+int32_t tdf_profile_reset(tdf_context *c);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char *tdf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TDF_H */

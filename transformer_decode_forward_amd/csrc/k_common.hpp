@@ -1,0 +1,92 @@
+// Device helpers shared by the gfx950 kernels: storage conversions and
+// wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tdf {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ---- storage types -----------------------------------------------------
+// bf16 and fp16 values are carried as uint16_t bit patterns in memory.
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+// round to nearest even (inputs here are finite)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// Cache element types: KvT = float, or a tag for 16-bit formats.
+struct kv_bf16 {};
+struct kv_f16 {};
+
+template <typename KvT> struct KvStore;
+template <> struct KvStore<float> {
+  typedef float T;
+  __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct KvStore<kv_bf16> {
+  typedef uint16_t T;
+  __device__ __forceinline__ static float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+template <> struct KvStore<kv_f16> {
+  typedef uint16_t T;
+  __device__ __forceinline__ static float load(const uint16_t* p, int64_t i) { return f16_to_f32(p[i]); }
+  __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float v) { p[i] = f32_to_f16(v); }
+};
+
+// ---- wave64 reductions ---------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
+  return v;
+}
+
+// (value, index) max with the lowest index winning ties
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) {
+    v = v2;
+    i = i2;
+  }
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    float v2 = __shfl_xor(v, m, kWave);
+    int i2 = __shfl_xor(i, m, kWave);
+    argmax_merge(v, i, v2, i2);
+  }
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+}  // namespace tdf

@@ -1,0 +1,478 @@
+// Decode-side kernels for gfx950: embedding gather, RMSNorm, GEMV with fused
+// epilogues (RoPE + KV write, SwiGLU, residual add), split-K attention over
+// KV cells with an online-softmax merge, row gather and greedy argmax.
+//
+// The math of each step is the Llama layer of the Ollama engine page ("Deep
+// dive: the Llama forward pass in Go"): RMSNorm, Q/K/V projections, RoPE,
+// scaled dot-product attention over cached K/V with fewer KV heads than
+// query heads, output projection + residual, RMSNorm, SILU(gate) * up, down
+// projection + residual.  Decode is bound by HBM (llama.cpp walkthrough,
+// "KV-cache and the Prefill / Decode stages": decode is memory-bound), so the
+// GEMV streams each weight row once with 16-byte loads per lane and keeps the
+// activations in float32.
+#include "k_common.hpp"
+#include "kernels.hpp"
+#include "tdf.h"
+
+namespace tdf {
+
+// ---------------------------------------------------------------------------
+// small kernels
+
+template <bool BF16>
+__global__ void __launch_bounds__(256) embed_kernel(const void* __restrict__ table,
+                                                    const int32_t* __restrict__ tokens, int d,
+                                                    float* __restrict__ x) {
+  const int t = blockIdx.x;
+  const int64_t row = (int64_t)tokens[t] * d;
+  for (int k = threadIdx.x; k < d; k += blockDim.x) {
+    float v = BF16 ? bf16_to_f32(((const uint16_t*)table)[row + k]) : ((const float*)table)[row + k];
+    x[(int64_t)t * d + k] = v;
+  }
+}
+
+hipError_t launch_embed(const void* table, int weight_bf16, const int32_t* tokens, int T, int d,
+                        float* x, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (weight_bf16)
+    embed_kernel<true><<<T, 256, 0, s>>>(table, tokens, d, x);
+  else
+    embed_kernel<false><<<T, 256, 0, s>>>(table, tokens, d, x);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ x,
+                                                      const float* __restrict__ g, int d, float eps,
+                                                      float* __restrict__ out_f32,
+                                                      uint16_t* __restrict__ out_bf16) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const float* xr = x + (int64_t)t * d;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < d; k += 256) {
+    float v = xr[k];
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  ss = red[0] + red[1] + red[2] + red[3];
+  const float r = 1.0f / sqrtf(ss / (float)d + eps);
+  for (int k = threadIdx.x; k < d; k += 256) {
+    float v = xr[k] * r * g[k];
+    if (out_f32) out_f32[(int64_t)t * d + k] = v;
+    if (out_bf16) out_bf16[(int64_t)t * d + k] = f32_to_bf16(v);
+  }
+}
+
+hipError_t launch_rmsnorm(const float* x, const float* g, int T, int d, float eps, float* out_f32,
+                          uint16_t* out_bf16, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  rmsnorm_kernel<<<T, 256, 0, s>>>(x, g, d, eps, out_f32, out_bf16);
+  return hipGetLastError();
+}
+
+__global__ void scatter_kernel(int32_t* __restrict__ dst, const int64_t* __restrict__ pairs, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[pairs[2 * i]] = (int32_t)pairs[2 * i + 1];
+}
+
+hipError_t launch_scatter(int32_t* dst, const int64_t* pairs, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  scatter_kernel<<<(n + 255) / 256, 256, 0, s>>>(dst, pairs, n);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(256) gather_rows_kernel(const float* __restrict__ src,
+                                                          const int32_t* __restrict__ rows, int d,
+                                                          float* __restrict__ dst) {
+  const int r = blockIdx.x;
+  const float* s = src + (int64_t)rows[r] * d;
+  for (int k = threadIdx.x; k < d; k += 256) dst[(int64_t)r * d + k] = s[k];
+}
+
+hipError_t launch_gather_rows(const float* src, const int32_t* rows, int R, int d, float* dst,
+                              hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  gather_rows_kernel<<<R, 256, 0, s>>>(src, rows, d, dst);
+  return hipGetLastError();
+}
+
+__global__ void __launch_bounds__(1024) argmax_kernel(const float* __restrict__ logits, int V,
+                                                      int32_t* __restrict__ tok) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const float* row = logits + (int64_t)blockIdx.x * V;
+  float best = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  for (int n = threadIdx.x; n < V; n += 1024) argmax_merge(best, bi, row[n], n);
+  wave_argmax(best, bi);
+  if ((threadIdx.x & 63) == 0) {
+    sv[threadIdx.x >> 6] = best;
+    si[threadIdx.x >> 6] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    best = sv[0];
+    bi = si[0];
+    for (int w = 1; w < 16; ++w) argmax_merge(best, bi, sv[w], si[w]);
+    tok[blockIdx.x] = bi;
+  }
+}
+
+hipError_t launch_argmax(const float* logits, int R, int V, int32_t* tok, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  argmax_kernel<<<R, 1024, 0, s>>>(logits, V, tok);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// GEMV: one wave per output pair.  For EPI_SWIGLU the pair is (gate row n,
+// up row n); otherwise rows (2p, 2p+1), so that a RoPE pair (2i, 2i+1) of a
+// head lands in one wave.  Lanes stride the row in chunks of 8 elements
+// (16 bytes of bf16), all NT tokens reuse each weight chunk from registers.
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* base, int64_t idx, float w[8]) {
+  if (BF16) {
+    const uint4 u = *(const uint4*)((const uint16_t*)base + idx);
+    const uint32_t p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[2 * j] = __builtin_bit_cast(float, p[j] << 16);
+      w[2 * j + 1] = __builtin_bit_cast(float, p[j] & 0xFFFF0000u);
+    }
+  } else {
+    const float4 a = *(const float4*)((const float*)base + idx);
+    const float4 b = *(const float4*)((const float*)base + idx + 4);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void* base, int64_t idx) {
+  return BF16 ? bf16_to_f32(((const uint16_t*)base)[idx]) : ((const float*)base)[idx];
+}
+
+template <typename KvT>
+__device__ __forceinline__ void kv_put(void* cache, int64_t idx, float v) {
+  KvStore<KvT>::store((typename KvStore<KvT>::T*)cache, idx, v);
+}
+
+template <bool BF16, int NT, int EPI, typename KvT>
+__global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int N = a.n0 + a.n1 + a.n2;
+  const int K = a.K;
+  // the two rows of this wave
+  int r0, r1;
+  const void *p0, *p1;
+  int64_t off0, off1;
+  if (EPI == EPI_SWIGLU) {
+    if (wave >= a.n0) return;
+    r0 = r1 = wave;
+    p0 = a.w0; p1 = a.w1;
+    off0 = off1 = (int64_t)wave * K;
+  } else {
+    r0 = 2 * wave;
+    if (r0 >= N) return;
+    r1 = r0 + 1 < N ? r0 + 1 : r0;
+    auto locate = [&](int r, const void*& p, int64_t& off) {
+      if (r < a.n0) { p = a.w0; off = (int64_t)r * K; }
+      else if (r < a.n0 + a.n1) { p = a.w1; off = (int64_t)(r - a.n0) * K; }
+      else { p = a.w2; off = (int64_t)(r - a.n0 - a.n1) * K; }
+    };
+    locate(r0, p0, off0);
+    locate(r1, p1, off1);
+  }
+  const float* act = a.act_f32 + (int64_t)t0 * K;
+
+  float acc0[NT], acc1[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc0[t] = acc1[t] = 0.f;
+
+  const bool vec = (K & 7) == 0;
+  if (vec) {
+#pragma unroll 2
+    for (int k = lane * 8; k < K; k += 512) {
+      float w0[8], w1[8];
+      load8<BF16>(p0, off0 + k, w0);
+      load8<BF16>(p1, off1 + k, w1);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (t < nt) {
+          const float4 x0 = *(const float4*)(act + (int64_t)t * K + k);
+          const float4 x1 = *(const float4*)(act + (int64_t)t * K + k + 4);
+          const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            acc0[t] = fmaf(w0[j], x[j], acc0[t]);
+            acc1[t] = fmaf(w1[j], x[j], acc1[t]);
+          }
+        }
+      }
+    }
+  } else {
+    for (int k = lane; k < K; k += 64) {
+      const float w0 = load1<BF16>(p0, off0 + k), w1 = load1<BF16>(p1, off1 + k);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (t < nt) {
+          const float x = act[(int64_t)t * K + k];
+          acc0[t] = fmaf(w0, x, acc0[t]);
+          acc1[t] = fmaf(w1, x, acc1[t]);
+        }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    acc0[t] = wave_sum(acc0[t]);
+    acc1[t] = wave_sum(acc1[t]);
+  }
+  // lane t writes token t
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (lane != t || t >= nt) continue;
+    const int tg = t0 + t;
+    const float y0 = acc0[t], y1 = acc1[t];
+    if (EPI == EPI_STORE) {
+      a.out[(int64_t)tg * a.ldo + r0] = y0;
+      if (r1 != r0) a.out[(int64_t)tg * a.ldo + r1] = y1;
+    } else if (EPI == EPI_RESIDUAL) {
+      a.out[(int64_t)tg * a.ldo + r0] += y0;
+      if (r1 != r0) a.out[(int64_t)tg * a.ldo + r1] += y1;
+    } else if (EPI == EPI_SWIGLU) {
+      a.out[(int64_t)tg * a.ldo + r0] = silu(y0) * y1;
+    } else if (EPI == EPI_QKV) {
+      const int hd = a.head_dim;
+      if (r0 < a.n0 + a.n1) {
+        // q or k row pair (2i, 2i+1) of one head: rotate by pos * theta^(-2i/hd)
+        const int lr = r0 < a.n0 ? r0 : r0 - a.n0;
+        const int i = (lr % hd) >> 1;
+        double sn, cs;
+        sincos((double)a.pos[tg] * a.inv_freq[i], &sn, &cs);
+        const float c = (float)cs, s = (float)sn;
+        const float z0 = y0 * c - y1 * s, z1 = y0 * s + y1 * c;
+        if (r0 < a.n0) {
+          a.q_out[(int64_t)tg * a.n0 + lr] = z0;
+          a.q_out[(int64_t)tg * a.n0 + lr + 1] = z1;
+        } else {
+          const int64_t ci = ((int64_t)(lr / hd) * a.n_ctx + a.slots[tg]) * hd + (lr % hd);
+          kv_put<KvT>(a.k_cache, ci, z0);
+          kv_put<KvT>(a.k_cache, ci + 1, z1);
+        }
+      } else {
+        const int lr = r0 - a.n0 - a.n1;
+        const int64_t ci = ((int64_t)(lr / hd) * a.n_ctx + a.slots[tg]) * hd + (lr % hd);
+        kv_put<KvT>(a.v_cache, ci, y0);
+        if (r1 != r0) kv_put<KvT>(a.v_cache, ci + 1, y1);
+      }
+    }
+  }
+}
+
+template <bool BF16, int NT, int EPI, typename KvT>
+static hipError_t gemv_launch_t(const LinearArgs& a, hipStream_t s) {
+  const int N = a.n0 + a.n1 + a.n2;
+  const int waves = EPI == EPI_SWIGLU ? a.n0 : (N + 1) / 2;
+  const int blocks = (waves + 3) / 4;
+  for (int t0 = 0; t0 < a.T; t0 += NT) {
+    const int nt = a.T - t0 < NT ? a.T - t0 : NT;
+    gemv_kernel<BF16, NT, EPI, KvT><<<blocks, 256, 0, s>>>(a, t0, nt);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <bool BF16, int NT>
+static hipError_t gemv_dispatch_epi(const LinearArgs& a, hipStream_t s) {
+  switch (a.epi) {
+    case EPI_STORE: return gemv_launch_t<BF16, NT, EPI_STORE, float>(a, s);
+    case EPI_RESIDUAL: return gemv_launch_t<BF16, NT, EPI_RESIDUAL, float>(a, s);
+    case EPI_SWIGLU: return gemv_launch_t<BF16, NT, EPI_SWIGLU, float>(a, s);
+    case EPI_QKV:
+      if (a.kv_dtype == TDF_BF16) return gemv_launch_t<BF16, NT, EPI_QKV, kv_bf16>(a, s);
+      if (a.kv_dtype == TDF_F16) return gemv_launch_t<BF16, NT, EPI_QKV, kv_f16>(a, s);
+      return gemv_launch_t<BF16, NT, EPI_QKV, float>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_linear_gemv(const LinearArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  // tokens per pass: 1 for the latency-critical single-token step, else 8
+  if (a.weight_bf16) {
+    if (a.T == 1) return gemv_dispatch_epi<true, 1>(a, s);
+    if (a.T <= 4) return gemv_dispatch_epi<true, 4>(a, s);
+    return gemv_dispatch_epi<true, 8>(a, s);
+  }
+  if (a.T == 1) return gemv_dispatch_epi<false, 1>(a, s);
+  if (a.T <= 4) return gemv_dispatch_epi<false, 4>(a, s);
+  return gemv_dispatch_epi<false, 8>(a, s);
+}
+
+// ---------------------------------------------------------------------------
+// Decode attention.  Block (chunk j, kv head g, token t): the G = H/Hkv query
+// heads of the group share each K/V tile of 64 cells staged in LDS as
+// float32; online softmax (running max m, running sum l, rescaled
+// accumulator) per head.  Partials of all chunks are merged afterwards.
+
+constexpr int kTile = 64;
+
+template <typename KvT, int HD, int G>
+__global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
+  typedef typename KvStore<KvT>::T ST;
+  __shared__ float q_s[G][HD];
+  __shared__ float k_s[kTile][HD + 1];
+  __shared__ float v_s[kTile][HD];
+  __shared__ float p_s[G][kTile];
+  __shared__ float m_s[G], l_s[G], alpha_s[G];
+
+  const int j = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int nvis = a.n_vis[t];
+  const int c_lo = j * a.chunk;
+  if (c_lo >= nvis) return;
+  const int c_hi = min(nvis, c_lo + a.chunk);
+  const int32_t* cells = a.cell_list + a.list_off[t];
+  const ST* kc = (const ST*)a.k_cache + (int64_t)g * a.n_ctx * HD;
+  const ST* vc = (const ST*)a.v_cache + (int64_t)g * a.n_ctx * HD;
+  const float scale = rsqrtf((float)HD);
+
+  for (int i = tid; i < G * HD; i += 256) {
+    const int h = i / HD, d = i % HD;
+    q_s[h][d] = a.q[((int64_t)t * a.H + g * G + h) * HD + d] * scale;
+  }
+  if (tid < G) {
+    m_s[tid] = -INFINITY;
+    l_s[tid] = 0.f;
+  }
+  constexpr int OUT_PER = (G * HD + 255) / 256;
+  float acc[OUT_PER];
+#pragma unroll
+  for (int o = 0; o < OUT_PER; ++o) acc[o] = 0.f;
+
+  for (int c0 = c_lo; c0 < c_hi; c0 += kTile) {
+    const int nc = min(kTile, c_hi - c0);
+    __syncthreads();
+    for (int i = tid; i < kTile * HD; i += 256) {
+      const int c = i / HD, d = i % HD;
+      float kv = 0.f, vv = 0.f;
+      if (c < nc) {
+        const int64_t row = (int64_t)cells[c0 + c] * HD + d;
+        kv = KvStore<KvT>::load(kc, row);
+        vv = KvStore<KvT>::load(vc, row);
+      }
+      k_s[c][d] = kv;
+      v_s[c][d] = vv;
+    }
+    __syncthreads();
+    // scores: wave w takes heads w, w+4, ...; lane = cell
+    const int lane = tid & 63, w = tid >> 6;
+    for (int h = w; h < G; h += 4) {
+      float sc = -INFINITY;
+      if (lane < nc) {
+        float s = 0.f;
+#pragma unroll 8
+        for (int d = 0; d < HD; ++d) s = fmaf(q_s[h][d], k_s[lane][d], s);
+        sc = s;
+      }
+      const float tmax = wave_max(sc);
+      const float m_old = m_s[h];
+      const float m_new = fmaxf(m_old, tmax);
+      const float p = lane < nc ? __expf(sc - m_new) : 0.f;
+      const float psum = wave_sum(p);
+      p_s[h][lane] = p;
+      if (lane == 0) {
+        const float al = __expf(m_old - m_new);
+        alpha_s[h] = al;
+        l_s[h] = l_s[h] * al + psum;
+        m_s[h] = m_new;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int o = 0; o < OUT_PER; ++o) {
+      const int id = tid + o * 256;
+      if (id < G * HD) {
+        const int h = id / HD, d = id % HD;
+        float s = acc[o] * alpha_s[h];
+        for (int c = 0; c < nc; ++c) s = fmaf(p_s[h][c], v_s[c][d], s);
+        acc[o] = s;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int o = 0; o < OUT_PER; ++o) {
+    const int id = tid + o * 256;
+    if (id < G * HD) {
+      const int h = id / HD, d = id % HD;
+      const int64_t base = ((int64_t)t * a.H + g * G + h) * a.n_chunks + j;
+      a.part_acc[base * HD + d] = acc[o];
+      if (d == 0) {
+        a.part_ml[base * 2] = m_s[h];
+        a.part_ml[base * 2 + 1] = l_s[h];
+      }
+    }
+  }
+}
+
+template <int HD>
+__global__ void __launch_bounds__(HD) attn_merge_kernel(AttnArgs a) {
+  const int h = blockIdx.x, t = blockIdx.y, d = threadIdx.x;
+  const int nch = (a.n_vis[t] + a.chunk - 1) / a.chunk;
+  const int64_t base = ((int64_t)t * a.H + h) * a.n_chunks;
+  float M = -INFINITY;
+  for (int j = 0; j < nch; ++j) M = fmaxf(M, a.part_ml[(base + j) * 2]);
+  float L = 0.f, o = 0.f;
+  for (int j = 0; j < nch; ++j) {
+    const float w = __expf(a.part_ml[(base + j) * 2] - M);
+    L = fmaf(a.part_ml[(base + j) * 2 + 1], w, L);
+    o = fmaf(a.part_acc[(base + j) * HD + d], w, o);
+  }
+  const float r = o / L;
+  const int64_t oi = ((int64_t)t * a.H + h) * HD + d;
+  if (a.out) a.out[oi] = r;
+  if (a.out_bf16) a.out_bf16[oi] = f32_to_bf16(r);
+}
+
+template <typename KvT, int HD>
+static hipError_t attn_launch_hd(const AttnArgs& a, hipStream_t s) {
+  const int G = a.H / a.Hkv;
+  dim3 grid(a.n_chunks, a.Hkv, a.T);
+  switch (G) {
+    case 1: attn_decode_kernel<KvT, HD, 1><<<grid, 256, 0, s>>>(a); break;
+    case 2: attn_decode_kernel<KvT, HD, 2><<<grid, 256, 0, s>>>(a); break;
+    case 4: attn_decode_kernel<KvT, HD, 4><<<grid, 256, 0, s>>>(a); break;
+    case 8: attn_decode_kernel<KvT, HD, 8><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  attn_merge_kernel<HD><<<dim3(a.H, a.T), HD, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <typename KvT>
+static hipError_t attn_launch_kv(const AttnArgs& a, hipStream_t s) {
+  switch (a.hd) {
+    case 16: return attn_launch_hd<KvT, 16>(a, s);
+    case 32: return attn_launch_hd<KvT, 32>(a, s);
+    case 64: return attn_launch_hd<KvT, 64>(a, s);
+    case 128: return attn_launch_hd<KvT, 128>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  if (a.kv_dtype == TDF_BF16) return attn_launch_kv<kv_bf16>(a, s);
+  if (a.kv_dtype == TDF_F16) return attn_launch_kv<kv_f16>(a, s);
+  return attn_launch_kv<float>(a, s);
+}
+
+}  // namespace tdf

@@ -1,0 +1,87 @@
+// Launch interface of the gfx950 kernels (host side).  Every launcher
+// enqueues on `stream` and returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tdf {
+
+enum Epilogue : int {
+  EPI_STORE = 0,     // out[t][n] = y                         (float32)
+  EPI_RESIDUAL = 1,  // out[t][n] += y                        (residual stream)
+  EPI_SWIGLU = 2,    // out[t][n] = silu(y_gate) * y_up       (w0 = gate, w1 = up)
+  EPI_QKV = 3,       // RoPE on q and k, q -> q_out, k/v -> cache cells
+};
+
+// y[t][n] = sum_k W[n][k] act[t][k] for the rows of up to three matrices
+// stacked along n (QKV: w0 = W_q, w1 = W_k, w2 = W_v).
+struct LinearArgs {
+  const void* w0 = nullptr;
+  const void* w1 = nullptr;
+  const void* w2 = nullptr;
+  int n0 = 0, n1 = 0, n2 = 0;  // rows of each matrix
+  int K = 0;                   // inner size (row length)
+  int T = 0;                   // tokens (rows of act)
+  int weight_bf16 = 1;         // 1: bf16 weights, 0: float32
+  // activations: float32 [T][K] (GEMV) or bf16 [T][K] (GEMM)
+  const float* act_f32 = nullptr;
+  const uint16_t* act_bf16 = nullptr;
+  // epilogue
+  int epi = EPI_STORE;
+  float* out = nullptr;        // [T][ldo] float32 (STORE / RESIDUAL / SWIGLU)
+  uint16_t* out_bf16 = nullptr;// [T][ldo] bf16 (GEMM SWIGLU)
+  int ldo = 0;
+  // EPI_QKV
+  float* q_out = nullptr;      // [T][n0] float32 (GEMV)
+  uint16_t* q_out_bf16 = nullptr;  // [T][n0] bf16 (GEMM)
+  void* k_cache = nullptr;     // layer base [n_head_kv][n_ctx][head_dim]
+  void* v_cache = nullptr;
+  int kv_dtype = 0;            // tdf_dtype
+  int n_ctx = 0;
+  int head_dim = 0;
+  const int32_t* slots = nullptr;  // [T] cell of each token
+  const int32_t* pos = nullptr;    // [T] position of each token
+  const double* inv_freq = nullptr;// [head_dim/2] theta^(-2i/head_dim)
+};
+
+hipError_t launch_linear_gemv(const LinearArgs& a, hipStream_t s);
+hipError_t launch_linear_gemm(const LinearArgs& a, hipStream_t s);
+bool gemm_supported(const LinearArgs& a);
+
+// x[t][:] = E[token[t]][:] (to float32)
+hipError_t launch_embed(const void* table, int weight_bf16, const int32_t* tokens, int T, int d,
+                        float* x, hipStream_t s);
+// out = x / sqrt(mean(x^2) + eps) * g, float32 and/or bf16 outputs
+hipError_t launch_rmsnorm(const float* x, const float* g, int T, int d, float eps, float* out_f32,
+                          uint16_t* out_bf16, hipStream_t s);
+// dst[pairs[2i]] = pairs[2i+1]
+hipError_t launch_scatter(int32_t* dst, const int64_t* pairs, int n, hipStream_t s);
+// dst[r][:] = src[rows[r]][:]
+hipError_t launch_gather_rows(const float* src, const int32_t* rows, int R, int d, float* dst,
+                              hipStream_t s);
+// tok[r] = argmax_n logits[r][n] (lowest index on ties)
+hipError_t launch_argmax(const float* logits, int R, int V, int32_t* tok, hipStream_t s);
+
+// Attention of T tokens over their visible cells (split over cell chunks,
+// then merged).  q [T][H][hd] float32; caches [Hkv][n_ctx][hd]; cell lists
+// [n_seq_max][n_ctx]; list_off[t] = seq * n_ctx; n_vis[t] = visible cells.
+struct AttnArgs {
+  const float* q = nullptr;
+  const void* k_cache = nullptr;
+  const void* v_cache = nullptr;
+  int kv_dtype = 0;
+  const int32_t* cell_list = nullptr;
+  const int32_t* list_off = nullptr;
+  const int32_t* n_vis = nullptr;
+  int T = 0, H = 0, Hkv = 0, hd = 0, n_ctx = 0;
+  int chunk = 256;       // cells per split
+  int n_chunks = 1;      // splits of the longest token
+  float* part_acc = nullptr;  // [T][H][n_chunks][hd]
+  float* part_ml = nullptr;   // [T][H][n_chunks][2]
+  float* out = nullptr;       // [T][H][hd] float32
+  uint16_t* out_bf16 = nullptr;  // optional bf16 copy
+};
+hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t s);
+
+}  // namespace tdf

@@ -1,0 +1,730 @@
+// C ABI and host runtime of the decoder forward pass (declared in tdf.h).
+//
+// One decode call (llama.cpp walkthrough, "Steps 11-12" and "Step 13"):
+// intake and defaults (host_plan), an all-or-nothing check that the batch
+// fits in the free cells, then per ubatch: place the tokens in cells and
+// commit them, upload the ubatch's small integer arrays in one copy, and
+// enqueue the layer loop of the Ollama engine page ("Deep dive: the Llama
+// forward pass in Go").  ubatches of at most 32 tokens take the decode
+// kernels (GEMV, split-K attention), larger ones the MFMA GEMM.  The logits
+// of flagged rows land in one device buffer in batch order ("Steps 14-15"),
+// followed by a device argmax per row; the call synchronises its stream
+// before returning.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "host_plan.hpp"
+#include "kernels.hpp"
+#include "tdf.h"
+
+using namespace tdf;
+
+namespace {
+
+thread_local std::string g_err;
+
+void set_err(const std::string& s) { g_err = s; }
+
+// test hook: TDF_FAULT_ALLOC=n makes the n-th device allocation fail
+int g_alloc_count = 0;
+hipError_t dev_alloc(void** p, size_t bytes) {
+  static const int fault_at = [] {
+    const char* e = getenv("TDF_FAULT_ALLOC");
+    return e ? atoi(e) : 0;
+  }();
+  ++g_alloc_count;
+  if (fault_at > 0 && g_alloc_count == fault_at) {
+    *p = nullptr;
+    return hipErrorOutOfMemory;
+  }
+  if (bytes == 0) bytes = 256;
+  return hipMalloc(p, bytes);
+}
+
+size_t dtype_size(int dt) { return dt == TDF_F32 ? 4 : 2; }
+
+constexpr int kDecodeMaxT = 32;     // ubatches up to this size use the decode kernels
+constexpr int kChunkCapDecode = 256; // attention splits per token (decode)
+constexpr int kChunkCapPrefill = 32; // attention splits per token (larger ubatches)
+
+// int32 entries of the per-call staging area: 5 per token + selected rows,
+// each ubatch region rounded up to 4 entries
+size_t staging_i32(int n_batch) { return (size_t)10 * n_batch + 16; }
+size_t staging_i64_base(int n_batch) { return (staging_i32(n_batch) * 4 + 15) & ~(size_t)15; }
+
+}  // namespace
+
+struct tdf_model {
+  tdf_hparams hp;
+  const void* token_embd;
+  const float* output_norm;
+  const void* output;
+  std::vector<tdf_layer_weights> layers;
+};
+
+struct tdf_context {
+  const tdf_model* m = nullptr;
+  int n_ctx = 0, n_batch = 0, n_ubatch = 0, n_seq_max = 0, kv_dtype = 0;
+  bool output_all = false, dry_run = false;
+  hipStream_t stream = nullptr;
+  bool own_stream = false;
+  KvBook book;
+
+  // device memory
+  void* kv = nullptr;               // [L][2][Hkv][n_ctx][hd]
+  size_t kv_layer_bytes = 0;        // one of K or V of one layer
+  int32_t* cell_list = nullptr;     // [n_seq_max][n_ctx]
+  double* inv_freq = nullptr;       // [hd/2]
+  float *x = nullptr, *xs = nullptr, *act = nullptr, *q = nullptr, *o = nullptr, *mb = nullptr;
+  uint16_t *h16 = nullptr, *o16 = nullptr, *m16 = nullptr;
+  float *part_acc = nullptr, *part_ml = nullptr;
+  size_t part_rows = 0;             // capacity in (token, head, chunk) triples
+  void* ints = nullptr;             // per-call packed integers
+  size_t ints_bytes = 0;
+  char* ints_host = nullptr;        // pinned staging
+  float* logits = nullptr;          // [cap][V]
+  int32_t* d_tok = nullptr;         // [cap]
+  int32_t* h_tok = nullptr;         // pinned [cap]
+  int logits_cap = 0;
+  std::vector<void*> owned;
+
+  // TDF_CTX_PROFILE: event pairs of the current call, totals per (op, path)
+  bool profile = false;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+  std::vector<int> ev_slot;          // slot of each recorded pair
+  int64_t prof_n[2 * TDF_OP_COUNT] = {};
+  double prof_ms[2 * TDF_OP_COUNT] = {};
+
+  // results of the last decode
+  int n_outputs = 0;
+  std::vector<int32_t> out_ids;     // batch index of each output row
+  std::vector<int32_t> row_of;      // batch index -> output row or -1
+  std::vector<int32_t> last_slots;
+  std::vector<float> logits_host;
+  std::vector<char> host_row_ok;
+};
+
+// ---------------------------------------------------------------------------
+// helpers
+
+#define TDF_HIP(expr)                                                        \
+  do {                                                                       \
+    hipError_t _e = (expr);                                                  \
+    if (_e != hipSuccess) {                                                  \
+      set_err(std::string(#expr) + ": " + hipGetErrorString(_e));            \
+      return TDF_E_DEVICE;                                                   \
+    }                                                                        \
+  } while (0)
+
+static int ctx_alloc(tdf_context* c, void** p, size_t bytes) {
+  hipError_t e = dev_alloc(p, bytes);
+  if (e != hipSuccess) {
+    set_err(std::string("device allocation failed: ") + hipGetErrorString(e));
+    return TDF_E_ALLOC;
+  }
+  c->owned.push_back(*p);
+  return TDF_OK;
+}
+
+// ---- profiling (TDF_CTX_PROFILE) ----
+
+static hipEvent_t prof_event(tdf_context* c) {
+  if (c->ev_used == c->ev_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    c->ev_pool.push_back(e);
+  }
+  return c->ev_pool[c->ev_used++];
+}
+
+// records a start event; returns the slot to pass to prof_end (or -1)
+static int prof_begin(tdf_context* c, int op, bool mfma) {
+  if (!c->profile) return -1;
+  hipEvent_t e = prof_event(c);
+  if (!e || hipEventRecord(e, c->stream) != hipSuccess) return -1;
+  return 2 * op + (mfma ? 1 : 0);
+}
+
+static void prof_end(tdf_context* c, int slot) {
+  if (slot < 0) return;
+  hipEvent_t e = prof_event(c);
+  if (!e || hipEventRecord(e, c->stream) != hipSuccess) return;
+  c->ev_slot.push_back(slot);
+}
+
+// after the stream has been synchronised: fold the recorded pairs in
+static void prof_collect(tdf_context* c) {
+  if (!c->profile) return;
+  for (size_t i = 0; i < c->ev_slot.size(); ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, c->ev_pool[2 * i], c->ev_pool[2 * i + 1]) == hipSuccess) {
+      c->prof_ms[c->ev_slot[i]] += ms;
+      c->prof_n[c->ev_slot[i]] += 1;
+    }
+  }
+  c->ev_slot.clear();
+  c->ev_used = 0;
+}
+
+static void ctx_release(tdf_context* c) {
+  for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
+  c->ev_pool.clear();
+  for (void* p : c->owned) (void)hipFree(p);
+  c->owned.clear();
+  if (c->ints_host) (void)hipHostFree(c->ints_host);
+  if (c->h_tok) (void)hipHostFree(c->h_tok);
+  c->ints_host = nullptr;
+  c->h_tok = nullptr;
+  if (c->own_stream && c->stream) (void)hipStreamDestroy(c->stream);
+  c->stream = nullptr;
+}
+
+static int ensure_logits(tdf_context* c, int rows) {
+  if (rows <= c->logits_cap) return TDF_OK;
+  const int V = c->m->hp.n_vocab;
+  void *lg = nullptr, *tk = nullptr;
+  hipError_t e = dev_alloc(&lg, (size_t)rows * V * sizeof(float));
+  if (e == hipSuccess) e = dev_alloc(&tk, (size_t)rows * sizeof(int32_t));
+  void* htk = nullptr;
+  if (e == hipSuccess) e = hipHostMalloc(&htk, (size_t)rows * sizeof(int32_t), hipHostMallocDefault);
+  if (e != hipSuccess) {
+    if (lg) (void)hipFree(lg);
+    if (tk) (void)hipFree(tk);
+    set_err(std::string("logits allocation failed: ") + hipGetErrorString(e));
+    return TDF_E_ALLOC;
+  }
+  auto drop = [&](void* p) {
+    if (!p) return;
+    auto it = std::find(c->owned.begin(), c->owned.end(), p);
+    if (it != c->owned.end()) c->owned.erase(it);
+    (void)hipFree(p);
+  };
+  (void)hipStreamSynchronize(c->stream);
+  drop(c->logits);
+  drop(c->d_tok);
+  if (c->h_tok) (void)hipHostFree(c->h_tok);
+  c->logits = (float*)lg;
+  c->d_tok = (int32_t*)tk;
+  c->h_tok = (int32_t*)htk;
+  c->owned.push_back(lg);
+  c->owned.push_back(tk);
+  c->logits_cap = rows;
+  return TDF_OK;
+}
+
+static void* kv_k(const tdf_context* c, int l) { return (char*)c->kv + (size_t)(2 * l) * c->kv_layer_bytes; }
+static void* kv_v(const tdf_context* c, int l) { return (char*)c->kv + (size_t)(2 * l + 1) * c->kv_layer_bytes; }
+
+// ---------------------------------------------------------------------------
+// model
+
+extern "C" tdf_model* tdf_model_create(const tdf_hparams* hp, const tdf_weights* w) {
+  if (!hp || !w) { set_err("hparams or weights is NULL"); return nullptr; }
+  const tdf_hparams& h = *hp;
+  if (h.n_vocab <= 0 || h.n_embd <= 0 || h.n_layer < 0 || h.n_head <= 0 || h.n_head_kv <= 0 ||
+      h.head_dim <= 0 || (h.head_dim & 1) || h.n_ff <= 0 || h.n_head % h.n_head_kv != 0 ||
+      !(h.rms_eps >= 0.f) || !(h.rope_theta > 0.f)) {
+    set_err("invalid hparams");
+    return nullptr;
+  }
+  if (h.weight_dtype != TDF_F32 && h.weight_dtype != TDF_BF16) { set_err("weight_dtype must be F32 or BF16"); return nullptr; }
+  const int G = h.n_head / h.n_head_kv;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8)) { set_err("n_head / n_head_kv must be 1, 2, 4 or 8"); return nullptr; }
+  if (!(h.head_dim == 16 || h.head_dim == 32 || h.head_dim == 64 || h.head_dim == 128)) {
+    set_err("head_dim must be 16, 32, 64 or 128");
+    return nullptr;
+  }
+  if (!w->token_embd || !w->output_norm || (h.n_layer > 0 && !w->layers)) { set_err("missing weight pointer"); return nullptr; }
+  for (int l = 0; l < h.n_layer; ++l) {
+    const tdf_layer_weights& L = w->layers[l];
+    if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.ffn_norm || !L.w_gate || !L.w_up || !L.w_down) {
+      set_err("missing layer weight pointer");
+      return nullptr;
+    }
+  }
+  tdf_model* m = new tdf_model();
+  m->hp = h;
+  m->token_embd = w->token_embd;
+  m->output_norm = (const float*)w->output_norm;
+  m->output = w->output ? w->output : w->token_embd;
+  m->layers.assign(w->layers, w->layers + h.n_layer);
+  return m;
+}
+
+extern "C" void tdf_model_free(tdf_model* m) { delete m; }
+
+// ---------------------------------------------------------------------------
+// context
+
+extern "C" tdf_context* tdf_context_create(const tdf_model* m, const tdf_context_params* p) {
+  if (!m || !p) { set_err("model or params is NULL"); return nullptr; }
+  if (p->n_ctx <= 0 || p->n_seq_max < 1 || p->n_seq_max > kMaxSeq || p->n_ubatch <= 0 || p->n_batch <= 0) {
+    set_err("invalid context parameters");
+    return nullptr;
+  }
+  if (p->kv_dtype != TDF_F32 && p->kv_dtype != TDF_F16 && p->kv_dtype != TDF_BF16) { set_err("invalid kv_dtype"); return nullptr; }
+  tdf_context* c = new tdf_context();
+  c->m = m;
+  c->n_ctx = p->n_ctx;
+  c->n_batch = std::min(p->n_ctx, p->n_batch);
+  c->n_ubatch = std::min(c->n_batch, p->n_ubatch);
+  c->n_seq_max = p->n_seq_max;
+  c->kv_dtype = p->kv_dtype;
+  c->output_all = p->output_all != 0;
+  c->dry_run = (p->flags & TDF_CTX_DRY_RUN) != 0;
+  c->profile = !c->dry_run && (p->flags & TDF_CTX_PROFILE) != 0;
+  c->book.init(c->n_ctx, c->n_seq_max);
+  if (c->dry_run) return c;
+
+  const tdf_hparams& h = m->hp;
+  const int d = h.n_embd, H = h.n_head, Hkv = h.n_head_kv, hd = h.head_dim, F = h.n_ff;
+  const int U = c->n_ubatch;
+  int rc = TDF_OK;
+  auto A = [&](void** ptr, size_t bytes) {
+    if (rc == TDF_OK) rc = ctx_alloc(c, ptr, bytes);
+  };
+  if (p->stream) {
+    c->stream = (hipStream_t)p->stream;
+  } else {
+    if (hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking) != hipSuccess) {
+      set_err("stream creation failed");
+      delete c;
+      return nullptr;
+    }
+    c->own_stream = true;
+  }
+  c->kv_layer_bytes = (size_t)Hkv * c->n_ctx * hd * dtype_size(c->kv_dtype);
+  A(&c->kv, c->kv_layer_bytes * 2 * std::max(1, h.n_layer));
+  A((void**)&c->cell_list, (size_t)c->n_seq_max * c->n_ctx * sizeof(int32_t));
+  A((void**)&c->inv_freq, (size_t)(hd / 2) * sizeof(double));
+  A((void**)&c->x, (size_t)U * d * 4);
+  A((void**)&c->xs, (size_t)U * d * 4);
+  A((void**)&c->act, (size_t)U * d * 4);
+  A((void**)&c->q, (size_t)U * H * hd * 4);
+  A((void**)&c->o, (size_t)U * H * hd * 4);
+  A((void**)&c->mb, (size_t)U * F * 4);
+  A((void**)&c->h16, (size_t)U * d * 2);
+  A((void**)&c->o16, (size_t)U * H * hd * 2);
+  A((void**)&c->m16, (size_t)U * F * 2);
+  c->part_rows = std::max((size_t)std::min(U, kDecodeMaxT) * H * kChunkCapDecode,
+                          (size_t)U * H * kChunkCapPrefill);
+  A((void**)&c->part_acc, c->part_rows * hd * 4);
+  A((void**)&c->part_ml, c->part_rows * 2 * 4);
+  // per-call integers: 5 int32 per token + selected rows, then int64 list writes
+  c->ints_bytes = staging_i64_base(c->n_batch) + (size_t)2 * c->n_batch * c->n_seq_max * 8;
+  A(&c->ints, c->ints_bytes);
+  if (rc == TDF_OK && hipHostMalloc((void**)&c->ints_host, c->ints_bytes, hipHostMallocDefault) != hipSuccess) {
+    set_err("pinned staging allocation failed");
+    rc = TDF_E_ALLOC;
+  }
+  if (rc == TDF_OK) rc = ensure_logits(c, 1);
+  if (rc == TDF_OK) {
+    std::vector<double> inv(hd / 2);
+    for (int i = 0; i < hd / 2; ++i) inv[i] = std::pow((double)h.rope_theta, -2.0 * i / hd);
+    if (hipMemcpy(c->inv_freq, inv.data(), inv.size() * sizeof(double), hipMemcpyHostToDevice) != hipSuccess) {
+      set_err("upload of rope frequencies failed");
+      rc = TDF_E_DEVICE;
+    }
+  }
+  if (rc != TDF_OK) {
+    ctx_release(c);
+    delete c;
+    return nullptr;
+  }
+  return c;
+}
+
+extern "C" void tdf_context_free(tdf_context* c) {
+  if (!c) return;
+  if (c->stream) (void)hipStreamSynchronize(c->stream);
+  ctx_release(c);
+  delete c;
+}
+
+// ---------------------------------------------------------------------------
+// forward pass of one ubatch
+
+struct UbatchDev {
+  int T = 0, R = 0;
+  const int32_t *tokens, *pos, *slots, *list_off, *n_vis, *sel;
+  const int64_t* list_writes;
+  int n_list_writes = 0;
+  int nvis_max = 0;
+  int out_row0 = 0;  // first logits row of this ubatch
+};
+
+static int run_linear(tdf_context* c, LinearArgs& a, bool mfma, int op) {
+  const int slot = prof_begin(c, op, mfma);
+  hipError_t e = mfma ? launch_linear_gemm(a, c->stream) : launch_linear_gemv(a, c->stream);
+  prof_end(c, slot);
+  if (e != hipSuccess) {
+    set_err(std::string("linear launch failed: ") + hipGetErrorString(e));
+    return TDF_E_DEVICE;
+  }
+  return TDF_OK;
+}
+
+static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
+  const tdf_model* m = c->m;
+  const tdf_hparams& h = m->hp;
+  const int d = h.n_embd, H = h.n_head, Hkv = h.n_head_kv, hd = h.head_dim, F = h.n_ff, V = h.n_vocab;
+  const int L = h.n_layer;
+  const bool wbf16 = h.weight_dtype == TDF_BF16;
+  hipStream_t s = c->stream;
+  int T = u.T;
+
+  const bool ub_mfma = wbf16 && T > kDecodeMaxT;
+  int ps = prof_begin(c, TDF_OP_EMBED, ub_mfma);
+  TDF_HIP(launch_embed(m->token_embd, wbf16, u.tokens, T, d, c->x, s));
+  TDF_HIP(launch_scatter(c->cell_list, u.list_writes, u.n_list_writes, s));
+  prof_end(c, ps);
+
+  auto use_mfma = [&](int rows, int K) { return wbf16 && rows > kDecodeMaxT && K % 64 == 0; };
+  float* cur = c->x;  // residual rows being carried
+  for (int l = 0; l < L; ++l) {
+    const tdf_layer_weights& W = m->layers[l];
+    // attention block
+    const bool big = use_mfma(T, d);
+    ps = prof_begin(c, TDF_OP_NORM, big);
+    TDF_HIP(launch_rmsnorm(cur, (const float*)W.attn_norm, T, d, h.rms_eps, big ? nullptr : c->act,
+                           big ? c->h16 : nullptr, s));
+    prof_end(c, ps);
+    LinearArgs qa;
+    qa.w0 = W.wq; qa.w1 = W.wk; qa.w2 = W.wv;
+    qa.n0 = H * hd; qa.n1 = Hkv * hd; qa.n2 = Hkv * hd;
+    qa.K = d; qa.T = T; qa.weight_bf16 = wbf16;
+    qa.act_f32 = c->act; qa.act_bf16 = c->h16;
+    qa.epi = EPI_QKV;
+    qa.q_out = c->q;
+    qa.k_cache = kv_k(c, l); qa.v_cache = kv_v(c, l);
+    qa.kv_dtype = c->kv_dtype; qa.n_ctx = c->n_ctx; qa.head_dim = hd;
+    qa.slots = u.slots; qa.pos = u.pos; qa.inv_freq = c->inv_freq;
+    if (int rc = run_linear(c, qa, big, TDF_OP_QKV)) return rc;
+
+    AttnArgs at;
+    at.q = c->q;
+    at.k_cache = kv_k(c, l); at.v_cache = kv_v(c, l);
+    at.kv_dtype = c->kv_dtype;
+    at.cell_list = c->cell_list; at.list_off = u.list_off; at.n_vis = u.n_vis;
+    at.T = T; at.H = H; at.Hkv = Hkv; at.hd = hd; at.n_ctx = c->n_ctx;
+    const int cap = T > kDecodeMaxT ? kChunkCapPrefill : kChunkCapDecode;
+    int chunk = (u.nvis_max + cap - 1) / cap;
+    chunk = std::max(64, (chunk + 63) / 64 * 64);
+    at.chunk = chunk;
+    at.n_chunks = (u.nvis_max + chunk - 1) / chunk;
+    at.part_acc = c->part_acc; at.part_ml = c->part_ml;
+    at.out = c->o;
+    at.out_bf16 = big ? c->o16 : nullptr;
+    ps = prof_begin(c, TDF_OP_ATTN, big);
+    TDF_HIP(launch_attention_decode(at, s));
+    prof_end(c, ps);
+
+    LinearArgs oa;
+    oa.w0 = W.wo; oa.n0 = d; oa.K = H * hd; oa.T = T; oa.weight_bf16 = wbf16;
+    oa.act_f32 = c->o; oa.act_bf16 = c->o16;
+    oa.epi = EPI_RESIDUAL; oa.out = cur; oa.ldo = d;
+    if (int rc = run_linear(c, oa, big && use_mfma(T, H * hd), TDF_OP_WO)) return rc;
+
+    if (l == L - 1) {
+      // last layer: keep only the rows whose logits are wanted
+      if (u.R == 0) return TDF_OK;
+      ps = prof_begin(c, TDF_OP_NORM, big);
+      TDF_HIP(launch_gather_rows(cur, u.sel, u.R, d, c->xs, s));
+      prof_end(c, ps);
+      cur = c->xs;
+      T = u.R;
+    }
+    // MLP block
+    const bool bigm = use_mfma(T, d) && use_mfma(T, F);
+    ps = prof_begin(c, TDF_OP_NORM, bigm);
+    TDF_HIP(launch_rmsnorm(cur, (const float*)W.ffn_norm, T, d, h.rms_eps, bigm ? nullptr : c->act,
+                           bigm ? c->h16 : nullptr, s));
+    prof_end(c, ps);
+    LinearArgs ga;
+    ga.w0 = W.w_gate; ga.w1 = W.w_up; ga.n0 = F; ga.K = d; ga.T = T; ga.weight_bf16 = wbf16;
+    ga.act_f32 = c->act; ga.act_bf16 = c->h16;
+    ga.epi = EPI_SWIGLU; ga.out = c->mb; ga.out_bf16 = c->m16; ga.ldo = F;
+    if (int rc = run_linear(c, ga, bigm, TDF_OP_GATE_UP)) return rc;
+    LinearArgs da;
+    da.w0 = W.w_down; da.n0 = d; da.K = F; da.T = T; da.weight_bf16 = wbf16;
+    da.act_f32 = c->mb; da.act_bf16 = c->m16;
+    da.epi = EPI_RESIDUAL; da.out = cur; da.ldo = d;
+    if (int rc = run_linear(c, da, bigm, TDF_OP_DOWN)) return rc;
+  }
+  if (L == 0) {
+    if (u.R == 0) return TDF_OK;
+    TDF_HIP(launch_gather_rows(cur, u.sel, u.R, d, c->xs, s));
+    cur = c->xs;
+    T = u.R;
+  }
+  // output norm + LM head into this ubatch's logits rows
+  const bool bigo = use_mfma(T, d);
+  ps = prof_begin(c, TDF_OP_NORM, bigo);
+  TDF_HIP(launch_rmsnorm(cur, m->output_norm, T, d, h.rms_eps, bigo ? nullptr : c->act,
+                         bigo ? c->h16 : nullptr, s));
+  prof_end(c, ps);
+  LinearArgs la;
+  la.w0 = m->output; la.n0 = V; la.K = d; la.T = T; la.weight_bf16 = wbf16;
+  la.act_f32 = c->act; la.act_bf16 = c->h16;
+  la.epi = EPI_STORE; la.out = c->logits + (size_t)u.out_row0 * V; la.ldo = V;
+  return run_linear(c, la, bigo, TDF_OP_LM_HEAD);
+}
+
+// ---------------------------------------------------------------------------
+// decode
+
+extern "C" int32_t tdf_decode(tdf_context* c, const tdf_batch* b) {
+  if (!c) { set_err("context is NULL"); return TDF_E_INVALID; }
+  g_err.clear();
+  Intake in;
+  std::string err;
+  int rc = intake_batch(c->book, b, c->m->hp.n_vocab, c->n_batch, c->output_all, in, err);
+  if (rc != TDF_OK) { set_err(err); return rc; }
+  const int n = in.n_tokens;
+  if (c->book.n_free() < n) {
+    set_err("not enough free KV cells");
+    return TDF_NO_SLOT;
+  }
+  int n_out = 0;
+  for (int i = 0; i < n; ++i) n_out += in.output[i] ? 1 : 0;
+  if (!c->dry_run) {
+    rc = ensure_logits(c, std::max(1, n_out));
+    if (rc != TDF_OK) return rc;
+  }
+  c->n_outputs = n_out;
+  c->out_ids.clear();
+  c->row_of.assign(n, -1);
+  c->last_slots.assign(n, -1);
+  c->logits_host.clear();
+  c->host_row_ok.assign(n_out, 0);
+  for (int i = 0; i < n; ++i)
+    if (in.output[i]) {
+      c->row_of[i] = (int32_t)c->out_ids.size();
+      c->out_ids.push_back(i);
+    }
+
+  // integers of every ubatch of this call go into one pinned staging area;
+  // region of a ubatch: tokens, pos, slots, list_off, n_vis, sel | list writes
+  size_t i32_off = 0, i64_off = 0;
+  const size_t i64_base = staging_i64_base(c->n_batch);
+  std::vector<int32_t> slots;
+  std::vector<int64_t> writes;
+  int out_row = 0;
+  for (int u0 = 0; u0 < n; u0 += c->n_ubatch) {
+    const int T = std::min(c->n_ubatch, n - u0);
+    if (!c->book.find_slots(T, slots)) {
+      set_err("internal: cells vanished during decode");
+      return TDF_E_DEVICE;
+    }
+    writes.clear();
+    std::vector<int32_t> list_off(T), n_vis(T), sel;
+    int nvis_max = 0;
+    for (int i = 0; i < T; ++i) {
+      const int t = u0 + i;
+      const int32_t idx = c->book.place(slots[i], in.pos[t], in.seq_mask[t], in.seq0[t], &writes);
+      list_off[i] = in.seq0[t] * c->n_ctx;
+      n_vis[i] = idx + 1;
+      nvis_max = std::max(nvis_max, n_vis[i]);
+      c->last_slots[t] = slots[i];
+      if (in.output[t]) sel.push_back(i);
+    }
+    if (c->dry_run) continue;
+
+    int32_t* h32 = (int32_t*)(c->ints_host + i32_off * 4);
+    int32_t* d32 = (int32_t*)((char*)c->ints + i32_off * 4);
+    memcpy(h32, &in.token[u0], T * 4);
+    memcpy(h32 + T, &in.pos[u0], T * 4);
+    memcpy(h32 + 2 * T, slots.data(), T * 4);
+    memcpy(h32 + 3 * T, list_off.data(), T * 4);
+    memcpy(h32 + 4 * T, n_vis.data(), T * 4);
+    if (!sel.empty()) memcpy(h32 + 5 * T, sel.data(), sel.size() * 4);
+    const size_t n32 = 5 * (size_t)T + sel.size();
+    int64_t* h64 = (int64_t*)(c->ints_host + i64_base + i64_off * 8);
+    int64_t* d64 = (int64_t*)((char*)c->ints + i64_base + i64_off * 8);
+    if (!writes.empty()) memcpy(h64, writes.data(), writes.size() * 8);
+    TDF_HIP(hipMemcpyAsync(d32, h32, n32 * 4, hipMemcpyHostToDevice, c->stream));
+    if (!writes.empty())
+      TDF_HIP(hipMemcpyAsync(d64, h64, writes.size() * 8, hipMemcpyHostToDevice, c->stream));
+
+    UbatchDev ud;
+    ud.T = T;
+    ud.R = (int)sel.size();
+    ud.tokens = d32; ud.pos = d32 + T; ud.slots = d32 + 2 * T;
+    ud.list_off = d32 + 3 * T; ud.n_vis = d32 + 4 * T; ud.sel = d32 + 5 * T;
+    ud.list_writes = d64;
+    ud.n_list_writes = (int)writes.size() / 2;
+    ud.nvis_max = nvis_max;
+    ud.out_row0 = out_row;
+    rc = forward_ubatch(c, ud);
+    if (rc != TDF_OK) return rc;
+    out_row += ud.R;
+    i32_off += (n32 + 3) & ~(size_t)3;
+    i64_off += writes.size();
+  }
+  if (c->dry_run) return TDF_OK;
+  if (n_out > 0) {
+    const int ps = prof_begin(c, TDF_OP_ARGMAX, false);
+    TDF_HIP(launch_argmax(c->logits, n_out, c->m->hp.n_vocab, c->d_tok, c->stream));
+    prof_end(c, ps);
+    TDF_HIP(hipMemcpyAsync(c->h_tok, c->d_tok, (size_t)n_out * 4, hipMemcpyDeviceToHost, c->stream));
+  }
+  TDF_HIP(hipStreamSynchronize(c->stream));
+  prof_collect(c);
+  return TDF_OK;
+}
+
+extern "C" int32_t tdf_n_outputs(const tdf_context* c) { return c ? c->n_outputs : TDF_E_INVALID; }
+
+extern "C" int32_t tdf_output_ids(const tdf_context* c, int32_t* out) {
+  if (!c) return TDF_E_INVALID;
+  if (out) std::copy(c->out_ids.begin(), c->out_ids.end(), out);
+  return c->n_outputs;
+}
+
+extern "C" const float* tdf_get_logits_ith(tdf_context* c, int32_t i) {
+  if (!c || c->dry_run || i < 0 || i >= (int32_t)c->row_of.size() || c->row_of[i] < 0) {
+    set_err("no logits for this batch index");
+    return nullptr;
+  }
+  const int V = c->m->hp.n_vocab;
+  const int r = c->row_of[i];
+  if (c->logits_host.size() < (size_t)c->n_outputs * V) c->logits_host.resize((size_t)c->n_outputs * V);
+  if (!c->host_row_ok[r]) {
+    if (hipMemcpy(&c->logits_host[(size_t)r * V], c->logits + (size_t)r * V, (size_t)V * 4,
+                  hipMemcpyDeviceToHost) != hipSuccess) {
+      set_err("logits copy failed");
+      return nullptr;
+    }
+    c->host_row_ok[r] = 1;
+  }
+  return &c->logits_host[(size_t)r * V];
+}
+
+extern "C" const float* tdf_get_logits_device(tdf_context* c) {
+  if (!c || c->dry_run) return nullptr;
+  return c->logits;
+}
+
+extern "C" int32_t tdf_argmax_ith(const tdf_context* c, int32_t i) {
+  if (!c || c->dry_run || i < 0 || i >= (int32_t)c->row_of.size() || c->row_of[i] < 0) return TDF_E_INVALID;
+  return c->h_tok[c->row_of[i]];
+}
+
+extern "C" int32_t tdf_seq_pos_max(const tdf_context* c, int32_t s) {
+  if (!c || s < 0 || s >= c->n_seq_max) return TDF_E_INVALID;
+  return c->book.seq_pos_max(s);
+}
+
+extern "C" int32_t tdf_kv_clear(tdf_context* c) {
+  if (!c) return TDF_E_INVALID;
+  if (c->stream) (void)hipStreamSynchronize(c->stream);
+  c->book.clear();
+  c->n_outputs = 0;
+  c->out_ids.clear();
+  c->row_of.clear();
+  c->logits_host.clear();
+  c->host_row_ok.clear();
+  return TDF_OK;
+}
+
+extern "C" int32_t tdf_kv_cell(const tdf_context* c, int32_t cell, int32_t* pos, uint64_t* seq_mask) {
+  if (!c || cell < 0 || cell >= c->n_ctx) return TDF_E_INVALID;
+  if (pos) *pos = c->book.cell_pos(cell);
+  if (seq_mask) *seq_mask = c->book.cell_seq(cell);
+  return TDF_OK;
+}
+
+extern "C" int32_t tdf_last_slots(const tdf_context* c, int32_t* slots) {
+  if (!c) return TDF_E_INVALID;
+  if (slots) std::copy(c->last_slots.begin(), c->last_slots.end(), slots);
+  return (int32_t)c->last_slots.size();
+}
+
+// ---------------------------------------------------------------------------
+// cache import
+
+template <typename E>
+__global__ void kv_import_kernel(E* __restrict__ dst, const E* __restrict__ src,
+                                 const int32_t* __restrict__ cells, int n, int Hkv, int hd, int n_ctx) {
+  const int64_t total = (int64_t)n * Hkv * hd;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int d = (int)(i % hd);
+    const int g = (int)((i / hd) % Hkv);
+    const int p = (int)(i / ((int64_t)hd * Hkv));
+    dst[((int64_t)g * n_ctx + cells[p]) * hd + d] = src[i];
+  }
+}
+
+extern "C" int32_t tdf_kv_import(tdf_context* c, int32_t s, int32_t pos0, int32_t n,
+                                 const void* const* k_layers, const void* const* v_layers) {
+  if (!c || s < 0 || s >= c->n_seq_max || n <= 0 || pos0 < 0 || pos0 <= c->book.seq_pos_max(s)) {
+    set_err("invalid kv_import arguments");
+    return TDF_E_INVALID;
+  }
+  const int L = c->m->hp.n_layer;
+  if (!c->dry_run && L > 0 && (!k_layers || !v_layers)) { set_err("missing layer arrays"); return TDF_E_INVALID; }
+  if (!c->dry_run)
+    for (int l = 0; l < L; ++l)
+      if (!k_layers[l] || !v_layers[l]) { set_err("missing layer array"); return TDF_E_INVALID; }
+  std::vector<int32_t> slots;
+  if (!c->book.find_slots(n, slots)) { set_err("not enough free KV cells"); return TDF_NO_SLOT; }
+  std::vector<int64_t> writes;
+  for (int i = 0; i < n; ++i) c->book.place(slots[i], pos0 + i, 1ull << s, s, &writes);
+  c->last_slots = slots;
+  if (c->dry_run) return TDF_OK;
+  const int Hkv = c->m->hp.n_head_kv, hd = c->m->hp.head_dim;
+  void *dcells = nullptr, *dwrites = nullptr;
+  TDF_HIP(hipMallocAsync(&dcells, (size_t)n * 4, c->stream));
+  TDF_HIP(hipMallocAsync(&dwrites, writes.size() * 8, c->stream));
+  TDF_HIP(hipMemcpyAsync(dcells, slots.data(), (size_t)n * 4, hipMemcpyHostToDevice, c->stream));
+  TDF_HIP(hipMemcpyAsync(dwrites, writes.data(), writes.size() * 8, hipMemcpyHostToDevice, c->stream));
+  TDF_HIP(launch_scatter(c->cell_list, (const int64_t*)dwrites, (int)writes.size() / 2, c->stream));
+  const int64_t total = (int64_t)n * Hkv * hd;
+  const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
+  for (int l = 0; l < L; ++l) {
+    if (c->kv_dtype == TDF_F32) {
+      kv_import_kernel<float><<<blocks, 256, 0, c->stream>>>((float*)kv_k(c, l), (const float*)k_layers[l],
+                                                            (const int32_t*)dcells, n, Hkv, hd, c->n_ctx);
+      kv_import_kernel<float><<<blocks, 256, 0, c->stream>>>((float*)kv_v(c, l), (const float*)v_layers[l],
+                                                            (const int32_t*)dcells, n, Hkv, hd, c->n_ctx);
+    } else {
+      kv_import_kernel<uint16_t><<<blocks, 256, 0, c->stream>>>((uint16_t*)kv_k(c, l), (const uint16_t*)k_layers[l],
+                                                               (const int32_t*)dcells, n, Hkv, hd, c->n_ctx);
+      kv_import_kernel<uint16_t><<<blocks, 256, 0, c->stream>>>((uint16_t*)kv_v(c, l), (const uint16_t*)v_layers[l],
+                                                               (const int32_t*)dcells, n, Hkv, hd, c->n_ctx);
+    }
+    TDF_HIP(hipGetLastError());
+  }
+  TDF_HIP(hipFreeAsync(dcells, c->stream));
+  TDF_HIP(hipFreeAsync(dwrites, c->stream));
+  TDF_HIP(hipStreamSynchronize(c->stream));
+  return TDF_OK;
+}
+
+extern "C" int32_t tdf_profile_read(const tdf_context* c, int32_t op, int32_t mfma, int64_t* launches, double* ms) {
+  if (!c || !c->profile || op < 0 || op >= TDF_OP_COUNT) return TDF_E_INVALID;
+  const int slot = 2 * op + (mfma ? 1 : 0);
+  if (launches) *launches = c->prof_n[slot];
+  if (ms) *ms = c->prof_ms[slot];
+  return TDF_OK;
+}
+
+extern "C" int32_t tdf_profile_reset(tdf_context* c) {
+  if (!c || !c->profile) return TDF_E_INVALID;
+  for (int i = 0; i < 2 * TDF_OP_COUNT; ++i) {
+    c->prof_n[i] = 0;
+    c->prof_ms[i] = 0.0;
+  }
+  return TDF_OK;
+}
+
+extern "C" const char* tdf_last_error(void) { return g_err.c_str(); }
