@@ -42,6 +42,11 @@ Readings where the pages are silent or inconsistent:
   first sequence id and whose position is <= the token's position; this
   includes itself and earlier tokens of its own ubatch.  Cached K is stored
   after RoPE.
+* The cache holds K and V in its element type (the Ollama cache carries a
+  DType; the llama.cpp walkthrough's KV-cache section names the cache type
+  as a storage setting): with ``kv_dtype`` set, each stored value is the
+  float64 result rounded to nearest-even in that type (f32, f16 or bf16);
+  without it the cache keeps float64.
 * Logits: one row per flagged token, in batch order, accumulated over the
   ubatches of the call.  Greedy ties go to the lowest index.
 """
@@ -78,7 +83,8 @@ class DecodeResult:
 
 
 def _round_storage(a: np.ndarray, dtype: Optional[str]) -> np.ndarray:
-    """Optional diagnosis switch: round stored K/V to the cache's type."""
+    """Value of ``a`` once stored in the cache's element type (round to
+    nearest, ties to even); float64 when no type is given."""
     if dtype is None or dtype == "f64":
         return a
     if dtype == "f32":
@@ -96,7 +102,7 @@ def _round_storage(a: np.ndarray, dtype: Optional[str]) -> np.ndarray:
 class OracleContext:
     def __init__(self, model: Optional[OracleModel], n_ctx: int, n_batch: Optional[int] = None,
                  n_ubatch: int = 512, n_seq_max: int = 1, output_all: bool = False,
-                 compute: bool = True, kv_round: Optional[str] = None):
+                 compute: bool = True, kv_dtype: Optional[str] = None):
         if n_ctx <= 0 or n_seq_max < 1 or n_seq_max > MAX_SEQ:
             raise ValueError("invalid context parameters")
         self.model = model
@@ -110,7 +116,7 @@ class OracleContext:
         self.n_seq_max = int(n_seq_max)
         self.output_all = bool(output_all)
         self.compute = compute and model is not None
-        self.kv_round = kv_round
+        self.kv_dtype = kv_dtype
         self.cell_pos = np.full(self.n_ctx, -1, dtype=np.int64)   # -1 = free
         self.cell_seq = np.zeros(self.n_ctx, dtype=np.uint64)     # bit s = belongs to seq s
         self.k_cache: dict = {}
@@ -272,8 +278,8 @@ class OracleContext:
             q = rope(q, pos, theta)
             k = rope(k, pos, theta)
             kc, vc = self._layer_cache(l)
-            kc[cells] = _round_storage(k, self.kv_round)
-            vc[cells] = _round_storage(v, self.kv_round)
+            kc[cells] = _round_storage(k, self.kv_dtype)
+            vc[cells] = _round_storage(v, self.kv_dtype)
             o = np.stack([attend(q[t], kc[visible[t]], vc[visible[t]]) for t in range(T)])
             x = x + o.reshape(T, H * hd) @ m.w(p + "attn_output.weight").T
             if l == L - 1:

@@ -1,5 +1,6 @@
 """GPU parity: the HIP path (through the C ABI) against the float64 oracle on
-the same seeded inputs.
+the same seeded inputs, the oracle's cache holding K/V in the same element
+type as the GPU context's cache.
 
 Logits: max-abs <= 3e-2 and rel-L2 <= 1e-2 for bf16 weights; 1e-4 / 1e-5 for
 the float32 model.  Greedy tokens: equal wherever the oracle's top-2 gap
@@ -30,7 +31,7 @@ def run_pair(cfg, tensors, ctx_kw, calls, tol, kv_dtype, label):
     import transformer_decode_forward_amd as tdf
     gm = device_model(cfg, tensors)
     gc = tdf.Context(gm, kv_dtype=kv_dtype, **ctx_kw)
-    oc = OracleContext(oracle_model(cfg, tensors), **ctx_kw)
+    oc = OracleContext(oracle_model(cfg, tensors), kv_dtype=kv_dtype, **ctx_kw)
     for k, call in enumerate(calls):
         call = dict(call)
         rg = gc.decode(**call)
@@ -49,7 +50,7 @@ def teacher_forced(cfg, tensors, n_ctx, prompt, steps, tol, kv_dtype, n_ubatch=5
     import transformer_decode_forward_amd as tdf
     gm = device_model(cfg, tensors)
     gc = tdf.Context(gm, n_ctx=n_ctx, n_ubatch=n_ubatch, kv_dtype=kv_dtype)
-    oc = OracleContext(oracle_model(cfg, tensors), n_ctx=n_ctx, n_ubatch=n_ubatch)
+    oc = OracleContext(oracle_model(cfg, tensors), n_ctx=n_ctx, n_ubatch=n_ubatch, kv_dtype=kv_dtype)
     assert gc.decode(prompt) == 0, tdf.tdf_last_error()
     ro = oc.decode(prompt)
     assert gc.last_slots() == ro.slots
@@ -125,7 +126,7 @@ def test_small_kv_import_then_decode():
     kd = [to_device(k) for k in ks]
     vd = [to_device(v) for v in vs]
     assert gc.kv_import(0, 0, P, [t.data_ptr() for t in kd], [t.data_ptr() for t in vd]) == 0
-    oc = OracleContext(oracle_model(cfg, w), n_ctx=512)
+    oc = OracleContext(oracle_model(cfg, w), n_ctx=512, kv_dtype="bf16")
     assert oc.kv_import(0, 0, P, ks, vs) == 0
     for t in tdf_synth.prompt(cfg, 2, 3):
         assert gc.decode([int(t)]) == 0

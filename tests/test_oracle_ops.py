@@ -188,3 +188,21 @@ def test_causal_attention_against_torch_sdpa():
     tv = torch.from_numpy(np.repeat(v, H // Hkv, axis=1)).transpose(0, 1)
     ref = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True).transpose(0, 1).numpy()
     np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-13)
+
+
+# ---- cache storage type ------------------------------------------------------
+
+def test_cache_storage_rounding_matches_numpy_and_bit_rule():
+    from oracle.context import _round_storage
+    x = rng.normal(size=4000) * 3
+    np.testing.assert_array_equal(_round_storage(x, "f32"), x.astype(np.float32).astype(np.float64))
+    np.testing.assert_array_equal(_round_storage(x, "f16"), x.astype(np.float16).astype(np.float64))
+    b = _round_storage(x, "bf16")
+    # bf16 keeps 8 significant bits: the result is a bf16 value, the nearest one
+    u = b.astype(np.float32).view(np.uint32)
+    assert np.all(u & 0xFFFF == 0)
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(x))) - 7)
+    assert np.all(np.abs(b - x) <= ulp / 2 + 1e-300)
+    # ties go to even: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7
+    assert _round_storage(np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8]), "bf16").tolist() == [1.0, 1 + 2 ** -6]
+    assert _round_storage(x, None) is x
