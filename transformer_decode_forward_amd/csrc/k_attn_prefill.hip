@@ -1,0 +1,255 @@
+// Prefill attention on the gfx950 matrix cores (flash-style, online softmax).
+//
+// Scaled dot-product attention of the ubatch's queries over the cached keys
+// and values of their sequence, causal by position (Ollama engine page,
+// "Deep dive: the Llama forward pass in Go" and "KV Cache: memory for causal
+// attention"; llama.cpp walkthrough, "KV-cache and the Prefill / Decode
+// stages").  Query head j reads KV head j / (n_head / n_head_kv).
+//
+// Block = one query tile (up to 32 tokens of one sequence) x one KV head;
+// wave w of the block handles query head g*G + w, so each K/V tile staged in
+// LDS serves the G heads of the group.  Per 64-cell K/V tile a wave computes
+//   S^T = K Q^T      (32x32x16 MFMA: lane = query, registers = cells)
+// so a query's 64 scores sit in two lanes (lane and lane^32); the running
+// max and sum need one cross-lane exchange.  The probabilities are then
+// already in the B-operand layout of
+//   O^T += V^T P^T   (lane = query, registers = head dims)
+// with V staged transposed in LDS, read in the same cell order.  The rescale
+// by exp(m_old - m_new) is per lane.  Cells come from the sequence's
+// position-ordered cell list; token t sees the first n_vis[t] entries.
+//
+// K and V are exact in their cache type; Q and the probabilities P are split
+// into a pair hi + lo of the MFMA type (hi = round(x), lo = round(x - hi)),
+// each product taking two MFMAs, so that the scores and the weighted sums keep
+// about 16 significant bits, as the projections do.
+//
+// With n_splits > 1 each block covers one range of `chunk` list entries and
+// writes (max, sum, unnormalised accumulator) partials, merged afterwards by
+// the decode merge kernel.
+#include "k_common.hpp"
+#include "kernels.hpp"
+#include "tdf.h"
+
+namespace tdf {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+template <typename KvT> struct MfmaOf;
+template <> struct MfmaOf<kv_bf16> {
+  typedef bf16x8 vec;
+  typedef __bf16 elem;
+  __device__ __forceinline__ static f32x16 mma(vec a, vec b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct MfmaOf<kv_f16> {
+  typedef f16x8 vec;
+  typedef _Float16 elem;
+  __device__ __forceinline__ static f32x16 mma(vec a, vec b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+constexpr int kQT = 32;   // queries per tile
+constexpr int kCT = 64;   // cells per K/V tile
+
+template <typename KvT, int HD, int G>
+__global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) attn_prefill_kernel(PrefillAttnArgs a) {
+  typedef MfmaOf<KvT> M;
+  typedef typename M::vec vec;
+  constexpr int KP = HD + 8;     // K row pitch (elements)
+  constexpr int VP = kCT + 8;    // V^T row pitch (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t k_s[kCT * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_s[HD * VP];
+
+  const int tile = blockIdx.x, g = blockIdx.y, split = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = g * G + w;
+  const int ql = lane & 31, qg = lane >> 5;
+  const int t = a.tile_tokens[tile * kQT + ql];      // -1 for padding
+  const int nvis = t >= 0 ? a.n_vis[t] : 0;
+  const int tile_nvis = a.tile_nvis_max[tile];
+  const int c_lo = split * a.chunk;
+  if (c_lo >= tile_nvis) return;
+  const int c_hi = min(tile_nvis, c_lo + a.chunk);
+  const int32_t* cells = a.cell_list + a.tile_list_off[tile];
+  const uint16_t* kc = (const uint16_t*)a.k_cache + (int64_t)g * a.n_ctx * HD;
+  const uint16_t* vc = (const uint16_t*)a.v_cache + (int64_t)g * a.n_ctx * HD;
+  const float scale = rsqrtf((float)HD);
+
+  typedef typename M::elem E;
+  // Q^T fragments (B operand), hi and lo: lane holds Q[query][ks*16 + qg*8 + 0..7]
+  vec qh[HD / 16], qlo[HD / 16];
+#pragma unroll
+  for (int ks = 0; ks < HD / 16; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = t >= 0 ? a.q[((int64_t)t * a.H + h) * HD + ks * 16 + qg * 8 + e] * scale : 0.f;
+      const E hi = (E)v;
+      qh[ks][e] = hi;
+      qlo[ks][e] = (E)(v - (float)hi);
+    }
+  }
+
+  f32x16 o[HD / 32];
+#pragma unroll
+  for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  constexpr int CHUNKS = kCT * HD / 8;  // 16-byte pieces of one K (or V) tile
+  for (int c0 = c_lo; c0 < c_hi; c0 += kCT) {
+    const int nc = min(kCT, c_hi - c0);
+    __syncthreads();
+    for (int i = tid; i < CHUNKS; i += 64 * G) {
+      const int c = i % kCT, dchunk = (i / kCT) * 8;
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (c < nc) {
+        const int64_t row = (int64_t)cells[c0 + c] * HD + dchunk;
+        kv = *(const uint4*)(kc + row);
+        vv = *(const uint4*)(vc + row);
+      }
+      *(uint4*)&k_s[c * KP + dchunk] = kv;
+      const uint16_t* vh = (const uint16_t*)&vv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt_s[(dchunk + e) * VP + c] = vh[e];
+    }
+    __syncthreads();
+
+    // S^T for two 32-cell halves: s[sub][r] <-> cell sub*32 + (r/4)*8 + qg*4 + r%4
+    f32x16 s[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[sub][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < HD / 16; ++ks) {
+        const vec kf = *(const vec*)&k_s[(sub * 32 + ql) * KP + ks * 16 + qg * 8];
+        s[sub] = M::mma(kf, qh[ks], s[sub]);
+        s[sub] = M::mma(kf, qlo[ks], s[sub]);
+      }
+    }
+    // causal / range mask and online softmax for this lane's query
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ci = c0 + sub * 32 + (r >> 2) * 8 + qg * 4 + (r & 3);
+        if (ci >= nvis || ci >= c_hi) s[sub][r] = -INFINITY;
+        tmax = fmaxf(tmax, s[sub][r]);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float m_new = fmaxf(m_run, tmax);
+    const bool live = m_new != -INFINITY;
+    const float alpha = live ? __expf(m_run - m_new) : 1.f;
+    float psum = 0.f;
+    vec ph[2][2], plo[2][2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = live ? __expf(s[sub][r] - m_new) : 0.f;
+        psum += p;
+        const E hi = (E)p;
+        ph[sub][r >> 3][r & 7] = hi;
+        plo[sub][r >> 3][r & 7] = (E)(p - (float)hi);
+      }
+    psum += __shfl_xor(psum, 32, kWave);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    // O^T += V^T P^T; A operand lane: d = dt*32 + ql, cells in P's order
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt) {
+      const uint16_t* vrow = &vt_s[(dt * 32 + ql) * VP];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int cb = sub * 32 + s2 * 16 + qg * 4;
+          const uint2 lo = *(const uint2*)(vrow + cb);
+          const uint2 hi = *(const uint2*)(vrow + cb + 8);
+          const vec vf = __builtin_bit_cast(vec, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          o[dt] = M::mma(vf, ph[sub][s2], o[dt]);
+          o[dt] = M::mma(vf, plo[sub][s2], o[dt]);
+        }
+    }
+  }
+
+  // o[dt][r] <-> head dim dt*32 + (r/4)*8 + qg*4 + r%4 of this lane's query
+  if (t < 0 || nvis <= c_lo) return;
+  if (a.n_splits == 1) {
+    const float inv = 1.f / l_run;
+    const int64_t base = ((int64_t)t * a.H + h) * HD;
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = dt * 32 + i * 8 + qg * 4;
+        const float4 v = make_float4(o[dt][4 * i] * inv, o[dt][4 * i + 1] * inv, o[dt][4 * i + 2] * inv,
+                                     o[dt][4 * i + 3] * inv);
+        if (a.out) *(float4*)&a.out[base + d] = v;
+        if (a.out_hi) {
+          uint16_t h[4], l[4];
+          split_bf16(v.x, h[0], l[0]);
+          split_bf16(v.y, h[1], l[1]);
+          split_bf16(v.z, h[2], l[2]);
+          split_bf16(v.w, h[3], l[3]);
+          *(uint2*)&a.out_hi[base + d] = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+          *(uint2*)&a.out_lo[base + d] = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+        }
+      }
+  } else {
+    const int64_t pb = ((int64_t)t * a.H + h) * a.n_splits + split;
+#pragma unroll
+    for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = dt * 32 + i * 8 + qg * 4;
+        *(float4*)&a.part_acc[pb * HD + d] =
+            make_float4(o[dt][4 * i], o[dt][4 * i + 1], o[dt][4 * i + 2], o[dt][4 * i + 3]);
+      }
+    if (qg == 0) {
+      a.part_ml[pb * 2] = m_run;
+      a.part_ml[pb * 2 + 1] = l_run;
+    }
+  }
+}
+
+template <typename KvT, int HD>
+static hipError_t prefill_attn_hd(const PrefillAttnArgs& a, hipStream_t s) {
+  const int G = a.H / a.Hkv;
+  dim3 grid(a.n_tiles, a.Hkv, a.n_splits);
+  switch (G) {
+    case 1: attn_prefill_kernel<KvT, HD, 1><<<grid, 64, 0, s>>>(a); break;
+    case 2: attn_prefill_kernel<KvT, HD, 2><<<grid, 128, 0, s>>>(a); break;
+    case 4: attn_prefill_kernel<KvT, HD, 4><<<grid, 256, 0, s>>>(a); break;
+    case 8: attn_prefill_kernel<KvT, HD, 8><<<grid, 512, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+bool prefill_attention_supported(int kv_dtype, int head_dim) {
+  return (kv_dtype == TDF_BF16 || kv_dtype == TDF_F16) && (head_dim == 64 || head_dim == 128);
+}
+
+hipError_t launch_attention_prefill(const PrefillAttnArgs& a, hipStream_t s) {
+  if (a.n_tiles <= 0) return hipSuccess;
+  hipError_t e;
+  if (a.kv_dtype == TDF_BF16)
+    e = a.hd == 128 ? prefill_attn_hd<kv_bf16, 128>(a, s) : prefill_attn_hd<kv_bf16, 64>(a, s);
+  else if (a.kv_dtype == TDF_F16)
+    e = a.hd == 128 ? prefill_attn_hd<kv_f16, 128>(a, s) : prefill_attn_hd<kv_f16, 64>(a, s);
+  else
+    return hipErrorInvalidValue;
+  if (e != hipSuccess || a.n_splits == 1) return e;
+  return launch_attention_merge(a.merge, s);
+}
+
+}  // namespace tdf

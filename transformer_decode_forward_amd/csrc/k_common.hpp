@@ -87,6 +87,12 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   }
 }
 
+// x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi): about 16 significant bits
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16(x);
+  lo = f32_to_bf16(x - bf16_to_f32(hi));
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 }  // namespace tdf

@@ -25,9 +25,23 @@ __global__ void __launch_bounds__(256) embed_kernel(const void* __restrict__ tab
                                                     float* __restrict__ x) {
   const int t = blockIdx.x;
   const int64_t row = (int64_t)tokens[t] * d;
-  for (int k = threadIdx.x; k < d; k += blockDim.x) {
-    float v = BF16 ? bf16_to_f32(((const uint16_t*)table)[row + k]) : ((const float*)table)[row + k];
-    x[(int64_t)t * d + k] = v;
+  float* xr = x + (int64_t)t * d;
+  if ((d & 3) == 0) {
+#pragma unroll 4
+    for (int k = threadIdx.x * 4; k < d; k += 1024) {
+      float4 v;
+      if (BF16) {
+        const uint2 u = *(const uint2*)((const uint16_t*)table + row + k);
+        v = make_float4(__builtin_bit_cast(float, u.x << 16), __builtin_bit_cast(float, u.x & 0xFFFF0000u),
+                        __builtin_bit_cast(float, u.y << 16), __builtin_bit_cast(float, u.y & 0xFFFF0000u));
+      } else {
+        v = *(const float4*)((const float*)table + row + k);
+      }
+      *(float4*)(xr + k) = v;
+    }
+  } else {
+    for (int k = threadIdx.x; k < d; k += 256)
+      xr[k] = BF16 ? bf16_to_f32(((const uint16_t*)table)[row + k]) : ((const float*)table)[row + k];
   }
 }
 
@@ -44,14 +58,20 @@ hipError_t launch_embed(const void* table, int weight_bf16, const int32_t* token
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ x,
                                                       const float* __restrict__ g, int d, float eps,
                                                       float* __restrict__ out_f32,
-                                                      uint16_t* __restrict__ out_bf16) {
+                                                      uint16_t* __restrict__ out_hi,
+                                                      uint16_t* __restrict__ out_lo) {
   __shared__ float red[4];
   const int t = blockIdx.x;
   const float* xr = x + (int64_t)t * d;
   float ss = 0.f;
-  for (int k = threadIdx.x; k < d; k += 256) {
-    float v = xr[k];
-    ss += v * v;
+  if ((d & 3) == 0) {
+#pragma unroll 4
+    for (int k = threadIdx.x * 4; k < d; k += 1024) {
+      const float4 v = *(const float4*)(xr + k);
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+  } else {
+    for (int k = threadIdx.x; k < d; k += 256) ss += xr[k] * xr[k];
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
@@ -61,14 +81,15 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
   for (int k = threadIdx.x; k < d; k += 256) {
     float v = xr[k] * r * g[k];
     if (out_f32) out_f32[(int64_t)t * d + k] = v;
-    if (out_bf16) out_bf16[(int64_t)t * d + k] = f32_to_bf16(v);
+    if (out_hi) split_bf16(v, out_hi[(int64_t)t * d + k], out_lo[(int64_t)t * d + k]);
   }
 }
 
 hipError_t launch_rmsnorm(const float* x, const float* g, int T, int d, float eps, float* out_f32,
-                          uint16_t* out_bf16, hipStream_t s) {
+                          uint16_t* out_hi, uint16_t* out_lo, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  rmsnorm_kernel<<<T, 256, 0, s>>>(x, g, d, eps, out_f32, out_bf16);
+  if ((out_hi == nullptr) != (out_lo == nullptr)) return hipErrorInvalidValue;
+  rmsnorm_kernel<<<T, 256, 0, s>>>(x, g, d, eps, out_f32, out_hi, out_lo);
   return hipGetLastError();
 }
 
@@ -105,7 +126,16 @@ __global__ void __launch_bounds__(1024) argmax_kernel(const float* __restrict__ 
   const float* row = logits + (int64_t)blockIdx.x * V;
   float best = -INFINITY;
   int bi = 0x7FFFFFFF;
-  for (int n = threadIdx.x; n < V; n += 1024) argmax_merge(best, bi, row[n], n);
+  const int V4 = (V & 3) == 0 ? V : 0;
+#pragma unroll 8
+  for (int n = threadIdx.x * 4; n < V4; n += 4096) {
+    const float4 v = *(const float4*)(row + n);
+    argmax_merge(best, bi, v.x, n);
+    argmax_merge(best, bi, v.y, n + 1);
+    argmax_merge(best, bi, v.z, n + 2);
+    argmax_merge(best, bi, v.w, n + 3);
+  }
+  for (int n = V4 + threadIdx.x; n < V; n += 1024) argmax_merge(best, bi, row[n], n);
   wave_argmax(best, bi);
   if ((threadIdx.x & 63) == 0) {
     sv[threadIdx.x >> 6] = best;
@@ -160,7 +190,7 @@ __device__ __forceinline__ void kv_put(void* cache, int64_t idx, float v) {
   KvStore<KvT>::store((typename KvStore<KvT>::T*)cache, idx, v);
 }
 
-template <bool BF16, int NT, int EPI, typename KvT>
+template <bool BF16, int NT, int EPI, typename KvT, bool NORM>
 __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt) {
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -189,23 +219,38 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
   }
   const float* act = a.act_f32 + (int64_t)t0 * K;
 
-  float acc0[NT], acc1[NT];
+  float acc0[NT], acc1[NT], ss[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc0[t] = acc1[t] = 0.f;
+  for (int t = 0; t < NT; ++t) acc0[t] = acc1[t] = ss[t] = 0.f;
 
   const bool vec = (K & 7) == 0;
   if (vec) {
-#pragma unroll 2
+    // four 16-byte weight loads per row in flight per lane
+#pragma unroll 4
     for (int k = lane * 8; k < K; k += 512) {
       float w0[8], w1[8];
       load8<BF16>(p0, off0 + k, w0);
       load8<BF16>(p1, off1 + k, w1);
+      float g[8];
+      if (NORM) {
+        const float4 g0 = *(const float4*)(a.norm_g + k);
+        const float4 g1 = *(const float4*)(a.norm_g + k + 4);
+        g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
+        g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+      }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if (t < nt) {
           const float4 x0 = *(const float4*)(act + (int64_t)t * K + k);
           const float4 x1 = *(const float4*)(act + (int64_t)t * K + k + 4);
-          const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          if (NORM) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              ss[t] = fmaf(x[j], x[j], ss[t]);
+              x[j] *= g[j];
+            }
+          }
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             acc0[t] = fmaf(w0[j], x[j], acc0[t]);
@@ -217,10 +262,15 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
   } else {
     for (int k = lane; k < K; k += 64) {
       const float w0 = load1<BF16>(p0, off0 + k), w1 = load1<BF16>(p1, off1 + k);
+      const float g = NORM ? a.norm_g[k] : 1.f;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         if (t < nt) {
-          const float x = act[(int64_t)t * K + k];
+          float x = act[(int64_t)t * K + k];
+          if (NORM) {
+            ss[t] = fmaf(x, x, ss[t]);
+            x *= g;
+          }
           acc0[t] = fmaf(w0, x, acc0[t]);
           acc1[t] = fmaf(w1, x, acc1[t]);
         }
@@ -230,6 +280,11 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
   for (int t = 0; t < NT; ++t) {
     acc0[t] = wave_sum(acc0[t]);
     acc1[t] = wave_sum(acc1[t]);
+    if (NORM) {
+      const float r = 1.0f / sqrtf(wave_sum(ss[t]) / (float)K + a.norm_eps);
+      acc0[t] *= r;
+      acc1[t] *= r;
+    }
   }
   // lane t writes token t
 #pragma unroll
@@ -280,7 +335,10 @@ static hipError_t gemv_launch_t(const LinearArgs& a, hipStream_t s) {
   const int blocks = (waves + 3) / 4;
   for (int t0 = 0; t0 < a.T; t0 += NT) {
     const int nt = a.T - t0 < NT ? a.T - t0 : NT;
-    gemv_kernel<BF16, NT, EPI, KvT><<<blocks, 256, 0, s>>>(a, t0, nt);
+    if (a.norm_g)
+      gemv_kernel<BF16, NT, EPI, KvT, true><<<blocks, 256, 0, s>>>(a, t0, nt);
+    else
+      gemv_kernel<BF16, NT, EPI, KvT, false><<<blocks, 256, 0, s>>>(a, t0, nt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -322,6 +380,29 @@ hipError_t launch_linear_gemv(const LinearArgs& a, hipStream_t s) {
 
 constexpr int kTile = 64;
 
+// 16 bytes of cache elements -> floats
+template <typename KvT> __device__ __forceinline__ void unpack16(uint4 u, float* out);
+template <> __device__ __forceinline__ void unpack16<float>(uint4 u, float* out) {
+  out[0] = __builtin_bit_cast(float, u.x); out[1] = __builtin_bit_cast(float, u.y);
+  out[2] = __builtin_bit_cast(float, u.z); out[3] = __builtin_bit_cast(float, u.w);
+}
+template <> __device__ __forceinline__ void unpack16<kv_bf16>(uint4 u, float* out) {
+  const uint32_t p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    out[2 * j] = __builtin_bit_cast(float, p[j] << 16);
+    out[2 * j + 1] = __builtin_bit_cast(float, p[j] & 0xFFFF0000u);
+  }
+}
+template <> __device__ __forceinline__ void unpack16<kv_f16>(uint4 u, float* out) {
+  const uint32_t p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    out[2 * j] = f16_to_f32((uint16_t)(p[j] & 0xFFFFu));
+    out[2 * j + 1] = f16_to_f32((uint16_t)(p[j] >> 16));
+  }
+}
+
 template <typename KvT, int HD, int G>
 __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
   typedef typename KvStore<KvT>::T ST;
@@ -358,16 +439,28 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
   for (int c0 = c_lo; c0 < c_hi; c0 += kTile) {
     const int nc = min(kTile, c_hi - c0);
     __syncthreads();
-    for (int i = tid; i < kTile * HD; i += 256) {
-      const int c = i / HD, d = i % HD;
-      float kv = 0.f, vv = 0.f;
+    // 16-byte pieces: 8 elements of 16-bit caches, 4 of float caches
+    constexpr int E = sizeof(ST) == 2 ? 8 : 4;
+    constexpr int PIECES = kTile * HD / E;
+#pragma unroll 2
+    for (int i = tid; i < PIECES; i += 256) {
+      const int c = i / (HD / E), d = (i % (HD / E)) * E;
+      float kv[E], vv[E];
       if (c < nc) {
         const int64_t row = (int64_t)cells[c0 + c] * HD + d;
-        kv = KvStore<KvT>::load(kc, row);
-        vv = KvStore<KvT>::load(vc, row);
+        const uint4 ku = *(const uint4*)(kc + row);
+        const uint4 vu = *(const uint4*)(vc + row);
+        unpack16<KvT>(ku, kv);
+        unpack16<KvT>(vu, vv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) kv[e] = vv[e] = 0.f;
       }
-      k_s[c][d] = kv;
-      v_s[c][d] = vv;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        k_s[c][d + e] = kv[e];
+        v_s[c][d + e] = vv[e];
+      }
     }
     __syncthreads();
     // scores: wave w takes heads w, w+4, ...; lane = cell
@@ -427,17 +520,20 @@ __global__ void __launch_bounds__(HD) attn_merge_kernel(AttnArgs a) {
   const int nch = (a.n_vis[t] + a.chunk - 1) / a.chunk;
   const int64_t base = ((int64_t)t * a.H + h) * a.n_chunks;
   float M = -INFINITY;
+#pragma unroll 8
   for (int j = 0; j < nch; ++j) M = fmaxf(M, a.part_ml[(base + j) * 2]);
   float L = 0.f, o = 0.f;
+#pragma unroll 8
   for (int j = 0; j < nch; ++j) {
-    const float w = __expf(a.part_ml[(base + j) * 2] - M);
-    L = fmaf(a.part_ml[(base + j) * 2 + 1], w, L);
+    const float2 ml = *(const float2*)&a.part_ml[(base + j) * 2];
+    const float w = __expf(ml.x - M);
+    L = fmaf(ml.y, w, L);
     o = fmaf(a.part_acc[(base + j) * HD + d], w, o);
   }
   const float r = o / L;
   const int64_t oi = ((int64_t)t * a.H + h) * HD + d;
   if (a.out) a.out[oi] = r;
-  if (a.out_bf16) a.out_bf16[oi] = f32_to_bf16(r);
+  if (a.out_hi) split_bf16(r, a.out_hi[oi], a.out_lo[oi]);
 }
 
 template <typename KvT, int HD>
@@ -453,7 +549,19 @@ static hipError_t attn_launch_hd(const AttnArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  attn_merge_kernel<HD><<<dim3(a.H, a.T), HD, 0, s>>>(a);
+  return launch_attention_merge(a, s);
+}
+
+hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  const dim3 grid(a.H, a.T);
+  switch (a.hd) {
+    case 16: attn_merge_kernel<16><<<grid, 16, 0, s>>>(a); break;
+    case 32: attn_merge_kernel<32><<<grid, 32, 0, s>>>(a); break;
+    case 64: attn_merge_kernel<64><<<grid, 64, 0, s>>>(a); break;
+    case 128: attn_merge_kernel<128><<<grid, 128, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -1,39 +1,55 @@
 // Prefill linear layers on the gfx950 matrix cores.
 //
-// C[m][n] = sum_k act[m][k] W[n][k] with bf16 operands and float32
-// accumulation (v_mfma_f32_32x32x16_bf16).  Both operands are K-contiguous,
-// as stored (W row-major [out][in]).  Prefill is compute-bound (llama.cpp
-// walkthrough, "KV-cache and the Prefill / Decode stages"), so the epilogues
-// of the Llama layer (Ollama engine page, "Deep dive: the Llama forward pass
-// in Go") are fused here: RoPE + K/V cache write for the stacked Q/K/V
-// projection, SILU(gate) * up for the gate/up pair, and the residual add
-// for the output and down projections.
+// C[m][n] = sum_k act[m][k] W[n][k], float32 accumulation on
+// v_mfma_f32_32x32x16_bf16.  W is bf16 as stored (row-major [out][in], both
+// operands K-contiguous).  The activations carry about 16 significant bits as
+// a pair of bf16 arrays, act = hi + lo (hi = bf16(x), lo = bf16(x - hi)), so
+// every weight fragment feeds two MFMAs: act_hi.W + act_lo.W.  A single bf16
+// rounding of the activations before each projection would put the logits of
+// the 32-layer models far outside the float64 oracle's tolerance (the error
+// grows through the layers); the pair keeps the prefill within it.
 //
-// Tiling: 256 threads = 4 waves in a 2x2 grid; block tile 128 x 128 x 64,
-// each wave 64 x 64 = 2 x 2 MFMA tiles of 32 x 32.  Tiles go through LDS
-// (row pitch 72 bf16 to spread banks), double-buffered with the next tile
-// prefetched into registers during the MFMAs.  Blocks are ordered so that
-// the m tiles and K splits of one n tile run back to back on one XCD
-// (dispatch is round-robin over the 8 XCDs), which keeps each weight tile's
-// re-reads inside that XCD's L2.
+// Prefill is compute-bound (llama.cpp walkthrough, "KV-cache and the Prefill
+// / Decode stages"), so the epilogues of the Llama layer (Ollama engine page,
+// "Deep dive: the Llama forward pass in Go") are fused: RoPE + K/V cache
+// write for the stacked Q/K/V projection, SILU(gate) * up for the gate/up
+// pair (written again as a hi/lo pair), and the residual add for the output
+// and down projections (split over K with atomic adds when the tiles alone
+// would leave CUs idle).
+//
+// Tiling: 256 threads = 4 waves in a 2 x 2 grid; wave tile (32 MT) x (32 NT)
+// = MT x NT MFMA tiles of 32 x 32, block tile (64 MT) x (64 NT) x 64.  Tiles
+// go through LDS (row pitch 72 bf16 to spread banks) with the next K tile
+// prefetched into registers during the MFMAs.  Blocks are ordered so that the
+// m tiles and K splits of one n tile run back to back on one XCD (dispatch is
+// round-robin over the 8 XCDs), keeping a weight tile's re-reads in that
+// XCD's L2.
 #include "k_common.hpp"
 #include "kernels.hpp"
 #include "tdf.h"
 
 namespace tdf {
 
-constexpr int GBM = 128, GBN = 128, GBK = 64, GPITCH = GBK + 8;
+constexpr int GBK = 64, GPITCH = GBK + 8;
 
 template <typename KvT>
 __device__ __forceinline__ void kv_store(void* cache, int64_t idx, float v) {
   KvStore<KvT>::store((typename KvStore<KvT>::T*)cache, idx, v);
 }
 
-template <int EPI, typename KvT>
-__global__ void __launch_bounds__(256) gemm_kernel(LinearArgs a, int M, int tiles_m, int tiles_n,
+__device__ __forceinline__ void split_store(uint16_t* hi, uint16_t* lo, int64_t i, float v) {
+  split_bf16(v, hi[i], lo[i]);
+}
+
+template <int EPI, typename KvT, int MT, int NT>
+__global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int tiles_m, int tiles_n,
                                                    int ksplit) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][GBM * GPITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GBN * GPITCH];
+  constexpr int BM = 64 * MT, BN = 64 * NT;
+  constexpr int A_PER = BM * 8 / 256;   // 16-byte A pieces per thread (each of hi, lo)
+  constexpr int B_PER = BN * 8 / 256;   // 16-byte B pieces per thread
+  __shared__ __attribute__((aligned(16))) uint16_t Ah[BM * GPITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t Al[BM * GPITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * GPITCH];
 
   const int total = tiles_m * tiles_n * ksplit;
   int b = blockIdx.x;
@@ -48,25 +64,31 @@ __global__ void __launch_bounds__(256) gemm_kernel(LinearArgs a, int M, int tile
   const int kchunk = K / ksplit;
   const int k_begin = ks * kchunk;
   const int nk = kchunk / GBK;
-  const int m0 = tm * GBM;
+  const int m0 = tm * BM;
   const int Ntot = a.n0 + a.n1 + a.n2;
-  // column base of this block (SwiGLU: 64 output columns, gate and up rows)
-  const int n0 = EPI == EPI_SWIGLU ? tn * 64 : tn * GBN;
+  // SwiGLU: a block covers BN/2 output columns; wave wn holds gate tiles
+  // [0, NT/2) and up tiles [NT/2, NT) for the same BN/4 columns
+  const int n0 = EPI == EPI_SWIGLU ? tn * (BN / 2) : tn * BN;
 
-  // rows this thread stages: chunk c = tid + 256 i -> row c / 8, k offset (c % 8) * 8
   const int kc = (tid & 7) * 8;
-  const uint16_t* arow[4];
-  const uint16_t* brow[4];
+  int64_t aoff[A_PER];
+  bool aok[A_PER];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < A_PER; ++i) {
+    const int gm = m0 + (tid >> 3) + 32 * i;
+    aok[i] = gm < M;
+    aoff[i] = (int64_t)(aok[i] ? gm : 0) * K;
+  }
+  const uint16_t* brow[B_PER];
+#pragma unroll
+  for (int i = 0; i < B_PER; ++i) {
     const int r = (tid >> 3) + 32 * i;
-    const int gm = m0 + r;
-    arow[i] = gm < M ? a.act_bf16 + (int64_t)gm * K : nullptr;
     const uint16_t* p = nullptr;
     if (EPI == EPI_SWIGLU) {
-      const int q = r >> 5;
-      const int f = n0 + (q >> 1) * 32 + (r & 31);
-      if (f < a.n0) p = (const uint16_t*)((q & 1) ? a.w1 : a.w0) + (int64_t)f * K;
+      constexpr int WN = BN / 2, HALF = WN / 2;
+      const int part = r / WN, rr = r % WN;
+      const int f = n0 + part * HALF + (rr % HALF);
+      if (f < a.n0) p = (const uint16_t*)(rr >= HALF ? a.w1 : a.w0) + (int64_t)f * K;
     } else {
       const int gr = n0 + r;
       if (gr < a.n0) p = (const uint16_t*)a.w0 + (int64_t)gr * K;
@@ -76,80 +98,97 @@ __global__ void __launch_bounds__(256) gemm_kernel(LinearArgs a, int M, int tile
     brow[i] = p;
   }
 
-  uint4 ra[4], rb[4];
+  uint4 rah[A_PER], ral[A_PER], rb[B_PER];
   const uint4 zero = make_uint4(0, 0, 0, 0);
   auto gload = [&](int k) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = arow[i] ? *(const uint4*)(arow[i] + k + kc) : zero;
-      rb[i] = brow[i] ? *(const uint4*)(brow[i] + k + kc) : zero;
+    for (int i = 0; i < A_PER; ++i) {
+      rah[i] = aok[i] ? *(const uint4*)(a.act_hi + aoff[i] + k + kc) : zero;
+      ral[i] = aok[i] ? *(const uint4*)(a.act_lo + aoff[i] + k + kc) : zero;
     }
-  };
-  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < B_PER; ++i) rb[i] = brow[i] ? *(const uint4*)(brow[i] + k + kc) : zero;
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
       const int r = (tid >> 3) + 32 * i;
-      *(uint4*)&As[buf][r * GPITCH + kc] = ra[i];
-      *(uint4*)&Bs[buf][r * GPITCH + kc] = rb[i];
+      *(uint4*)&Ah[r * GPITCH + kc] = rah[i];
+      *(uint4*)&Al[r * GPITCH + kc] = ral[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i) {
+      const int r = (tid >> 3) + 32 * i;
+      *(uint4*)&Bs[r * GPITCH + kc] = rb[i];
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[MT][NT];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   gload(k_begin);
-  lstore(0);
+  lstore();
   __syncthreads();
 
   const int frow = lane & 31;
   const int fk = (lane >> 5) * 8;
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
     if (kt + 1 < nk) gload(k_begin + (kt + 1) * GBK);
 #pragma unroll
     for (int kk = 0; kk < GBK; kk += 16) {
-      bf16x8 af[2], bfr[2];
+      bf16x8 ah[MT], al[MT], bfr[NT];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        af[mt] = *(const bf16x8*)&As[cur][(wm * 64 + mt * 32 + frow) * GPITCH + kk + fk];
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = (wm * 32 * MT + mt * 32 + frow) * GPITCH + kk + fk;
+        ah[mt] = *(const bf16x8*)&Ah[r];
+        al[mt] = *(const bf16x8*)&Al[r];
+      }
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        bfr[nt] = *(const bf16x8*)&Bs[cur][(wn * 64 + nt * 32 + frow) * GPITCH + kk + fk];
+      for (int nt = 0; nt < NT; ++nt)
+        bfr[nt] = *(const bf16x8*)&Bs[(wn * 32 * NT + nt * 32 + frow) * GPITCH + kk + fk];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
+        }
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+    if (kt + 1 < nk) {
+      __syncthreads();
+      lstore();
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: lane holds column (lane % 32) and rows i*8 + (lane/32)*4 + j
   const int ccol = lane & 31;
   const int rsub = (lane >> 5) * 4;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * 64 + mt * 32 + (r >> 2) * 8 + rsub + (r & 3);
+      const int row = m0 + wm * 32 * MT + mt * 32 + (r >> 2) * 8 + rsub + (r & 3);
       const bool row_ok = row < M;
       if (EPI == EPI_SWIGLU) {
-        const int f = n0 + wn * 32 + ccol;
-        if (row_ok && f < a.n0) {
-          const float v = silu(acc[mt][0][r]) * acc[mt][1][r];
-          a.out_bf16[(int64_t)row * a.ldo + f] = f32_to_bf16(v);
+#pragma unroll
+        for (int nt = 0; nt < NT / 2; ++nt) {
+          const int f = n0 + wn * (BN / 4) + nt * 32 + ccol;
+          if (row_ok && f < a.n0) {
+            const float v = silu(acc[mt][nt][r]) * acc[mt][nt + NT / 2][r];
+            split_store(a.out_hi, a.out_lo, (int64_t)row * a.ldo + f, v);
+          }
         }
         continue;
       }
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int col = n0 + wn * 64 + nt * 32 + ccol;
+      for (int nt = 0; nt < NT; ++nt) {
+        const int col = n0 + wn * 32 * NT + nt * 32 + ccol;
         const float y = acc[mt][nt][r];
         if (EPI == EPI_QKV) {
           const float partner = __shfl_xor(y, 1, kWave);
@@ -163,8 +202,7 @@ __global__ void __launch_bounds__(256) gemm_kernel(LinearArgs a, int M, int tile
             const float c = (float)cs, s = (float)sn;
             const float z = (col & 1) ? partner * s + y * c : y * c - partner * s;
             if (col < a.n0) {
-              if (a.q_out) a.q_out[(int64_t)row * a.n0 + lc] = z;
-              if (a.q_out_bf16) a.q_out_bf16[(int64_t)row * a.n0 + lc] = f32_to_bf16(z);
+              a.q_out[(int64_t)row * a.n0 + lc] = z;
             } else {
               kv_store<KvT>(a.k_cache, ((int64_t)(lc / hd) * a.n_ctx + a.slots[row]) * hd + (lc % hd), z);
             }
@@ -184,26 +222,39 @@ __global__ void __launch_bounds__(256) gemm_kernel(LinearArgs a, int M, int tile
 }
 
 bool gemm_supported(const LinearArgs& a) {
-  return a.weight_bf16 && a.act_bf16 && a.K % GBK == 0 && a.K >= GBK;
+  return a.weight_bf16 && a.act_hi && a.act_lo && a.K % GBK == 0 && a.K >= GBK;
 }
 
+template <int EPI, typename KvT, int MT, int NT>
+static hipError_t gemm_launch_tile(const LinearArgs& a, int ksplit, hipStream_t s) {
+  const int M = a.T;
+  const int tiles_m = (M + 64 * MT - 1) / (64 * MT);
+  const int Ntot = a.n0 + a.n1 + a.n2;
+  const int tiles_n = EPI == EPI_SWIGLU ? (a.n0 + 32 * NT - 1) / (32 * NT) : (Ntot + 64 * NT - 1) / (64 * NT);
+  gemm_kernel<EPI, KvT, MT, NT><<<tiles_m * tiles_n * ksplit, 256, 0, s>>>(a, M, tiles_m, tiles_n, ksplit);
+  return hipGetLastError();
+}
+
+// Tile choice: the largest of 128x256, 128x128, 64x128 that gives at least
+// 384 blocks (1.5 per CU), counting K splits for the residual epilogue.
 template <int EPI, typename KvT>
 static hipError_t gemm_launch_t(const LinearArgs& a, hipStream_t s) {
   const int M = a.T;
-  const int tiles_m = (M + GBM - 1) / GBM;
-  const int Ntot = a.n0 + a.n1 + a.n2;
-  const int tiles_n = EPI == EPI_SWIGLU ? (a.n0 + 63) / 64 : (Ntot + GBN - 1) / GBN;
-  int ksplit = 1;
-  if (EPI == EPI_RESIDUAL) {
-    // fill the 256 CUs: split K (partial sums are added atomically)
-    const int nkt = a.K / GBK;
-    while (tiles_m * tiles_n * ksplit < 512 && ksplit < 8 && nkt % (ksplit * 2) == 0 &&
-           nkt / (ksplit * 2) >= 4)
-      ksplit *= 2;
-  }
-  const int blocks = tiles_m * tiles_n * ksplit;
-  gemm_kernel<EPI, KvT><<<blocks, 256, 0, s>>>(a, M, tiles_m, tiles_n, ksplit);
-  return hipGetLastError();
+  const int Ntot = EPI == EPI_SWIGLU ? 2 * a.n0 : a.n0 + a.n1 + a.n2;
+  const int nkt = a.K / GBK;
+  auto splits = [&](int blocks) {
+    int ksplit = 1;
+    if (EPI == EPI_RESIDUAL)
+      while (blocks * ksplit < 512 && ksplit < 8 && nkt % (ksplit * 2) == 0 && nkt / (ksplit * 2) >= 4)
+        ksplit *= 2;
+    return ksplit;
+  };
+  const int b24 = ((M + 127) / 128) * ((Ntot + 255) / 256);
+  const int b22 = ((M + 127) / 128) * ((Ntot + 127) / 128);
+  if (b24 * splits(b24) >= 384) return gemm_launch_tile<EPI, KvT, 2, 4>(a, splits(b24), s);
+  if (b22 * splits(b22) >= 384) return gemm_launch_tile<EPI, KvT, 2, 2>(a, splits(b22), s);
+  const int b12 = ((M + 63) / 64) * ((Ntot + 127) / 128);
+  return gemm_launch_tile<EPI, KvT, 1, 2>(a, splits(b12), s);
 }
 
 hipError_t launch_linear_gemm(const LinearArgs& a, hipStream_t s) {

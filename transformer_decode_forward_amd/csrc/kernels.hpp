@@ -24,17 +24,22 @@ struct LinearArgs {
   int K = 0;                   // inner size (row length)
   int T = 0;                   // tokens (rows of act)
   int weight_bf16 = 1;         // 1: bf16 weights, 0: float32
-  // activations: float32 [T][K] (GEMV) or bf16 [T][K] (GEMM)
+  // activations: float32 [T][K] (GEMV), or a bf16 pair hi + lo [T][K] (GEMM)
   const float* act_f32 = nullptr;
-  const uint16_t* act_bf16 = nullptr;
+  // GEMV only: when set, act_f32 is the raw residual x and the kernel applies
+  // RMSNorm on the fly: y = (sum_k W[n][k] g[k] x[k]) / sqrt(mean(x^2) + eps)
+  const float* norm_g = nullptr;
+  float norm_eps = 0.f;
+  const uint16_t* act_hi = nullptr;
+  const uint16_t* act_lo = nullptr;
   // epilogue
   int epi = EPI_STORE;
   float* out = nullptr;        // [T][ldo] float32 (STORE / RESIDUAL / SWIGLU)
-  uint16_t* out_bf16 = nullptr;// [T][ldo] bf16 (GEMM SWIGLU)
+  uint16_t* out_hi = nullptr;  // [T][ldo] bf16 pair (GEMM SWIGLU)
+  uint16_t* out_lo = nullptr;
   int ldo = 0;
   // EPI_QKV
-  float* q_out = nullptr;      // [T][n0] float32 (GEMV)
-  uint16_t* q_out_bf16 = nullptr;  // [T][n0] bf16 (GEMM)
+  float* q_out = nullptr;      // [T][n0] float32
   void* k_cache = nullptr;     // layer base [n_head_kv][n_ctx][head_dim]
   void* v_cache = nullptr;
   int kv_dtype = 0;            // tdf_dtype
@@ -52,9 +57,10 @@ bool gemm_supported(const LinearArgs& a);
 // x[t][:] = E[token[t]][:] (to float32)
 hipError_t launch_embed(const void* table, int weight_bf16, const int32_t* tokens, int T, int d,
                         float* x, hipStream_t s);
-// out = x / sqrt(mean(x^2) + eps) * g, float32 and/or bf16 outputs
+// out = x / sqrt(mean(x^2) + eps) * g, as float32 and/or a bf16 pair
+// (hi = bf16(out), lo = bf16(out - hi))
 hipError_t launch_rmsnorm(const float* x, const float* g, int T, int d, float eps, float* out_f32,
-                          uint16_t* out_bf16, hipStream_t s);
+                          uint16_t* out_hi, uint16_t* out_lo, hipStream_t s);
 // dst[pairs[2i]] = pairs[2i+1]
 hipError_t launch_scatter(int32_t* dst, const int64_t* pairs, int n, hipStream_t s);
 // dst[r][:] = src[rows[r]][:]
@@ -80,8 +86,37 @@ struct AttnArgs {
   float* part_acc = nullptr;  // [T][H][n_chunks][hd]
   float* part_ml = nullptr;   // [T][H][n_chunks][2]
   float* out = nullptr;       // [T][H][hd] float32
-  uint16_t* out_bf16 = nullptr;  // optional bf16 copy
+  uint16_t* out_hi = nullptr; // optional bf16 pair
+  uint16_t* out_lo = nullptr;
 };
 hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t s);
+// merge of split partials only (part_* -> out / out_bf16)
+hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s);
+
+// Prefill attention on the matrix cores.  Query tiles of up to 32 tokens of
+// one sequence: tile_tokens [n_tiles][32] (ubatch token index, -1 padding),
+// tile_list_off[i] = seq * n_ctx, tile_nvis_max[i] = largest n_vis in the
+// tile.  q is float32 [T][H][hd]; bf16 or f16 caches, head_dim 64 or 128.
+struct PrefillAttnArgs {
+  const float* q = nullptr;
+  const void* k_cache = nullptr;
+  const void* v_cache = nullptr;
+  int kv_dtype = 0;
+  const int32_t* cell_list = nullptr;
+  const int32_t* n_vis = nullptr;
+  const int32_t* tile_tokens = nullptr;
+  const int32_t* tile_list_off = nullptr;
+  const int32_t* tile_nvis_max = nullptr;
+  int n_tiles = 0, H = 0, Hkv = 0, hd = 0, n_ctx = 0;
+  int chunk = 0, n_splits = 1;
+  float* part_acc = nullptr;
+  float* part_ml = nullptr;
+  float* out = nullptr;
+  uint16_t* out_hi = nullptr;
+  uint16_t* out_lo = nullptr;
+  AttnArgs merge;  // used when n_splits > 1 (T, H, hd, chunk, n_chunks = n_splits, n_vis, parts, outs)
+};
+bool prefill_attention_supported(int kv_dtype, int head_dim);
+hipError_t launch_attention_prefill(const PrefillAttnArgs& a, hipStream_t s);
 
 }  // namespace tdf

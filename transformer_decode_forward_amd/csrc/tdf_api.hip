@@ -54,10 +54,20 @@ constexpr int kDecodeMaxT = 32;     // ubatches up to this size use the decode k
 constexpr int kChunkCapDecode = 256; // attention splits per token (decode)
 constexpr int kChunkCapPrefill = 32; // attention splits per token (larger ubatches)
 
-// int32 entries of the per-call staging area: 5 per token + selected rows,
-// each ubatch region rounded up to 4 entries
-size_t staging_i32(int n_batch) { return (size_t)10 * n_batch + 16; }
-size_t staging_i64_base(int n_batch) { return (staging_i32(n_batch) * 4 + 15) & ~(size_t)15; }
+constexpr int kQTile = 32;           // tokens per prefill attention query tile
+
+// int32 entries of the per-call staging area.  A ubatch of U tokens stores 5
+// per token, its selected rows (<= U) and its query tiles (at most
+// U/32 + 1 + min(U, n_seq_max) tiles of 34 entries), rounded up to 4.
+size_t staging_i32(int n_batch, int n_ubatch, int n_seq_max) {
+  const size_t U = (size_t)n_ubatch;
+  const size_t n_ub = ((size_t)n_batch + U - 1) / U;
+  const size_t tiles = U / kQTile + 1 + std::min<size_t>(U, (size_t)n_seq_max);
+  return n_ub * (6 * U + (kQTile + 2) * tiles + 4) + 16;
+}
+size_t staging_i64_base(int n_batch, int n_ubatch, int n_seq_max) {
+  return (staging_i32(n_batch, n_ubatch, n_seq_max) * 4 + 15) & ~(size_t)15;
+}
 
 }  // namespace
 
@@ -83,7 +93,8 @@ struct tdf_context {
   int32_t* cell_list = nullptr;     // [n_seq_max][n_ctx]
   double* inv_freq = nullptr;       // [hd/2]
   float *x = nullptr, *xs = nullptr, *act = nullptr, *q = nullptr, *o = nullptr, *mb = nullptr;
-  uint16_t *h16 = nullptr, *o16 = nullptr, *m16 = nullptr;
+  // bf16 hi/lo pairs of the matrix-core inputs: normed rows, attention output, MLP product
+  uint16_t *h_hi = nullptr, *h_lo = nullptr, *o_hi = nullptr, *o_lo = nullptr, *m_hi = nullptr, *m_lo = nullptr;
   float *part_acc = nullptr, *part_ml = nullptr;
   size_t part_rows = 0;             // capacity in (token, head, chunk) triples
   void* ints = nullptr;             // per-call packed integers
@@ -311,15 +322,19 @@ extern "C" tdf_context* tdf_context_create(const tdf_model* m, const tdf_context
   A((void**)&c->q, (size_t)U * H * hd * 4);
   A((void**)&c->o, (size_t)U * H * hd * 4);
   A((void**)&c->mb, (size_t)U * F * 4);
-  A((void**)&c->h16, (size_t)U * d * 2);
-  A((void**)&c->o16, (size_t)U * H * hd * 2);
-  A((void**)&c->m16, (size_t)U * F * 2);
+  A((void**)&c->h_hi, (size_t)U * d * 2);
+  A((void**)&c->h_lo, (size_t)U * d * 2);
+  A((void**)&c->o_hi, (size_t)U * H * hd * 2);
+  A((void**)&c->o_lo, (size_t)U * H * hd * 2);
+  A((void**)&c->m_hi, (size_t)U * F * 2);
+  A((void**)&c->m_lo, (size_t)U * F * 2);
   c->part_rows = std::max((size_t)std::min(U, kDecodeMaxT) * H * kChunkCapDecode,
                           (size_t)U * H * kChunkCapPrefill);
   A((void**)&c->part_acc, c->part_rows * hd * 4);
   A((void**)&c->part_ml, c->part_rows * 2 * 4);
   // per-call integers: 5 int32 per token + selected rows, then int64 list writes
-  c->ints_bytes = staging_i64_base(c->n_batch) + (size_t)2 * c->n_batch * c->n_seq_max * 8;
+  c->ints_bytes = staging_i64_base(c->n_batch, c->n_ubatch, c->n_seq_max) +
+                  (size_t)2 * c->n_batch * c->n_seq_max * 8;
   A(&c->ints, c->ints_bytes);
   if (rc == TDF_OK && hipHostMalloc((void**)&c->ints_host, c->ints_bytes, hipHostMallocDefault) != hipSuccess) {
     set_err("pinned staging allocation failed");
@@ -357,6 +372,8 @@ struct UbatchDev {
   const int32_t *tokens, *pos, *slots, *list_off, *n_vis, *sel;
   const int64_t* list_writes;
   int n_list_writes = 0;
+  const int32_t *tile_tokens = nullptr, *tile_off = nullptr, *tile_nvis = nullptr;
+  int n_tiles = 0;
   int nvis_max = 0;
   int out_row0 = 0;  // first logits row of this ubatch
 };
@@ -393,15 +410,17 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     const tdf_layer_weights& W = m->layers[l];
     // attention block
     const bool big = use_mfma(T, d);
-    ps = prof_begin(c, TDF_OP_NORM, big);
-    TDF_HIP(launch_rmsnorm(cur, (const float*)W.attn_norm, T, d, h.rms_eps, big ? nullptr : c->act,
-                           big ? c->h16 : nullptr, s));
-    prof_end(c, ps);
+    if (big) {  // the decode GEMV applies RMSNorm itself
+      ps = prof_begin(c, TDF_OP_NORM, big);
+      TDF_HIP(launch_rmsnorm(cur, (const float*)W.attn_norm, T, d, h.rms_eps, nullptr, c->h_hi, c->h_lo, s));
+      prof_end(c, ps);
+    }
     LinearArgs qa;
     qa.w0 = W.wq; qa.w1 = W.wk; qa.w2 = W.wv;
     qa.n0 = H * hd; qa.n1 = Hkv * hd; qa.n2 = Hkv * hd;
     qa.K = d; qa.T = T; qa.weight_bf16 = wbf16;
-    qa.act_f32 = c->act; qa.act_bf16 = c->h16;
+    qa.act_f32 = cur; qa.act_hi = c->h_hi; qa.act_lo = c->h_lo;
+    qa.norm_g = (const float*)W.attn_norm; qa.norm_eps = h.rms_eps;
     qa.epi = EPI_QKV;
     qa.q_out = c->q;
     qa.k_cache = kv_k(c, l); qa.v_cache = kv_v(c, l);
@@ -409,6 +428,33 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     qa.slots = u.slots; qa.pos = u.pos; qa.inv_freq = c->inv_freq;
     if (int rc = run_linear(c, qa, big, TDF_OP_QKV)) return rc;
 
+    if (big && prefill_attention_supported(c->kv_dtype, hd)) {
+      PrefillAttnArgs pa;
+      pa.q = c->q;
+      pa.k_cache = kv_k(c, l); pa.v_cache = kv_v(c, l);
+      pa.kv_dtype = c->kv_dtype;
+      pa.cell_list = c->cell_list; pa.n_vis = u.n_vis;
+      pa.tile_tokens = u.tile_tokens; pa.tile_list_off = u.tile_off; pa.tile_nvis_max = u.tile_nvis;
+      pa.n_tiles = u.n_tiles; pa.H = H; pa.Hkv = Hkv; pa.hd = hd; pa.n_ctx = c->n_ctx;
+      // split the cell range only when the tiles alone leave CUs idle; at
+      // least 256 cells per split, at most kChunkCapPrefill splits
+      const int blocks = u.n_tiles * Hkv;
+      int want = std::max(1, (512 + blocks - 1) / blocks);
+      int chunk = std::max(256, (u.nvis_max + want - 1) / want);
+      chunk = std::max(chunk, (u.nvis_max + kChunkCapPrefill - 1) / kChunkCapPrefill);
+      chunk = (chunk + 63) / 64 * 64;
+      pa.chunk = chunk;
+      pa.n_splits = (u.nvis_max + chunk - 1) / chunk;
+      pa.part_acc = c->part_acc; pa.part_ml = c->part_ml;
+      pa.out = c->o; pa.out_hi = c->o_hi; pa.out_lo = c->o_lo;
+      pa.merge.T = T; pa.merge.H = H; pa.merge.Hkv = Hkv; pa.merge.hd = hd;
+      pa.merge.n_vis = u.n_vis; pa.merge.chunk = chunk; pa.merge.n_chunks = pa.n_splits;
+      pa.merge.part_acc = c->part_acc; pa.merge.part_ml = c->part_ml;
+      pa.merge.out = c->o; pa.merge.out_hi = c->o_hi; pa.merge.out_lo = c->o_lo;
+      ps = prof_begin(c, TDF_OP_ATTN, big);
+      TDF_HIP(launch_attention_prefill(pa, s));
+      prof_end(c, ps);
+    } else {
     AttnArgs at;
     at.q = c->q;
     at.k_cache = kv_k(c, l); at.v_cache = kv_v(c, l);
@@ -422,14 +468,16 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     at.n_chunks = (u.nvis_max + chunk - 1) / chunk;
     at.part_acc = c->part_acc; at.part_ml = c->part_ml;
     at.out = c->o;
-    at.out_bf16 = big ? c->o16 : nullptr;
+    at.out_hi = big ? c->o_hi : nullptr;
+    at.out_lo = big ? c->o_lo : nullptr;
     ps = prof_begin(c, TDF_OP_ATTN, big);
     TDF_HIP(launch_attention_decode(at, s));
     prof_end(c, ps);
+    }
 
     LinearArgs oa;
     oa.w0 = W.wo; oa.n0 = d; oa.K = H * hd; oa.T = T; oa.weight_bf16 = wbf16;
-    oa.act_f32 = c->o; oa.act_bf16 = c->o16;
+    oa.act_f32 = c->o; oa.act_hi = c->o_hi; oa.act_lo = c->o_lo;
     oa.epi = EPI_RESIDUAL; oa.out = cur; oa.ldo = d;
     if (int rc = run_linear(c, oa, big && use_mfma(T, H * hd), TDF_OP_WO)) return rc;
 
@@ -444,18 +492,20 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     }
     // MLP block
     const bool bigm = use_mfma(T, d) && use_mfma(T, F);
-    ps = prof_begin(c, TDF_OP_NORM, bigm);
-    TDF_HIP(launch_rmsnorm(cur, (const float*)W.ffn_norm, T, d, h.rms_eps, bigm ? nullptr : c->act,
-                           bigm ? c->h16 : nullptr, s));
-    prof_end(c, ps);
+    if (bigm) {
+      ps = prof_begin(c, TDF_OP_NORM, bigm);
+      TDF_HIP(launch_rmsnorm(cur, (const float*)W.ffn_norm, T, d, h.rms_eps, nullptr, c->h_hi, c->h_lo, s));
+      prof_end(c, ps);
+    }
     LinearArgs ga;
     ga.w0 = W.w_gate; ga.w1 = W.w_up; ga.n0 = F; ga.K = d; ga.T = T; ga.weight_bf16 = wbf16;
-    ga.act_f32 = c->act; ga.act_bf16 = c->h16;
-    ga.epi = EPI_SWIGLU; ga.out = c->mb; ga.out_bf16 = c->m16; ga.ldo = F;
+    ga.act_f32 = cur; ga.act_hi = c->h_hi; ga.act_lo = c->h_lo;
+    ga.norm_g = (const float*)W.ffn_norm; ga.norm_eps = h.rms_eps;
+    ga.epi = EPI_SWIGLU; ga.out = c->mb; ga.out_hi = c->m_hi; ga.out_lo = c->m_lo; ga.ldo = F;
     if (int rc = run_linear(c, ga, bigm, TDF_OP_GATE_UP)) return rc;
     LinearArgs da;
     da.w0 = W.w_down; da.n0 = d; da.K = F; da.T = T; da.weight_bf16 = wbf16;
-    da.act_f32 = c->mb; da.act_bf16 = c->m16;
+    da.act_f32 = c->mb; da.act_hi = c->m_hi; da.act_lo = c->m_lo;
     da.epi = EPI_RESIDUAL; da.out = cur; da.ldo = d;
     if (int rc = run_linear(c, da, bigm, TDF_OP_DOWN)) return rc;
   }
@@ -467,13 +517,15 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
   }
   // output norm + LM head into this ubatch's logits rows
   const bool bigo = use_mfma(T, d);
-  ps = prof_begin(c, TDF_OP_NORM, bigo);
-  TDF_HIP(launch_rmsnorm(cur, m->output_norm, T, d, h.rms_eps, bigo ? nullptr : c->act,
-                         bigo ? c->h16 : nullptr, s));
-  prof_end(c, ps);
+  if (bigo) {
+    ps = prof_begin(c, TDF_OP_NORM, bigo);
+    TDF_HIP(launch_rmsnorm(cur, m->output_norm, T, d, h.rms_eps, nullptr, c->h_hi, c->h_lo, s));
+    prof_end(c, ps);
+  }
   LinearArgs la;
   la.w0 = m->output; la.n0 = V; la.K = d; la.T = T; la.weight_bf16 = wbf16;
-  la.act_f32 = c->act; la.act_bf16 = c->h16;
+  la.act_f32 = cur; la.act_hi = c->h_hi; la.act_lo = c->h_lo;
+  la.norm_g = m->output_norm; la.norm_eps = h.rms_eps;
   la.epi = EPI_STORE; la.out = c->logits + (size_t)u.out_row0 * V; la.ldo = V;
   return run_linear(c, la, bigo, TDF_OP_LM_HEAD);
 }
@@ -514,7 +566,7 @@ extern "C" int32_t tdf_decode(tdf_context* c, const tdf_batch* b) {
   // integers of every ubatch of this call go into one pinned staging area;
   // region of a ubatch: tokens, pos, slots, list_off, n_vis, sel | list writes
   size_t i32_off = 0, i64_off = 0;
-  const size_t i64_base = staging_i64_base(c->n_batch);
+  const size_t i64_base = staging_i64_base(c->n_batch, c->n_ubatch, c->n_seq_max);
   std::vector<int32_t> slots;
   std::vector<int64_t> writes;
   int out_row = 0;
@@ -546,7 +598,36 @@ extern "C" int32_t tdf_decode(tdf_context* c, const tdf_batch* b) {
     memcpy(h32 + 3 * T, list_off.data(), T * 4);
     memcpy(h32 + 4 * T, n_vis.data(), T * 4);
     if (!sel.empty()) memcpy(h32 + 5 * T, sel.data(), sel.size() * 4);
-    const size_t n32 = 5 * (size_t)T + sel.size();
+    // query tiles for the matrix-core attention: tokens of one sequence in
+    // batch order, 32 at a time
+    std::vector<int32_t> tile_tok, tile_off, tile_nvis;
+    if (T > kDecodeMaxT) {
+      std::vector<int> order(T);
+      for (int i = 0; i < T; ++i) order[i] = i;
+      std::stable_sort(order.begin(), order.end(),
+                       [&](int x, int y) { return in.seq0[u0 + x] < in.seq0[u0 + y]; });
+      for (int k = 0; k < T;) {
+        const int s0 = in.seq0[u0 + order[k]];
+        int nmax = 0, cnt = 0;
+        const size_t base = tile_tok.size();
+        tile_tok.resize(base + kQTile, -1);
+        while (k < T && cnt < kQTile && in.seq0[u0 + order[k]] == s0) {
+          tile_tok[base + cnt++] = order[k];
+          nmax = std::max(nmax, n_vis[order[k]]);
+          ++k;
+        }
+        tile_off.push_back(s0 * c->n_ctx);
+        tile_nvis.push_back(nmax);
+      }
+    }
+    const int n_tiles = (int)tile_off.size();
+    if (n_tiles) {
+      int32_t* tp = h32 + 5 * T + sel.size();
+      memcpy(tp, tile_tok.data(), tile_tok.size() * 4);
+      memcpy(tp + tile_tok.size(), tile_off.data(), n_tiles * 4);
+      memcpy(tp + tile_tok.size() + n_tiles, tile_nvis.data(), n_tiles * 4);
+    }
+    const size_t n32 = 5 * (size_t)T + sel.size() + (size_t)(kQTile + 2) * n_tiles;
     int64_t* h64 = (int64_t*)(c->ints_host + i64_base + i64_off * 8);
     int64_t* d64 = (int64_t*)((char*)c->ints + i64_base + i64_off * 8);
     if (!writes.empty()) memcpy(h64, writes.data(), writes.size() * 8);
@@ -562,6 +643,10 @@ extern "C" int32_t tdf_decode(tdf_context* c, const tdf_batch* b) {
     ud.list_writes = d64;
     ud.n_list_writes = (int)writes.size() / 2;
     ud.nvis_max = nvis_max;
+    ud.n_tiles = n_tiles;
+    ud.tile_tokens = d32 + 5 * T + sel.size();
+    ud.tile_off = ud.tile_tokens + (size_t)kQTile * n_tiles;
+    ud.tile_nvis = ud.tile_off + n_tiles;
     ud.out_row0 = out_row;
     rc = forward_ubatch(c, ud);
     if (rc != TDF_OK) return rc;
