@@ -19,39 +19,68 @@ namespace tdf {
 // ---------------------------------------------------------------------------
 // small kernels
 
+// block sum of 256 threads (4 waves); every thread gets the total
+__device__ __forceinline__ float block_sum256(float v, float* red4) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return red4[0] + red4[1] + red4[2] + red4[3];
+}
+
 template <bool BF16>
 __global__ void __launch_bounds__(256) embed_kernel(const void* __restrict__ table,
                                                     const int32_t* __restrict__ tokens, int d,
-                                                    float* __restrict__ x) {
+                                                    float* __restrict__ x, const float* __restrict__ g,
+                                                    float* __restrict__ u, float* __restrict__ ssp,
+                                                    int stride) {
+  __shared__ float red[4];
   const int t = blockIdx.x;
   const int64_t row = (int64_t)tokens[t] * d;
   float* xr = x + (int64_t)t * d;
+  float* ur = u ? u + (int64_t)t * d : nullptr;
+  float ss = 0.f;
   if ((d & 3) == 0) {
 #pragma unroll 4
     for (int k = threadIdx.x * 4; k < d; k += 1024) {
       float4 v;
       if (BF16) {
-        const uint2 u = *(const uint2*)((const uint16_t*)table + row + k);
-        v = make_float4(__builtin_bit_cast(float, u.x << 16), __builtin_bit_cast(float, u.x & 0xFFFF0000u),
-                        __builtin_bit_cast(float, u.y << 16), __builtin_bit_cast(float, u.y & 0xFFFF0000u));
+        const uint2 q = *(const uint2*)((const uint16_t*)table + row + k);
+        v = make_float4(__builtin_bit_cast(float, q.x << 16), __builtin_bit_cast(float, q.x & 0xFFFF0000u),
+                        __builtin_bit_cast(float, q.y << 16), __builtin_bit_cast(float, q.y & 0xFFFF0000u));
       } else {
         v = *(const float4*)((const float*)table + row + k);
       }
       *(float4*)(xr + k) = v;
+      if (g) {
+        const float4 gv = *(const float4*)(g + k);
+        *(float4*)(ur + k) = make_float4(gv.x * v.x, gv.y * v.y, gv.z * v.z, gv.w * v.w);
+        ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      }
     }
   } else {
-    for (int k = threadIdx.x; k < d; k += 256)
-      xr[k] = BF16 ? bf16_to_f32(((const uint16_t*)table)[row + k]) : ((const float*)table)[row + k];
+    for (int k = threadIdx.x; k < d; k += 256) {
+      const float v = BF16 ? bf16_to_f32(((const uint16_t*)table)[row + k]) : ((const float*)table)[row + k];
+      xr[k] = v;
+      if (g) {
+        ur[k] = g[k] * v;
+        ss += v * v;
+      }
+    }
+  }
+  if (g) {
+    ss = block_sum256(ss, red);
+    if (threadIdx.x == 0) ssp[(int64_t)t * stride] = ss;
   }
 }
 
 hipError_t launch_embed(const void* table, int weight_bf16, const int32_t* tokens, int T, int d,
-                        float* x, hipStream_t s) {
+                        float* x, const float* g, float* u, float* ssp, int stride, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (weight_bf16)
-    embed_kernel<true><<<T, 256, 0, s>>>(table, tokens, d, x);
+    embed_kernel<true><<<T, 256, 0, s>>>(table, tokens, d, x, g, u, ssp, stride);
   else
-    embed_kernel<false><<<T, 256, 0, s>>>(table, tokens, d, x);
+    embed_kernel<false><<<T, 256, 0, s>>>(table, tokens, d, x, g, u, ssp, stride);
   return hipGetLastError();
 }
 
@@ -106,16 +135,31 @@ hipError_t launch_scatter(int32_t* dst, const int64_t* pairs, int n, hipStream_t
 
 __global__ void __launch_bounds__(256) gather_rows_kernel(const float* __restrict__ src,
                                                           const int32_t* __restrict__ rows, int d,
-                                                          float* __restrict__ dst) {
+                                                          float* __restrict__ dst, const float* __restrict__ g,
+                                                          float* __restrict__ u, float* __restrict__ ssp,
+                                                          int stride) {
+  __shared__ float red[4];
   const int r = blockIdx.x;
-  const float* s = src + (int64_t)rows[r] * d;
-  for (int k = threadIdx.x; k < d; k += 256) dst[(int64_t)r * d + k] = s[k];
+  const float* sr = src + (int64_t)(rows ? rows[r] : r) * d;
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < d; k += 256) {
+    const float v = sr[k];
+    if (dst) dst[(int64_t)r * d + k] = v;
+    if (g) {
+      u[(int64_t)r * d + k] = g[k] * v;
+      ss += v * v;
+    }
+  }
+  if (g) {
+    ss = block_sum256(ss, red);
+    if (threadIdx.x == 0) ssp[(int64_t)r * stride] = ss;
+  }
 }
 
 hipError_t launch_gather_rows(const float* src, const int32_t* rows, int R, int d, float* dst,
-                              hipStream_t s) {
+                              const float* g, float* u, float* ssp, int stride, hipStream_t s) {
   if (R <= 0) return hipSuccess;
-  gather_rows_kernel<<<R, 256, 0, s>>>(src, rows, d, dst);
+  gather_rows_kernel<<<R, 256, 0, s>>>(src, rows, d, dst, g, u, ssp, stride);
   return hipGetLastError();
 }
 
@@ -180,6 +224,23 @@ __device__ __forceinline__ void load8(const void* base, int64_t idx, float w[8])
   }
 }
 
+// 8 weights from raw 16-byte vectors (one for bf16, two for float32)
+template <bool BF16>
+__device__ __forceinline__ void unpack_w(const uint4* raw, float w[8]) {
+  if (BF16) {
+    const uint32_t p[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[2 * j] = __builtin_bit_cast(float, p[j] << 16);
+      w[2 * j + 1] = __builtin_bit_cast(float, p[j] & 0xFFFF0000u);
+    }
+  } else {
+    const uint32_t p[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = __builtin_bit_cast(float, p[j]);
+  }
+}
+
 template <bool BF16>
 __device__ __forceinline__ float load1(const void* base, int64_t idx) {
   return BF16 ? bf16_to_f32(((const uint16_t*)base)[idx]) : ((const float*)base)[idx];
@@ -192,112 +253,162 @@ __device__ __forceinline__ void kv_put(void* cache, int64_t idx, float v) {
 
 template <bool BF16, int NT, int EPI, typename KvT, bool NORM>
 __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt) {
-  const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ float red[4][NT];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wave = blockIdx.x * 4 + wid;
   const int N = a.n0 + a.n1 + a.n2;
   const int K = a.K;
-  // the two rows of this wave
+  // the two rows of this wave (inactive waves still join the block reduction)
   int r0, r1;
-  const void *p0, *p1;
-  int64_t off0, off1;
+  const void *p0 = a.w0, *p1 = a.w0;
+  int64_t off0 = 0, off1 = 0;
+  bool active;
   if (EPI == EPI_SWIGLU) {
-    if (wave >= a.n0) return;
+    active = wave < a.n0;
     r0 = r1 = wave;
     p0 = a.w0; p1 = a.w1;
     off0 = off1 = (int64_t)wave * K;
   } else {
     r0 = 2 * wave;
-    if (r0 >= N) return;
+    active = r0 < N;
     r1 = r0 + 1 < N ? r0 + 1 : r0;
     auto locate = [&](int r, const void*& p, int64_t& off) {
       if (r < a.n0) { p = a.w0; off = (int64_t)r * K; }
       else if (r < a.n0 + a.n1) { p = a.w1; off = (int64_t)(r - a.n0) * K; }
       else { p = a.w2; off = (int64_t)(r - a.n0 - a.n1) * K; }
     };
-    locate(r0, p0, off0);
-    locate(r1, p1, off1);
+    if (active) {
+      locate(r0, p0, off0);
+      locate(r1, p1, off1);
+    }
   }
   const float* act = a.act_f32 + (int64_t)t0 * K;
 
-  float acc0[NT], acc1[NT], ss[NT];
+  float acc0[NT], acc1[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc0[t] = acc1[t] = ss[t] = 0.f;
+  for (int t = 0; t < NT; ++t) acc0[t] = acc1[t] = 0.f;
 
-  const bool vec = (K & 7) == 0;
-  if (vec) {
-    // four 16-byte weight loads per row in flight per lane
-#pragma unroll 4
-    for (int k = lane * 8; k < K; k += 512) {
-      float w0[8], w1[8];
-      load8<BF16>(p0, off0 + k, w0);
-      load8<BF16>(p1, off1 + k, w1);
-      float g[8];
-      if (NORM) {
-        const float4 g0 = *(const float4*)(a.norm_g + k);
-        const float4 g1 = *(const float4*)(a.norm_g + k + 4);
-        g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w;
-        g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
-      }
+  if (active) {
+    if ((K & 7) == 0) {
+      // Batches of U chunks of 512 elements: every lane issues all 2*U weight
+      // loads (16 bytes of bf16 each) and the activation loads of the batch
+      // before it waits, so each wave keeps 2*U KB of weights in flight.
+      constexpr int U = BF16 ? 4 : 2;
+      constexpr int WV = BF16 ? 1 : 2;  // 16-byte vectors per 8 weights
+      const int n_full = K / 512;
+      int it = 0;
+      for (; it + U <= n_full; it += U) {
+        uint4 raw0[U][WV], raw1[U][WV];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t < nt) {
-          const float4 x0 = *(const float4*)(act + (int64_t)t * K + k);
-          const float4 x1 = *(const float4*)(act + (int64_t)t * K + k + 4);
-          float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-          if (NORM) {
+        for (int u = 0; u < U; ++u) {
+          const int64_t k = (int64_t)(it + u) * 512 + lane * 8;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              ss[t] = fmaf(x[j], x[j], ss[t]);
-              x[j] *= g[j];
+          for (int v = 0; v < WV; ++v) {
+            raw0[u][v] = *(const uint4*)((const char*)p0 + (off0 + k) * (BF16 ? 2 : 4) + 16 * v);
+            raw1[u][v] = *(const uint4*)((const char*)p1 + (off1 + k) * (BF16 ? 2 : 4) + 16 * v);
+          }
+        }
+        float4 xa[NT][U], xb[NT][U];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          if (t < nt) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+              const int k = (it + u) * 512 + lane * 8;
+              xa[t][u] = *(const float4*)(act + (int64_t)t * K + k);
+              xb[t][u] = *(const float4*)(act + (int64_t)t * K + k + 4);
             }
           }
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            acc0[t] = fmaf(w0[j], x[j], acc0[t]);
-            acc1[t] = fmaf(w1[j], x[j], acc1[t]);
-          }
+        for (int u = 0; u < U; ++u) {
+          float w0[8], w1[8];
+          unpack_w<BF16>(raw0[u], w0);
+          unpack_w<BF16>(raw1[u], w1);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            if (t < nt) {
+              const float x[8] = {xa[t][u].x, xa[t][u].y, xa[t][u].z, xa[t][u].w,
+                                  xb[t][u].x, xb[t][u].y, xb[t][u].z, xb[t][u].w};
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                acc0[t] = fmaf(w0[j], x[j], acc0[t]);
+                acc1[t] = fmaf(w1[j], x[j], acc1[t]);
+              }
+            }
         }
       }
-    }
-  } else {
-    for (int k = lane; k < K; k += 64) {
-      const float w0 = load1<BF16>(p0, off0 + k), w1 = load1<BF16>(p1, off1 + k);
-      const float g = NORM ? a.norm_g[k] : 1.f;
+      // remaining chunks (fewer than U) and the ragged end of the row
+      for (int k = it * 512 + lane * 8; k < K; k += 512) {
+        float w0[8], w1[8];
+        load8<BF16>(p0, off0 + k, w0);
+        load8<BF16>(p1, off1 + k, w1);
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        if (t < nt) {
-          float x = act[(int64_t)t * K + k];
-          if (NORM) {
-            ss[t] = fmaf(x, x, ss[t]);
-            x *= g;
+        for (int t = 0; t < NT; ++t)
+          if (t < nt) {
+            const float4 x0 = *(const float4*)(act + (int64_t)t * K + k);
+            const float4 x1 = *(const float4*)(act + (int64_t)t * K + k + 4);
+            const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              acc0[t] = fmaf(w0[j], x[j], acc0[t]);
+              acc1[t] = fmaf(w1[j], x[j], acc1[t]);
+            }
           }
-          acc0[t] = fmaf(w0, x, acc0[t]);
-          acc1[t] = fmaf(w1, x, acc1[t]);
-        }
+      }
+    } else {
+      for (int k = lane; k < K; k += 64) {
+        const float w0 = load1<BF16>(p0, off0 + k), w1 = load1<BF16>(p1, off1 + k);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          if (t < nt) {
+            const float x = act[(int64_t)t * K + k];
+            acc0[t] = fmaf(w0, x, acc0[t]);
+            acc1[t] = fmaf(w1, x, acc1[t]);
+          }
+      }
     }
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     acc0[t] = wave_sum(acc0[t]);
     acc1[t] = wave_sum(acc1[t]);
-    if (NORM) {
-      const float r = 1.0f / sqrtf(wave_sum(ss[t]) / (float)K + a.norm_eps);
+    if (NORM && t < nt) {
+      // RMS scale from the producer's partial sums of x^2
+      float ss = 0.f;
+      for (int p = lane; p < a.norm_nparts; p += 64) ss += a.norm_ssp[(int64_t)(t0 + t) * a.norm_stride + p];
+      const float r = 1.0f / sqrtf(wave_sum(ss) / (float)K + a.norm_eps);
       acc0[t] *= r;
       acc1[t] *= r;
     }
   }
   // lane t writes token t
+  const bool produce = EPI == EPI_RESIDUAL && a.next_g != nullptr;
+  float sq[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    if (lane != t || t >= nt) continue;
+    sq[t] = 0.f;
+    if (!active || lane != t || t >= nt) continue;
     const int tg = t0 + t;
     const float y0 = acc0[t], y1 = acc1[t];
     if (EPI == EPI_STORE) {
       a.out[(int64_t)tg * a.ldo + r0] = y0;
       if (r1 != r0) a.out[(int64_t)tg * a.ldo + r1] = y1;
     } else if (EPI == EPI_RESIDUAL) {
-      a.out[(int64_t)tg * a.ldo + r0] += y0;
-      if (r1 != r0) a.out[(int64_t)tg * a.ldo + r1] += y1;
+      float* xo = a.out + (int64_t)tg * a.ldo;
+      const float x0 = xo[r0] + y0;
+      xo[r0] = x0;
+      if (produce) {
+        a.next_u[(int64_t)tg * a.ldo + r0] = a.next_g[r0] * x0;
+        sq[t] = x0 * x0;
+      }
+      if (r1 != r0) {
+        const float x1 = xo[r1] + y1;
+        xo[r1] = x1;
+        if (produce) {
+          a.next_u[(int64_t)tg * a.ldo + r1] = a.next_g[r1] * x1;
+          sq[t] += x1 * x1;
+        }
+      }
     } else if (EPI == EPI_SWIGLU) {
       a.out[(int64_t)tg * a.ldo + r0] = silu(y0) * y1;
     } else if (EPI == EPI_QKV) {
@@ -326,7 +437,21 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
       }
     }
   }
+  if (produce) {
+    // per-block partial sums of x_new^2, one per token
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float v = __shfl(sq[t], t, kWave);
+      if (lane == 0) red[wid][t] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < nt)
+      a.next_ssp[(int64_t)(t0 + threadIdx.x) * a.next_stride + blockIdx.x] =
+          red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] + red[3][threadIdx.x];
+  }
 }
+
+int gemv_residual_parts(int N) { return ((N + 1) / 2 + 3) / 4; }
 
 template <bool BF16, int NT, int EPI, typename KvT>
 static hipError_t gemv_launch_t(const LinearArgs& a, hipStream_t s) {
@@ -335,7 +460,7 @@ static hipError_t gemv_launch_t(const LinearArgs& a, hipStream_t s) {
   const int blocks = (waves + 3) / 4;
   for (int t0 = 0; t0 < a.T; t0 += NT) {
     const int nt = a.T - t0 < NT ? a.T - t0 : NT;
-    if (a.norm_g)
+    if (a.norm_ssp)
       gemv_kernel<BF16, NT, EPI, KvT, true><<<blocks, 256, 0, s>>>(a, t0, nt);
     else
       gemv_kernel<BF16, NT, EPI, KvT, false><<<blocks, 256, 0, s>>>(a, t0, nt);
@@ -499,6 +624,22 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
     }
   }
   __syncthreads();
+  const int nch = (nvis + a.chunk - 1) / a.chunk;
+  if (nch == 1) {
+    // the whole visible range is in this block: normalise and write
+#pragma unroll
+    for (int o = 0; o < OUT_PER; ++o) {
+      const int id = tid + o * 256;
+      if (id < G * HD) {
+        const int h = id / HD, d = id % HD;
+        const float r = acc[o] / l_s[h];
+        const int64_t oi = ((int64_t)t * a.H + g * G + h) * HD + d;
+        if (a.out) a.out[oi] = r;
+        if (a.out_hi) split_bf16(r, a.out_hi[oi], a.out_lo[oi]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int o = 0; o < OUT_PER; ++o) {
     const int id = tid + o * 256;
@@ -518,6 +659,7 @@ template <int HD>
 __global__ void __launch_bounds__(HD) attn_merge_kernel(AttnArgs a) {
   const int h = blockIdx.x, t = blockIdx.y, d = threadIdx.x;
   const int nch = (a.n_vis[t] + a.chunk - 1) / a.chunk;
+  if (nch == 1 && !a.merge_single) return;  // the split kernel wrote this token already
   const int64_t base = ((int64_t)t * a.H + h) * a.n_chunks;
   float M = -INFINITY;
 #pragma unroll 8
@@ -549,6 +691,8 @@ static hipError_t attn_launch_hd(const AttnArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // a single chunk per token writes its output directly
+  if (a.n_chunks == 1) return hipSuccess;
   return launch_attention_merge(a, s);
 }
 

@@ -26,10 +26,19 @@ struct LinearArgs {
   int weight_bf16 = 1;         // 1: bf16 weights, 0: float32
   // activations: float32 [T][K] (GEMV), or a bf16 pair hi + lo [T][K] (GEMM)
   const float* act_f32 = nullptr;
-  // GEMV only: when set, act_f32 is the raw residual x and the kernel applies
-  // RMSNorm on the fly: y = (sum_k W[n][k] g[k] x[k]) / sqrt(mean(x^2) + eps)
-  const float* norm_g = nullptr;
+  // GEMV RMSNorm consumer: when norm_ssp is set, act_f32 holds u = g * x (the
+  // gain times the raw residual) and y = (sum_k W[n][k] u[k]) / sqrt(ss/K + eps)
+  // with ss = sum of norm_ssp[t][0 .. norm_nparts) (partial sums of x^2)
+  const float* norm_ssp = nullptr;
+  int norm_nparts = 0, norm_stride = 0;
   float norm_eps = 0.f;
+  // GEMV residual producer: when next_g is set, the EPI_RESIDUAL epilogue also
+  // writes next_u[t][n] = next_g[n] * x_new[t][n] and, per block, the partial
+  // sum of x_new^2 over its rows to next_ssp[t][blockIdx]
+  const float* next_g = nullptr;
+  float* next_u = nullptr;
+  float* next_ssp = nullptr;
+  int next_stride = 0;
   const uint16_t* act_hi = nullptr;
   const uint16_t* act_lo = nullptr;
   // epilogue
@@ -54,18 +63,22 @@ hipError_t launch_linear_gemv(const LinearArgs& a, hipStream_t s);
 hipError_t launch_linear_gemm(const LinearArgs& a, hipStream_t s);
 bool gemm_supported(const LinearArgs& a);
 
-// x[t][:] = E[token[t]][:] (to float32)
+// x[t][:] = E[token[t]][:] (to float32); with g set also u = g * x and
+// ssp[t * stride] = sum x^2 (one partial per row)
 hipError_t launch_embed(const void* table, int weight_bf16, const int32_t* tokens, int T, int d,
-                        float* x, hipStream_t s);
+                        float* x, const float* g, float* u, float* ssp, int stride, hipStream_t s);
+// number of blocks (= partial sums) a residual GEMV writes for N rows
+int gemv_residual_parts(int N);
 // out = x / sqrt(mean(x^2) + eps) * g, as float32 and/or a bf16 pair
 // (hi = bf16(out), lo = bf16(out - hi))
 hipError_t launch_rmsnorm(const float* x, const float* g, int T, int d, float eps, float* out_f32,
                           uint16_t* out_hi, uint16_t* out_lo, hipStream_t s);
 // dst[pairs[2i]] = pairs[2i+1]
 hipError_t launch_scatter(int32_t* dst, const int64_t* pairs, int n, hipStream_t s);
-// dst[r][:] = src[rows[r]][:]
+// dst[r][:] = src[rows[r]][:] (rows == NULL: identity, dst == NULL: no copy);
+// with g set also u[r] = g * src[rows[r]] and ssp[r * stride] = its sum of squares
 hipError_t launch_gather_rows(const float* src, const int32_t* rows, int R, int d, float* dst,
-                              hipStream_t s);
+                              const float* g, float* u, float* ssp, int stride, hipStream_t s);
 // tok[r] = argmax_n logits[r][n] (lowest index on ties)
 hipError_t launch_argmax(const float* logits, int R, int V, int32_t* tok, hipStream_t s);
 
@@ -85,6 +98,10 @@ struct AttnArgs {
   int n_chunks = 1;      // splits of the longest token
   float* part_acc = nullptr;  // [T][H][n_chunks][hd]
   float* part_ml = nullptr;   // [T][H][n_chunks][2]
+  // merge kernel: also merge tokens with a single chunk (the prefill split
+  // kernel always writes partials; the decode split kernel writes such tokens
+  // directly)
+  int merge_single = 0;
   float* out = nullptr;       // [T][H][hd] float32
   uint16_t* out_hi = nullptr; // optional bf16 pair
   uint16_t* out_lo = nullptr;

@@ -92,7 +92,10 @@ struct tdf_context {
   size_t kv_layer_bytes = 0;        // one of K or V of one layer
   int32_t* cell_list = nullptr;     // [n_seq_max][n_ctx]
   double* inv_freq = nullptr;       // [hd/2]
-  float *x = nullptr, *xs = nullptr, *act = nullptr, *q = nullptr, *o = nullptr, *mb = nullptr;
+  float *x = nullptr, *xs = nullptr, *q = nullptr, *o = nullptr, *mb = nullptr;
+  // decode-path RMSNorm hand-off: u = g * x rows and partial sums of x^2
+  float *u = nullptr, *ssp = nullptr;
+  int ssp_stride = 0;
   // bf16 hi/lo pairs of the matrix-core inputs: normed rows, attention output, MLP product
   uint16_t *h_hi = nullptr, *h_lo = nullptr, *o_hi = nullptr, *o_lo = nullptr, *m_hi = nullptr, *m_lo = nullptr;
   float *part_acc = nullptr, *part_ml = nullptr;
@@ -318,7 +321,9 @@ extern "C" tdf_context* tdf_context_create(const tdf_model* m, const tdf_context
   A((void**)&c->inv_freq, (size_t)(hd / 2) * sizeof(double));
   A((void**)&c->x, (size_t)U * d * 4);
   A((void**)&c->xs, (size_t)U * d * 4);
-  A((void**)&c->act, (size_t)U * d * 4);
+  A((void**)&c->u, (size_t)U * d * 4);
+  c->ssp_stride = std::max(1, gemv_residual_parts(d));
+  A((void**)&c->ssp, (size_t)U * c->ssp_stride * 4);
   A((void**)&c->q, (size_t)U * H * hd * 4);
   A((void**)&c->o, (size_t)U * H * hd * 4);
   A((void**)&c->mb, (size_t)U * F * 4);
@@ -374,6 +379,7 @@ struct UbatchDev {
   int n_list_writes = 0;
   const int32_t *tile_tokens = nullptr, *tile_off = nullptr, *tile_nvis = nullptr;
   int n_tiles = 0;
+  bool sel_identity = false;  // selected rows are exactly 0..T-1
   int nvis_max = 0;
   int out_row0 = 0;  // first logits row of this ubatch
 };
@@ -397,36 +403,55 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
   const bool wbf16 = h.weight_dtype == TDF_BF16;
   hipStream_t s = c->stream;
   int T = u.T;
+  auto use_mfma = [&](int rows, int K) { return wbf16 && rows > kDecodeMaxT && K % 64 == 0; };
+  auto attn_gain = [&](int l) { return (const float*)(l < L ? m->layers[l].attn_norm : m->output_norm); };
 
-  const bool ub_mfma = wbf16 && T > kDecodeMaxT;
-  int ps = prof_begin(c, TDF_OP_EMBED, ub_mfma);
-  TDF_HIP(launch_embed(m->token_embd, wbf16, u.tokens, T, d, c->x, s));
+  // RMSNorm hand-off to the decode GEMV: c->u holds g * x of the rows in
+  // `cur`, c->ssp their partial sums of x^2 (u_parts per row), produced by the
+  // kernel that last wrote `cur` (embedding, residual GEMV, row gather) or by
+  // an explicit pass when that kernel could not (matrix-core producer).
+  int u_parts = 0;  // 0: not ready
+  float* cur = c->x;  // residual rows being carried
+  auto prep_norm = [&](const float* g, int rows) -> int {
+    const int ps = prof_begin(c, TDF_OP_NORM, false);
+    TDF_HIP(launch_gather_rows(cur, nullptr, rows, d, nullptr, g, c->u, c->ssp, c->ssp_stride, s));
+    prof_end(c, ps);
+    u_parts = 1;
+    return TDF_OK;
+  };
+
+  const bool first_gemv = !use_mfma(T, d);
+  int ps = prof_begin(c, TDF_OP_EMBED, !first_gemv);
+  TDF_HIP(launch_embed(m->token_embd, wbf16, u.tokens, T, d, c->x, first_gemv ? attn_gain(0) : nullptr,
+                       c->u, c->ssp, c->ssp_stride, s));
   TDF_HIP(launch_scatter(c->cell_list, u.list_writes, u.n_list_writes, s));
   prof_end(c, ps);
+  if (first_gemv) u_parts = 1;
 
-  auto use_mfma = [&](int rows, int K) { return wbf16 && rows > kDecodeMaxT && K % 64 == 0; };
-  float* cur = c->x;  // residual rows being carried
   for (int l = 0; l < L; ++l) {
     const tdf_layer_weights& W = m->layers[l];
     // attention block
     const bool big = use_mfma(T, d);
-    if (big) {  // the decode GEMV applies RMSNorm itself
+    if (big) {
       ps = prof_begin(c, TDF_OP_NORM, big);
       TDF_HIP(launch_rmsnorm(cur, (const float*)W.attn_norm, T, d, h.rms_eps, nullptr, c->h_hi, c->h_lo, s));
       prof_end(c, ps);
+    } else if (!u_parts) {
+      if (int rc = prep_norm((const float*)W.attn_norm, T)) return rc;
     }
     LinearArgs qa;
     qa.w0 = W.wq; qa.w1 = W.wk; qa.w2 = W.wv;
     qa.n0 = H * hd; qa.n1 = Hkv * hd; qa.n2 = Hkv * hd;
     qa.K = d; qa.T = T; qa.weight_bf16 = wbf16;
-    qa.act_f32 = cur; qa.act_hi = c->h_hi; qa.act_lo = c->h_lo;
-    qa.norm_g = (const float*)W.attn_norm; qa.norm_eps = h.rms_eps;
+    qa.act_f32 = c->u; qa.act_hi = c->h_hi; qa.act_lo = c->h_lo;
+    qa.norm_ssp = c->ssp; qa.norm_nparts = u_parts; qa.norm_stride = c->ssp_stride; qa.norm_eps = h.rms_eps;
     qa.epi = EPI_QKV;
     qa.q_out = c->q;
     qa.k_cache = kv_k(c, l); qa.v_cache = kv_v(c, l);
     qa.kv_dtype = c->kv_dtype; qa.n_ctx = c->n_ctx; qa.head_dim = hd;
     qa.slots = u.slots; qa.pos = u.pos; qa.inv_freq = c->inv_freq;
     if (int rc = run_linear(c, qa, big, TDF_OP_QKV)) return rc;
+    u_parts = 0;
 
     if (big && prefill_attention_supported(c->kv_dtype, hd)) {
       PrefillAttnArgs pa;
@@ -449,70 +474,94 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
       pa.out = c->o; pa.out_hi = c->o_hi; pa.out_lo = c->o_lo;
       pa.merge.T = T; pa.merge.H = H; pa.merge.Hkv = Hkv; pa.merge.hd = hd;
       pa.merge.n_vis = u.n_vis; pa.merge.chunk = chunk; pa.merge.n_chunks = pa.n_splits;
+      pa.merge.merge_single = 1;
       pa.merge.part_acc = c->part_acc; pa.merge.part_ml = c->part_ml;
       pa.merge.out = c->o; pa.merge.out_hi = c->o_hi; pa.merge.out_lo = c->o_lo;
       ps = prof_begin(c, TDF_OP_ATTN, big);
       TDF_HIP(launch_attention_prefill(pa, s));
       prof_end(c, ps);
     } else {
-    AttnArgs at;
-    at.q = c->q;
-    at.k_cache = kv_k(c, l); at.v_cache = kv_v(c, l);
-    at.kv_dtype = c->kv_dtype;
-    at.cell_list = c->cell_list; at.list_off = u.list_off; at.n_vis = u.n_vis;
-    at.T = T; at.H = H; at.Hkv = Hkv; at.hd = hd; at.n_ctx = c->n_ctx;
-    const int cap = T > kDecodeMaxT ? kChunkCapPrefill : kChunkCapDecode;
-    int chunk = (u.nvis_max + cap - 1) / cap;
-    chunk = std::max(64, (chunk + 63) / 64 * 64);
-    at.chunk = chunk;
-    at.n_chunks = (u.nvis_max + chunk - 1) / chunk;
-    at.part_acc = c->part_acc; at.part_ml = c->part_ml;
-    at.out = c->o;
-    at.out_hi = big ? c->o_hi : nullptr;
-    at.out_lo = big ? c->o_lo : nullptr;
-    ps = prof_begin(c, TDF_OP_ATTN, big);
-    TDF_HIP(launch_attention_decode(at, s));
-    prof_end(c, ps);
+      AttnArgs at;
+      at.q = c->q;
+      at.k_cache = kv_k(c, l); at.v_cache = kv_v(c, l);
+      at.kv_dtype = c->kv_dtype;
+      at.cell_list = c->cell_list; at.list_off = u.list_off; at.n_vis = u.n_vis;
+      at.T = T; at.H = H; at.Hkv = Hkv; at.hd = hd; at.n_ctx = c->n_ctx;
+      const int cap = T > kDecodeMaxT ? kChunkCapPrefill : kChunkCapDecode;
+      int chunk = (u.nvis_max + cap - 1) / cap;
+      chunk = std::max(64, (chunk + 63) / 64 * 64);
+      at.chunk = chunk;
+      at.n_chunks = (u.nvis_max + chunk - 1) / chunk;
+      at.part_acc = c->part_acc; at.part_ml = c->part_ml;
+      at.out = c->o;
+      at.out_hi = big ? c->o_hi : nullptr;
+      at.out_lo = big ? c->o_lo : nullptr;
+      ps = prof_begin(c, TDF_OP_ATTN, big);
+      TDF_HIP(launch_attention_decode(at, s));
+      prof_end(c, ps);
     }
 
+    const bool last = l == L - 1;
+    // the last layer keeps only the rows whose logits are wanted before its MLP
+    const bool narrow = last && !(u.R == T && u.sel_identity);
+    const int T_mlp = last ? u.R : T;
+    const bool bigm = use_mfma(T_mlp, d) && use_mfma(T_mlp, F);
     LinearArgs oa;
     oa.w0 = W.wo; oa.n0 = d; oa.K = H * hd; oa.T = T; oa.weight_bf16 = wbf16;
     oa.act_f32 = c->o; oa.act_hi = c->o_hi; oa.act_lo = c->o_lo;
     oa.epi = EPI_RESIDUAL; oa.out = cur; oa.ldo = d;
-    if (int rc = run_linear(c, oa, big && use_mfma(T, H * hd), TDF_OP_WO)) return rc;
+    const bool wo_mfma = big && use_mfma(T, H * hd);
+    if (!wo_mfma && !bigm && !narrow) {
+      oa.next_g = (const float*)W.ffn_norm; oa.next_u = c->u; oa.next_ssp = c->ssp; oa.next_stride = c->ssp_stride;
+    }
+    if (int rc = run_linear(c, oa, wo_mfma, TDF_OP_WO)) return rc;
+    u_parts = oa.next_g ? gemv_residual_parts(d) : 0;
 
-    if (l == L - 1) {
-      // last layer: keep only the rows whose logits are wanted
+    if (last) {
       if (u.R == 0) return TDF_OK;
-      ps = prof_begin(c, TDF_OP_NORM, big);
-      TDF_HIP(launch_gather_rows(cur, u.sel, u.R, d, c->xs, s));
-      prof_end(c, ps);
-      cur = c->xs;
+      if (narrow) {
+        ps = prof_begin(c, TDF_OP_NORM, big);
+        TDF_HIP(launch_gather_rows(cur, u.sel, u.R, d, c->xs, bigm ? nullptr : (const float*)W.ffn_norm,
+                                   c->u, c->ssp, c->ssp_stride, s));
+        prof_end(c, ps);
+        cur = c->xs;
+        u_parts = bigm ? 0 : 1;
+      }
       T = u.R;
     }
     // MLP block
-    const bool bigm = use_mfma(T, d) && use_mfma(T, F);
     if (bigm) {
       ps = prof_begin(c, TDF_OP_NORM, bigm);
       TDF_HIP(launch_rmsnorm(cur, (const float*)W.ffn_norm, T, d, h.rms_eps, nullptr, c->h_hi, c->h_lo, s));
       prof_end(c, ps);
+    } else if (!u_parts) {
+      if (int rc = prep_norm((const float*)W.ffn_norm, T)) return rc;
     }
     LinearArgs ga;
     ga.w0 = W.w_gate; ga.w1 = W.w_up; ga.n0 = F; ga.K = d; ga.T = T; ga.weight_bf16 = wbf16;
-    ga.act_f32 = cur; ga.act_hi = c->h_hi; ga.act_lo = c->h_lo;
-    ga.norm_g = (const float*)W.ffn_norm; ga.norm_eps = h.rms_eps;
+    ga.act_f32 = c->u; ga.act_hi = c->h_hi; ga.act_lo = c->h_lo;
+    ga.norm_ssp = c->ssp; ga.norm_nparts = u_parts; ga.norm_stride = c->ssp_stride; ga.norm_eps = h.rms_eps;
     ga.epi = EPI_SWIGLU; ga.out = c->mb; ga.out_hi = c->m_hi; ga.out_lo = c->m_lo; ga.ldo = F;
     if (int rc = run_linear(c, ga, bigm, TDF_OP_GATE_UP)) return rc;
+    u_parts = 0;
     LinearArgs da;
     da.w0 = W.w_down; da.n0 = d; da.K = F; da.T = T; da.weight_bf16 = wbf16;
     da.act_f32 = c->mb; da.act_hi = c->m_hi; da.act_lo = c->m_lo;
     da.epi = EPI_RESIDUAL; da.out = cur; da.ldo = d;
+    const bool next_gemv = last ? !use_mfma(T, d) : !use_mfma(T, d);
+    if (!bigm && next_gemv) {
+      da.next_g = attn_gain(l + 1); da.next_u = c->u; da.next_ssp = c->ssp; da.next_stride = c->ssp_stride;
+    }
     if (int rc = run_linear(c, da, bigm, TDF_OP_DOWN)) return rc;
+    u_parts = da.next_g ? gemv_residual_parts(d) : 0;
   }
   if (L == 0) {
     if (u.R == 0) return TDF_OK;
-    TDF_HIP(launch_gather_rows(cur, u.sel, u.R, d, c->xs, s));
-    cur = c->xs;
+    if (!(u.R == T && u.sel_identity)) {
+      TDF_HIP(launch_gather_rows(cur, u.sel, u.R, d, c->xs, nullptr, nullptr, nullptr, 0, s));
+      cur = c->xs;
+      u_parts = 0;
+    }
     T = u.R;
   }
   // output norm + LM head into this ubatch's logits rows
@@ -521,11 +570,13 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     ps = prof_begin(c, TDF_OP_NORM, bigo);
     TDF_HIP(launch_rmsnorm(cur, m->output_norm, T, d, h.rms_eps, nullptr, c->h_hi, c->h_lo, s));
     prof_end(c, ps);
+  } else if (!u_parts) {
+    if (int rc = prep_norm(m->output_norm, T)) return rc;
   }
   LinearArgs la;
   la.w0 = m->output; la.n0 = V; la.K = d; la.T = T; la.weight_bf16 = wbf16;
-  la.act_f32 = cur; la.act_hi = c->h_hi; la.act_lo = c->h_lo;
-  la.norm_g = m->output_norm; la.norm_eps = h.rms_eps;
+  la.act_f32 = c->u; la.act_hi = c->h_hi; la.act_lo = c->h_lo;
+  la.norm_ssp = c->ssp; la.norm_nparts = u_parts; la.norm_stride = c->ssp_stride; la.norm_eps = h.rms_eps;
   la.epi = EPI_STORE; la.out = c->logits + (size_t)u.out_row0 * V; la.ldo = V;
   return run_linear(c, la, bigo, TDF_OP_LM_HEAD);
 }
@@ -638,6 +689,7 @@ extern "C" int32_t tdf_decode(tdf_context* c, const tdf_batch* b) {
     UbatchDev ud;
     ud.T = T;
     ud.R = (int)sel.size();
+    ud.sel_identity = ud.R == T;
     ud.tokens = d32; ud.pos = d32 + T; ud.slots = d32 + 2 * T;
     ud.list_off = d32 + 3 * T; ud.n_vis = d32 + 4 * T; ud.sel = d32 + 5 * T;
     ud.list_writes = d64;
