@@ -70,58 +70,36 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
   // [0, NT/2) and up tiles [NT/2, NT) for the same BN/4 columns
   const int n0 = EPI == EPI_SWIGLU ? tn * (BN / 2) : tn * BN;
 
+  // Each thread stages 16-byte pieces: row (tid / 8) + 32 i, k offset
+  // (tid % 8) * 8.  Rows past the end are clamped to a valid row; their
+  // products are discarded by the epilogue's bounds checks.
   const int kc = (tid & 7) * 8;
-  int64_t aoff[A_PER];
-  bool aok[A_PER];
+  const uint16_t* ap_hi[A_PER];
+  const uint16_t* ap_lo[A_PER];
 #pragma unroll
   for (int i = 0; i < A_PER; ++i) {
-    const int gm = m0 + (tid >> 3) + 32 * i;
-    aok[i] = gm < M;
-    aoff[i] = (int64_t)(aok[i] ? gm : 0) * K;
+    const int gm = min(m0 + (tid >> 3) + 32 * i, M - 1);
+    ap_hi[i] = a.act_hi + (int64_t)gm * K + kc;
+    ap_lo[i] = a.act_lo + (int64_t)gm * K + kc;
   }
-  const uint16_t* brow[B_PER];
+  const uint16_t* bp[B_PER];
 #pragma unroll
   for (int i = 0; i < B_PER; ++i) {
     const int r = (tid >> 3) + 32 * i;
-    const uint16_t* p = nullptr;
     if (EPI == EPI_SWIGLU) {
       constexpr int WN = BN / 2, HALF = WN / 2;
       const int part = r / WN, rr = r % WN;
-      const int f = n0 + part * HALF + (rr % HALF);
-      if (f < a.n0) p = (const uint16_t*)(rr >= HALF ? a.w1 : a.w0) + (int64_t)f * K;
+      const int f = min(n0 + part * HALF + (rr % HALF), a.n0 - 1);
+      bp[i] = (const uint16_t*)(rr >= HALF ? a.w1 : a.w0) + (int64_t)f * K + kc;
     } else {
-      const int gr = n0 + r;
-      if (gr < a.n0) p = (const uint16_t*)a.w0 + (int64_t)gr * K;
-      else if (gr < a.n0 + a.n1) p = (const uint16_t*)a.w1 + (int64_t)(gr - a.n0) * K;
-      else if (gr < Ntot) p = (const uint16_t*)a.w2 + (int64_t)(gr - a.n0 - a.n1) * K;
+      const int gr = min(n0 + r, Ntot - 1);
+      if (gr < a.n0) bp[i] = (const uint16_t*)a.w0 + (int64_t)gr * K + kc;
+      else if (gr < a.n0 + a.n1) bp[i] = (const uint16_t*)a.w1 + (int64_t)(gr - a.n0) * K + kc;
+      else bp[i] = (const uint16_t*)a.w2 + (int64_t)(gr - a.n0 - a.n1) * K + kc;
     }
-    brow[i] = p;
   }
 
-  uint4 rah[A_PER], ral[A_PER], rb[B_PER];
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  auto gload = [&](int k) {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      rah[i] = aok[i] ? *(const uint4*)(a.act_hi + aoff[i] + k + kc) : zero;
-      ral[i] = aok[i] ? *(const uint4*)(a.act_lo + aoff[i] + k + kc) : zero;
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) rb[i] = brow[i] ? *(const uint4*)(brow[i] + k + kc) : zero;
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      *(uint4*)&Ah[r * GPITCH + kc] = rah[i];
-      *(uint4*)&Al[r * GPITCH + kc] = ral[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      *(uint4*)&Bs[r * GPITCH + kc] = rb[i];
-    }
-  };
+  bf16x8 rah[A_PER], ral[A_PER], rb[B_PER];
 
   f32x16 acc[MT][NT];
 #pragma unroll
@@ -131,14 +109,39 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  gload(k_begin);
-  lstore();
+  // first K tile
+#pragma unroll
+  for (int i = 0; i < A_PER; ++i) {
+    rah[i] = *(const bf16x8*)(ap_hi[i] + k_begin);
+    ral[i] = *(const bf16x8*)(ap_lo[i] + k_begin);
+  }
+#pragma unroll
+  for (int i = 0; i < B_PER; ++i) rb[i] = *(const bf16x8*)(bp[i] + k_begin);
+#pragma unroll
+  for (int i = 0; i < A_PER; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    *(bf16x8*)&Ah[r * GPITCH + kc] = rah[i];
+    *(bf16x8*)&Al[r * GPITCH + kc] = ral[i];
+  }
+#pragma unroll
+  for (int i = 0; i < B_PER; ++i) *(bf16x8*)&Bs[((tid >> 3) + 32 * i) * GPITCH + kc] = rb[i];
   __syncthreads();
 
   const int frow = lane & 31;
   const int fk = (lane >> 5) * 8;
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload(k_begin + (kt + 1) * GBK);
+    const bool more = kt + 1 < nk;
+    if (more) {
+      // prefetch the next K tile into registers while the MFMAs run
+      const int kn = k_begin + (kt + 1) * GBK;
+#pragma unroll
+      for (int i = 0; i < A_PER; ++i) {
+        rah[i] = *(const bf16x8*)(ap_hi[i] + kn);
+        ral[i] = *(const bf16x8*)(ap_lo[i] + kn);
+      }
+#pragma unroll
+      for (int i = 0; i < B_PER; ++i) rb[i] = *(const bf16x8*)(bp[i] + kn);
+    }
 #pragma unroll
     for (int kk = 0; kk < GBK; kk += 16) {
       bf16x8 ah[MT], al[MT], bfr[NT];
@@ -159,9 +162,16 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
         }
     }
-    if (kt + 1 < nk) {
+    if (more) {
       __syncthreads();
-      lstore();
+#pragma unroll
+      for (int i = 0; i < A_PER; ++i) {
+        const int r = (tid >> 3) + 32 * i;
+        *(bf16x8*)&Ah[r * GPITCH + kc] = rah[i];
+        *(bf16x8*)&Al[r * GPITCH + kc] = ral[i];
+      }
+#pragma unroll
+      for (int i = 0; i < B_PER; ++i) *(bf16x8*)&Bs[((tid >> 3) + 32 * i) * GPITCH + kc] = rb[i];
       __syncthreads();
     }
   }
