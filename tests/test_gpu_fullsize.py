@@ -1,0 +1,187 @@
+"""GPU parity at the workloads' full sizes.
+
+The float64 oracle cannot replay an 8B/70B prompt of thousands of tokens in
+seconds, so full-depth cases restore the cache from the same synthetic
+post-RoPE K/V on both sides (through tdf_kv_import / OracleContext.kv_import,
+values drawn by tdf_synth) and compare the outputs the oracle can compute one
+by one: a matrix-core ubatch on top of the restored context and single-token
+decode steps.  The multi-sequence workload is checked in full for its
+bookkeeping (cells, positions, rows) and on a two-layer full-width model for
+its math, using the independence of sequences.  Tolerances as in
+test_gpu_parity.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import tdf_synth
+from oracle import OracleContext
+
+from gpu_common import TOL_BF16, check_logits, check_token, device_model, log, make_weights, oracle_model
+
+pytestmark = pytest.mark.gpu
+
+
+def _fill(cfg, P):
+    L = cfg["n_layer"]
+    return ([tdf_synth.kv_fill(cfg, l, "k", 0, P, "bf16") for l in range(L)],
+            [tdf_synth.kv_fill(cfg, l, "v", 0, P, "bf16") for l in range(L)])
+
+
+def _restored_pair(cfg, w, P, n_ctx, cache):
+    """GPU and oracle contexts with positions [0, P) of sequence 0 restored."""
+    import transformer_decode_forward_amd as tdf
+    from transformer_decode_forward_amd.device import to_device
+    ks, vs = _fill(cfg, P)
+    gm = device_model(cfg, w)
+    gc = tdf.Context(gm, n_ctx=n_ctx, n_ubatch=512, kv_dtype="bf16")
+    kd = [to_device(k) for k in ks]
+    vd = [to_device(v) for v in vs]
+    assert gc.kv_import(0, 0, P, [t.data_ptr() for t in kd], [t.data_ptr() for t in vd]) == 0
+    del kd, vd
+    oc = OracleContext(oracle_model(cfg, w, cache=cache), n_ctx=n_ctx, kv_dtype="bf16")
+    assert oc.kv_import(0, 0, P, ks, vs) == 0
+    assert gc.last_slots() == list(oc.last_import_cells)
+    return gm, gc, oc
+
+
+def test_llama1b_full_workload_shape():
+    """1B-class model at full depth: 512-token prompt in one ubatch (last-row
+    logits), then 12 teacher-forced greedy steps (of the workload's 128)."""
+    cfg = tdf_synth.CONFIGS["llama1b"]
+    cfg, w = make_weights(cfg)
+    import transformer_decode_forward_amd as tdf
+    gm = device_model(cfg, w)
+    gc = tdf.Context(gm, n_ctx=cfg["n_ctx"], n_ubatch=512, kv_dtype="f16")
+    oc = OracleContext(oracle_model(cfg, w), n_ctx=cfg["n_ctx"], kv_dtype="f16")
+    prompt = tdf_synth.prompt(cfg, 0, cfg["prompt_len"])
+    assert gc.decode(prompt) == 0
+    ro = oc.decode(prompt)
+    assert gc.last_slots() == ro.slots
+    errs = [check_logits(gc.logits_ith(511), ro.logits[0], TOL_BF16, "1b prefill")]
+    check_token(gc.argmax_ith(511), ro.logits[0], "1b prefill")
+    nxt = int(ro.tokens[0])
+    for step in range(12):
+        assert gc.decode([nxt]) == 0
+        ro = oc.decode([nxt])
+        assert gc.last_slots() == ro.slots
+        errs.append(check_logits(gc.logits_ith(0), ro.logits[0], TOL_BF16, f"1b step {step}"))
+        check_token(gc.argmax_ith(0), ro.logits[0], f"1b step {step}")
+        nxt = int(ro.tokens[0])
+    log(f"1b full: worst max-abs {max(e[0] for e in errs):.2e}, rel-L2 {max(e[1] for e in errs):.2e}")
+
+
+def test_llama8b_full_depth():
+    """8B-class model, all 32 layers: context 2048 restored, then a 64-token
+    ubatch (matrix-core path; logits for 3 rows) and 2 decode steps."""
+    cfg = tdf_synth.CONFIGS["llama8b"]
+    cfg, w = make_weights(cfg)
+    log("8b weights generated")
+    gm, gc, oc = _restored_pair(cfg, w, 2048, 4096, cache=False)
+    toks = tdf_synth.prompt(cfg, 3, 64)
+    flags = np.zeros(64, dtype=np.int8)
+    flags[[0, 31, 63]] = 1
+    assert gc.decode(toks, logits=flags) == 0
+    ro = oc.decode(toks, logits=flags)
+    log("8b ubatch done")
+    assert gc.last_slots() == ro.slots and gc.output_ids() == ro.out_index == [0, 31, 63]
+    errs = []
+    for r, i in enumerate(ro.out_index):
+        errs.append(check_logits(gc.logits_ith(i), ro.logits[r], TOL_BF16, f"8b ubatch row {i}"))
+        check_token(gc.argmax_ith(i), ro.logits[r], f"8b ubatch row {i}")
+    nxt = int(ro.tokens[-1])
+    for step in range(2):
+        assert gc.decode([nxt]) == 0
+        ro = oc.decode([nxt])
+        assert gc.last_slots() == ro.slots
+        errs.append(check_logits(gc.logits_ith(0), ro.logits[0], TOL_BF16, f"8b step {step}"))
+        check_token(gc.argmax_ith(0), ro.logits[0], f"8b step {step}")
+        nxt = int(ro.tokens[0])
+        log(f"8b step {step} done")
+    log(f"8b full depth: worst max-abs {max(e[0] for e in errs):.2e}, rel-L2 {max(e[1] for e in errs):.2e}")
+
+
+def test_multisequence_bookkeeping_full():
+    """All 32 sequences of the multi-sequence workload (lengths uniform on
+    [1024, 8192]): prefill calls in sequence order, then lock-step steps of 32
+    tokens; cells, positions and output rows bit-exact (bookkeeping-only
+    contexts on both sides)."""
+    import transformer_decode_forward_amd as tdf
+    cfg = tdf_synth.CONFIGS["llama8b_multiseq"]
+    hp = tdf_synth.hparams(cfg)
+    lens = tdf_synth.seq_lengths(cfg)
+    gm = tdf.Model(hp, dry_run=True)
+    gc = tdf.Context(gm, n_ctx=cfg["n_ctx"], n_batch=8192, n_ubatch=512, n_seq_max=32, dry_run=True)
+    from oracle import OracleModel
+    oc = OracleContext(OracleModel(hp, {}), n_ctx=cfg["n_ctx"], n_batch=8192, n_ubatch=512, n_seq_max=32,
+                       compute=False)
+    for s in range(32):
+        toks = tdf_synth.prompt(cfg, s, int(lens[s]))
+        assert gc.decode(toks, seq_ids=[[s]] * len(toks)) == 0
+        r = oc.decode(toks, seq_ids=[[s]] * len(toks))
+        assert gc.last_slots() == r.slots
+    for step in range(4):
+        toks = tdf_synth.prompt(cfg, 100 + step, 32)
+        assert gc.decode(toks, seq_ids=[[s] for s in range(32)], logits=np.ones(32, np.int8)) == 0
+        r = oc.decode(toks, seq_ids=[[s] for s in range(32)], logits=np.ones(32, np.int8))
+        assert gc.last_slots() == r.slots and gc.output_ids() == list(range(32))
+        assert r.positions == [int(lens[s]) + step for s in range(32)]
+    for s in range(32):
+        assert gc.seq_pos_max(s) == oc.seq_pos_max(s) == int(lens[s]) + 3
+
+
+def test_multisequence_math_two_layers():
+    """Multi-sequence decode at full width on a two-layer model: 4 sequences
+    (the shortest and the longest of the workload's lengths, and two others)
+    prefilled in their own calls, then 3 lock-step steps with one token per
+    sequence and logits for every row (ubatch of 4 tokens, GEMV path), and one
+    step of 32 tokens spread over the 4 sequences (matrix-core path)."""
+    cfg = dict(tdf_synth.CONFIGS["llama8b_multiseq"])
+    lens = tdf_synth.seq_lengths(cfg)
+    order = np.argsort(lens)
+    picks = [int(order[0]), int(order[1]), int(order[-2]), int(order[-1])]
+    cfg, w = make_weights(cfg, layers=2)
+    import transformer_decode_forward_amd as tdf
+    gm = device_model(cfg, w)
+    n_ctx = int(sum(lens[p] for p in picks)) + 128
+    gc = tdf.Context(gm, n_ctx=n_ctx, n_batch=8192, n_ubatch=512, n_seq_max=4, kv_dtype="bf16")
+    oc = OracleContext(oracle_model(cfg, w), n_ctx=n_ctx, n_batch=8192, n_ubatch=512, n_seq_max=4,
+                       kv_dtype="bf16")
+    for j, s in enumerate(picks):
+        toks = tdf_synth.prompt(cfg, s, int(lens[s]))
+        assert gc.decode(toks, seq_ids=[[j]] * len(toks)) == 0
+        r = oc.decode(toks, seq_ids=[[j]] * len(toks))
+        assert gc.last_slots() == r.slots
+        check_logits(gc.logits_ith(len(toks) - 1), r.logits[0], TOL_BF16, f"seq {s} prefill")
+        log(f"seq {s} (length {lens[s]}) prefill ok")
+    calls = [dict(tokens=tdf_synth.prompt(cfg, 200 + k, 4), seq_ids=[[0], [1], [2], [3]],
+                  logits=np.ones(4, np.int8)) for k in range(3)]
+    calls.append(dict(tokens=tdf_synth.prompt(cfg, 300, 32), seq_ids=[[j % 4] for j in range(32)],
+                      logits=np.ones(32, np.int8)))
+    for k, call in enumerate(calls):
+        assert gc.decode(**call) == 0
+        r = oc.decode(**call)
+        assert gc.last_slots() == r.slots and gc.output_ids() == r.out_index
+        for row, i in enumerate(r.out_index):
+            check_logits(gc.logits_ith(i), r.logits[row], TOL_BF16, f"lock-step call {k} row {i}")
+            check_token(gc.argmax_ith(i), r.logits[row], f"lock-step call {k} row {i}")
+
+
+@pytest.mark.slow
+@pytest.mark.skipif(not os.environ.get("TDF_RUN_70B"),
+                    reason="needs ~150 GB of host memory and ~6 minutes; set TDF_RUN_70B=1 to run")
+def test_llama70b_decode_at_context_4096():
+    """70B-class model (141 GB resident): positions [0, 4096) restored, then one
+    decode step at position 4096, all 80 layers."""
+    cfg = tdf_synth.CONFIGS["llama70b"]
+    c, w = make_weights(cfg)
+    log("70b weights generated")
+    gm, gc, oc = _restored_pair(c, w, 4096, 4224, cache=False)
+    tok = int(tdf_synth.prompt(c, 5, 1)[0])
+    assert gc.decode([tok]) == 0
+    ro = oc.decode([tok])
+    assert gc.last_slots() == ro.slots
+    e = check_logits(gc.logits_ith(0), ro.logits[0], TOL_BF16, "70b step")
+    check_token(gc.argmax_ith(0), ro.logits[0], "70b step")
+    log(f"70b decode at 4096: max-abs {e[0]:.2e}, rel-L2 {e[1]:.2e}")

@@ -5,8 +5,10 @@
 // fits in the free cells, then per ubatch: place the tokens in cells and
 // commit them, upload the ubatch's small integer arrays in one copy, and
 // enqueue the layer loop of the Ollama engine page ("Deep dive: the Llama
-// forward pass in Go").  ubatches of at most 32 tokens take the decode
-// kernels (GEMV, split-K attention), larger ones the MFMA GEMM.  The logits
+// forward pass in Go").  Linear layers over at most 8 rows stream the
+// weights as GEMVs (float32 activations), larger ones run on the MFMA GEMM;
+// ubatches of at most 32 tokens use the split-K decode attention, larger ones
+// the MFMA attention.  The logits
 // of flagged rows land in one device buffer in batch order ("Steps 14-15"),
 // followed by a device argmax per row; the call synchronises its stream
 // before returning.
@@ -50,7 +52,8 @@ hipError_t dev_alloc(void** p, size_t bytes) {
 
 size_t dtype_size(int dt) { return dt == TDF_F32 ? 4 : 2; }
 
-constexpr int kDecodeMaxT = 32;     // ubatches up to this size use the decode kernels
+constexpr int kGemvMaxT = 8;        // linear layers of up to this many rows stream weights as GEMVs
+constexpr int kDecodeMaxT = 32;     // ubatches up to this size use the split-K decode attention
 constexpr int kChunkCapDecode = 256; // attention splits per token (decode)
 constexpr int kChunkCapPrefill = 32; // attention splits per token (larger ubatches)
 
@@ -403,7 +406,7 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
   const bool wbf16 = h.weight_dtype == TDF_BF16;
   hipStream_t s = c->stream;
   int T = u.T;
-  auto use_mfma = [&](int rows, int K) { return wbf16 && rows > kDecodeMaxT && K % 64 == 0; };
+  auto use_mfma = [&](int rows, int K) { return wbf16 && rows > kGemvMaxT && K % 64 == 0; };
   auto attn_gain = [&](int l) { return (const float*)(l < L ? m->layers[l].attn_norm : m->output_norm); };
 
   // RMSNorm hand-off to the decode GEMV: c->u holds g * x of the rows in
@@ -453,7 +456,7 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     if (int rc = run_linear(c, qa, big, TDF_OP_QKV)) return rc;
     u_parts = 0;
 
-    if (big && prefill_attention_supported(c->kv_dtype, hd)) {
+    if (T > kDecodeMaxT && prefill_attention_supported(c->kv_dtype, hd)) {
       PrefillAttnArgs pa;
       pa.q = c->q;
       pa.k_cache = kv_k(c, l); pa.v_cache = kv_v(c, l);
