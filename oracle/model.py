@@ -21,9 +21,15 @@ import numpy as np
 
 
 def widen(a: np.ndarray) -> np.ndarray:
-    """Exact float64 value of stored weights (float32, or uint16 bf16 bits)."""
+    """Exact float64 value of stored weights (float32, or uint16 bf16 bits).
+    A bf16 value is the float32 whose upper 16 bits are the stored bits."""
     if a.dtype == np.uint16:
-        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        src = np.ascontiguousarray(a).reshape(-1)
+        out = np.empty(src.size, dtype=np.float64)
+        step = 1 << 22
+        for i in range(0, src.size, step):
+            out[i:i + step] = (src[i:i + step].astype(np.uint32) << 16).view(np.float32)
+        return out.reshape(a.shape)
     return np.asarray(a, dtype=np.float64)
 
 

@@ -75,15 +75,15 @@ def attend(q: np.ndarray, k_vis: np.ndarray, v_vis: np.ndarray) -> np.ndarray:
     k_vis  [n, n_head_kv, hd]    rotated keys of the visible cells
     v_vis  [n, n_head_kv, hd]    values of the visible cells
     returns [n_head, hd]
+
+    Query head j uses KV head j // (n_head / n_head_kv): the heads are viewed
+    as [n_head_kv, group, hd] and each group is scored against its KV head.
     """
     n_head, hd = q.shape
     n_head_kv = k_vis.shape[1]
     group = n_head // n_head_kv
-    out = np.empty((n_head, hd), dtype=np.float64)
-    for j in range(n_head):
-        g = j // group
-        s = (k_vis[:, g, :] @ q[j]) / np.sqrt(hd)
-        a = np.exp(s - np.max(s))
-        a /= np.sum(a)
-        out[j] = a @ v_vis[:, g, :]
-    return out
+    qg = q.reshape(n_head_kv, group, hd)
+    s = np.matmul(qg, k_vis.transpose(1, 2, 0)) / np.sqrt(hd)      # [Hkv, group, n]
+    a = np.exp(s - np.max(s, axis=-1, keepdims=True))
+    a /= np.sum(a, axis=-1, keepdims=True)
+    return np.matmul(a, v_vis.transpose(1, 0, 2)).reshape(n_head, hd)  # [Hkv, group, hd]

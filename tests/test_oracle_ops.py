@@ -169,7 +169,7 @@ def test_gqa_equals_mha_with_replicated_heads_and_mha_special_case():
     v = rng.normal(size=(n, Hkv, hd))
     rep_k = np.repeat(k, H // Hkv, axis=1)  # contiguous groups: heads 0-3 -> kv 0
     rep_v = np.repeat(v, H // Hkv, axis=1)
-    np.testing.assert_allclose(ops.attend(q, k, v), ops.attend(q, rep_k, rep_v), rtol=0, atol=0)
+    np.testing.assert_allclose(ops.attend(q, k, v), ops.attend(q, rep_k, rep_v), rtol=1e-13, atol=1e-15)
     # n_head_kv == n_head is plain multi-head attention (torch library, fp64)
     ref = F.scaled_dot_product_attention(torch.from_numpy(q)[:, None, :], torch.from_numpy(rep_k).transpose(0, 1),
                                          torch.from_numpy(rep_v).transpose(0, 1))[:, 0, :].numpy()
