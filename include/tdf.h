@@ -194,6 +194,12 @@ int32_t tdf_kv_import(tdf_context *c, int32_t s, int32_t pos0, int32_t n,
 int32_t tdf_profile_read(const tdf_context *c, int32_t op, int32_t mfma, int64_t *launches, double *ms);
 int32_t tdf_profile_reset(tdf_context *c);
 
+/* Launch replay (llama.cpp walkthrough, "Step 13": graph reuse for same-shape
+ * ubatches): ubatches of up to 32 tokens run as a captured HIP graph, one per
+ * shape, replayed on later calls.  Counts of captures and replays so far.
+ * Disabled in TDF_CTX_PROFILE contexts and when TDF_NO_GRAPH=1 is set. */
+int32_t tdf_graph_counts(const tdf_context *c, int64_t *captures, int64_t *replays);
+
 /* Message of the last failure on the calling thread ("" if none). */
 const char *tdf_last_error(void);
 

@@ -84,6 +84,7 @@ def lib():
             "tdf_profile_read": (_i32, [_vp, _i32, _i32, ctypes.POINTER(ctypes.c_int64),
                                         ctypes.POINTER(ctypes.c_double)]),
             "tdf_profile_reset": (_i32, [_vp]),
+            "tdf_graph_counts": (_i32, [_vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
             "tdf_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -290,6 +291,12 @@ class Context:
                         and n.value:
                     out[(name, "mfma" if mfma else "decode")] = (n.value, ms.value)
         return out
+
+    def graph_counts(self):
+        """(captures, replays) of the decode launch graphs."""
+        cap, rep = ctypes.c_int64(), ctypes.c_int64()
+        lib().tdf_graph_counts(self.handle, ctypes.byref(cap), ctypes.byref(rep))
+        return cap.value, rep.value
 
     def profile_reset(self) -> int:
         return lib().tdf_profile_reset(self.handle)

@@ -10,6 +10,8 @@
 // "KV-cache and the Prefill / Decode stages": decode is memory-bound), so the
 // GEMV streams each weight row once with 16-byte loads per lane and keeps the
 // activations in float32.
+#include <algorithm>
+
 #include "k_common.hpp"
 #include "kernels.hpp"
 #include "tdf.h"
@@ -130,6 +132,25 @@ __global__ void scatter_kernel(int32_t* __restrict__ dst, const int64_t* __restr
 hipError_t launch_scatter(int32_t* dst, const int64_t* pairs, int n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   scatter_kernel<<<(n + 255) / 256, 256, 0, s>>>(dst, pairs, n);
+  return hipGetLastError();
+}
+
+// cs[t][i] = (cos, sin)(pos[t] * theta^(-2i/hd)), angles in double
+__global__ void rope_table_kernel(const int32_t* __restrict__ pos, const double* __restrict__ inv_freq,
+                                  int half, int n, float2* __restrict__ cs) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int t = i / half, j = i % half;
+  double sn, c;
+  sincos((double)pos[t] * inv_freq[j], &sn, &c);
+  cs[i] = make_float2((float)c, (float)sn);
+}
+
+hipError_t launch_rope_table(const int32_t* pos, const double* inv_freq, int T, int half, float2* cs,
+                             hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int n = T * half;
+  rope_table_kernel<<<(n + 255) / 256, 256, 0, s>>>(pos, inv_freq, half, n, cs);
   return hipGetLastError();
 }
 
@@ -417,10 +438,8 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
         // q or k row pair (2i, 2i+1) of one head: rotate by pos * theta^(-2i/hd)
         const int lr = r0 < a.n0 ? r0 : r0 - a.n0;
         const int i = (lr % hd) >> 1;
-        double sn, cs;
-        sincos((double)a.pos[tg] * a.inv_freq[i], &sn, &cs);
-        const float c = (float)cs, s = (float)sn;
-        const float z0 = y0 * c - y1 * s, z1 = y0 * s + y1 * c;
+        const float2 cs = a.rope_cs[(int64_t)tg * (hd >> 1) + i];
+        const float z0 = y0 * cs.x - y1 * cs.y, z1 = y0 * cs.y + y1 * cs.x;
         if (r0 < a.n0) {
           a.q_out[(int64_t)tg * a.n0 + lr] = z0;
           a.q_out[(int64_t)tg * a.n0 + lr + 1] = z1;
@@ -548,9 +567,13 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
   const ST* vc = (const ST*)a.v_cache + (int64_t)g * a.n_ctx * HD;
   const float scale = rsqrtf((float)HD);
 
-  for (int i = tid; i < G * HD; i += 256) {
-    const int h = i / HD, d = i % HD;
-    q_s[h][d] = a.q[((int64_t)t * a.H + g * G + h) * HD + d] * scale;
+  // q and the first K/V tile are requested together (one memory round trip)
+  constexpr int QPER = (G * HD + 255) / 256;
+  float qv[QPER];
+#pragma unroll
+  for (int o = 0; o < QPER; ++o) {
+    const int i = tid + o * 256;
+    qv[o] = i < G * HD ? a.q[((int64_t)t * a.H + g * G + i / HD) * HD + i % HD] * scale : 0.f;
   }
   if (tid < G) {
     m_s[tid] = -INFINITY;
@@ -561,30 +584,46 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
 #pragma unroll
   for (int o = 0; o < OUT_PER; ++o) acc[o] = 0.f;
 
+  // 16-byte pieces: 8 elements of 16-bit caches, 4 of float caches
+  constexpr int E = sizeof(ST) == 2 ? 8 : 4;
+  constexpr int PIECES = kTile * HD / E;
+  constexpr int PPER = (PIECES + 255) / 256;
   for (int c0 = c_lo; c0 < c_hi; c0 += kTile) {
     const int nc = min(kTile, c_hi - c0);
-    __syncthreads();
-    // 16-byte pieces: 8 elements of 16-bit caches, 4 of float caches
-    constexpr int E = sizeof(ST) == 2 ? 8 : 4;
-    constexpr int PIECES = kTile * HD / E;
-#pragma unroll 2
-    for (int i = tid; i < PIECES; i += 256) {
+    uint4 kr[PPER], vr[PPER];
+#pragma unroll
+    for (int pi = 0; pi < PPER; ++pi) {
+      const int i = tid + pi * 256;
       const int c = i / (HD / E), d = (i % (HD / E)) * E;
-      float kv[E], vv[E];
-      if (c < nc) {
+      if (i < PIECES && c < nc) {
         const int64_t row = (int64_t)cells[c0 + c] * HD + d;
-        const uint4 ku = *(const uint4*)(kc + row);
-        const uint4 vu = *(const uint4*)(vc + row);
-        unpack16<KvT>(ku, kv);
-        unpack16<KvT>(vu, vv);
+        kr[pi] = *(const uint4*)(kc + row);
+        vr[pi] = *(const uint4*)(vc + row);
       } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) kv[e] = vv[e] = 0.f;
+        kr[pi] = vr[pi] = make_uint4(0, 0, 0, 0);
       }
+    }
+    __syncthreads();  // the previous tile's readers are done with the LDS
+    if (c0 == c_lo) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        k_s[c][d + e] = kv[e];
-        v_s[c][d + e] = vv[e];
+      for (int o = 0; o < QPER; ++o) {
+        const int i = tid + o * 256;
+        if (i < G * HD) q_s[i / HD][i % HD] = qv[o];
+      }
+    }
+#pragma unroll
+    for (int pi = 0; pi < PPER; ++pi) {
+      const int i = tid + pi * 256;
+      if (i < PIECES) {
+        const int c = i / (HD / E), d = (i % (HD / E)) * E;
+        float kf[E], vf[E];
+        unpack16<KvT>(kr[pi], kf);
+        unpack16<KvT>(vr[pi], vf);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          k_s[c][d + e] = kf[e];
+          v_s[c][d + e] = vf[e];
+        }
       }
     }
     __syncthreads();

@@ -207,9 +207,8 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
           if (col < a.n0 + a.n1) {
             const int lc = col < a.n0 ? col : col - a.n0;
             const int i = (lc % hd) >> 1;
-            double sn, cs;
-            sincos((double)a.pos[row] * a.inv_freq[i], &sn, &cs);
-            const float c = (float)cs, s = (float)sn;
+            const float2 cs = a.rope_cs[(int64_t)row * (hd >> 1) + i];
+            const float c = cs.x, s = cs.y;
             const float z = (col & 1) ? partner * s + y * c : y * c - partner * s;
             if (col < a.n0) {
               a.q_out[(int64_t)row * a.n0 + lc] = z;

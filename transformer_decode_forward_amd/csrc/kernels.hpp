@@ -56,7 +56,7 @@ struct LinearArgs {
   int head_dim = 0;
   const int32_t* slots = nullptr;  // [T] cell of each token
   const int32_t* pos = nullptr;    // [T] position of each token
-  const double* inv_freq = nullptr;// [head_dim/2] theta^(-2i/head_dim)
+  const float2* rope_cs = nullptr; // [T][head_dim/2] (cos, sin) of pos * theta^(-2i/head_dim)
 };
 
 hipError_t launch_linear_gemv(const LinearArgs& a, hipStream_t s);
@@ -73,6 +73,9 @@ int gemv_residual_parts(int N);
 // (hi = bf16(out), lo = bf16(out - hi))
 hipError_t launch_rmsnorm(const float* x, const float* g, int T, int d, float eps, float* out_f32,
                           uint16_t* out_hi, uint16_t* out_lo, hipStream_t s);
+// cs[t][i] = (cos, sin)(pos[t] * inv_freq[i]) for i < half, angles in double
+hipError_t launch_rope_table(const int32_t* pos, const double* inv_freq, int T, int half, float2* cs,
+                             hipStream_t s);
 // dst[pairs[2i]] = pairs[2i+1]
 hipError_t launch_scatter(int32_t* dst, const int64_t* pairs, int n, hipStream_t s);
 // dst[r][:] = src[rows[r]][:] (rows == NULL: identity, dst == NULL: no copy);

@@ -16,6 +16,8 @@
 
 #include <algorithm>
 #include <cmath>
+#include <map>
+#include <tuple>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -95,6 +97,7 @@ struct tdf_context {
   size_t kv_layer_bytes = 0;        // one of K or V of one layer
   int32_t* cell_list = nullptr;     // [n_seq_max][n_ctx]
   double* inv_freq = nullptr;       // [hd/2]
+  float2* rope_cs = nullptr;        // [U][hd/2] (cos, sin) of the ubatch's positions
   float *x = nullptr, *xs = nullptr, *q = nullptr, *o = nullptr, *mb = nullptr;
   // decode-path RMSNorm hand-off: u = g * x rows and partial sums of x^2
   float *u = nullptr, *ssp = nullptr;
@@ -119,6 +122,11 @@ struct tdf_context {
   std::vector<int> ev_slot;          // slot of each recorded pair
   int64_t prof_n[2 * TDF_OP_COUNT] = {};
   double prof_ms[2 * TDF_OP_COUNT] = {};
+
+  // launch replay: one instantiated graph per decode ubatch shape
+  bool use_graphs = true;
+  std::map<std::tuple<int, int, int, int, int, const void*, const void*, int, int>, hipGraphExec_t> graphs;
+  int64_t n_graph_captures = 0, n_graph_replays = 0;
 
   // results of the last decode
   int n_outputs = 0;
@@ -192,6 +200,8 @@ static void prof_collect(tdf_context* c) {
 }
 
 static void ctx_release(tdf_context* c) {
+  for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
+  c->graphs.clear();
   for (hipEvent_t e : c->ev_pool) (void)hipEventDestroy(e);
   c->ev_pool.clear();
   for (void* p : c->owned) (void)hipFree(p);
@@ -225,6 +235,8 @@ static int ensure_logits(tdf_context* c, int rows) {
     (void)hipFree(p);
   };
   (void)hipStreamSynchronize(c->stream);
+  for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
+  c->graphs.clear();
   drop(c->logits);
   drop(c->d_tok);
   if (c->h_tok) (void)hipHostFree(c->h_tok);
@@ -298,6 +310,10 @@ extern "C" tdf_context* tdf_context_create(const tdf_model* m, const tdf_context
   c->output_all = p->output_all != 0;
   c->dry_run = (p->flags & TDF_CTX_DRY_RUN) != 0;
   c->profile = !c->dry_run && (p->flags & TDF_CTX_PROFILE) != 0;
+  {
+    const char* e = getenv("TDF_NO_GRAPH");
+    c->use_graphs = !c->profile && !(e && atoi(e) != 0);
+  }
   c->book.init(c->n_ctx, c->n_seq_max);
   if (c->dry_run) return c;
 
@@ -322,6 +338,7 @@ extern "C" tdf_context* tdf_context_create(const tdf_model* m, const tdf_context
   A(&c->kv, c->kv_layer_bytes * 2 * std::max(1, h.n_layer));
   A((void**)&c->cell_list, (size_t)c->n_seq_max * c->n_ctx * sizeof(int32_t));
   A((void**)&c->inv_freq, (size_t)(hd / 2) * sizeof(double));
+  A((void**)&c->rope_cs, (size_t)U * (hd / 2) * sizeof(float2));
   A((void**)&c->x, (size_t)U * d * 4);
   A((void**)&c->xs, (size_t)U * d * 4);
   A((void**)&c->u, (size_t)U * d * 4);
@@ -383,6 +400,7 @@ struct UbatchDev {
   const int32_t *tile_tokens = nullptr, *tile_off = nullptr, *tile_nvis = nullptr;
   int n_tiles = 0;
   bool sel_identity = false;  // selected rows are exactly 0..T-1
+  int attn_chunk = 64, attn_grid = 1;  // split-K decode attention: cells per split, splits launched
   int nvis_max = 0;
   int out_row0 = 0;  // first logits row of this ubatch
 };
@@ -428,6 +446,7 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
   TDF_HIP(launch_embed(m->token_embd, wbf16, u.tokens, T, d, c->x, first_gemv ? attn_gain(0) : nullptr,
                        c->u, c->ssp, c->ssp_stride, s));
   TDF_HIP(launch_scatter(c->cell_list, u.list_writes, u.n_list_writes, s));
+  TDF_HIP(launch_rope_table(u.pos, c->inv_freq, T, hd / 2, c->rope_cs, s));
   prof_end(c, ps);
   if (first_gemv) u_parts = 1;
 
@@ -452,7 +471,7 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     qa.q_out = c->q;
     qa.k_cache = kv_k(c, l); qa.v_cache = kv_v(c, l);
     qa.kv_dtype = c->kv_dtype; qa.n_ctx = c->n_ctx; qa.head_dim = hd;
-    qa.slots = u.slots; qa.pos = u.pos; qa.inv_freq = c->inv_freq;
+    qa.slots = u.slots; qa.pos = u.pos; qa.rope_cs = c->rope_cs;
     if (int rc = run_linear(c, qa, big, TDF_OP_QKV)) return rc;
     u_parts = 0;
 
@@ -490,11 +509,8 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
       at.kv_dtype = c->kv_dtype;
       at.cell_list = c->cell_list; at.list_off = u.list_off; at.n_vis = u.n_vis;
       at.T = T; at.H = H; at.Hkv = Hkv; at.hd = hd; at.n_ctx = c->n_ctx;
-      const int cap = T > kDecodeMaxT ? kChunkCapPrefill : kChunkCapDecode;
-      int chunk = (u.nvis_max + cap - 1) / cap;
-      chunk = std::max(64, (chunk + 63) / 64 * 64);
-      at.chunk = chunk;
-      at.n_chunks = (u.nvis_max + chunk - 1) / chunk;
+      at.chunk = u.attn_chunk;
+      at.n_chunks = u.attn_grid;
       at.part_acc = c->part_acc; at.part_ml = c->part_ml;
       at.out = c->o;
       at.out_hi = big ? c->o_hi : nullptr;
@@ -582,6 +598,49 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
   la.norm_ssp = c->ssp; la.norm_nparts = u_parts; la.norm_stride = c->ssp_stride; la.norm_eps = h.rms_eps;
   la.epi = EPI_STORE; la.out = c->logits + (size_t)u.out_row0 * V; la.ldo = V;
   return run_linear(c, la, bigo, TDF_OP_LM_HEAD);
+}
+
+// Replay of the decode launch sequence (the graph reuse of llama.cpp
+// walkthrough "Step 13": same-shape ubatches skip rebuilding).  Every
+// per-call value the kernels read lives in device memory at fixed addresses
+// (the ubatch's integers, cell lists, caches); the key holds everything that
+// enters a kernel argument.
+static int run_graphed(tdf_context* c, const UbatchDev& u) {
+  const auto key = std::make_tuple(u.T, u.R, u.n_list_writes, u.attn_chunk, u.attn_grid,
+                                   (const void*)c->logits, (const void*)u.tokens, u.out_row0,
+                                   (int)u.sel_identity);
+  auto it = c->graphs.find(key);
+  if (it == c->graphs.end()) {
+    if (c->graphs.size() >= 64) {
+      for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
+      c->graphs.clear();
+    }
+    TDF_HIP(hipStreamBeginCapture(c->stream, hipStreamCaptureModeThreadLocal));
+    const int rc = forward_ubatch(c, u);
+    hipGraph_t graph = nullptr;
+    const hipError_t e = hipStreamEndCapture(c->stream, &graph);
+    if (rc != TDF_OK) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return rc;
+    }
+    if (e != hipSuccess) {
+      set_err(std::string("graph capture failed: ") + hipGetErrorString(e));
+      return TDF_E_DEVICE;
+    }
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ei != hipSuccess) {
+      set_err(std::string("graph instantiation failed: ") + hipGetErrorString(ei));
+      return TDF_E_DEVICE;
+    }
+    it = c->graphs.emplace(key, exec).first;
+    ++c->n_graph_captures;
+  } else {
+    ++c->n_graph_replays;
+  }
+  TDF_HIP(hipGraphLaunch(it->second, c->stream));
+  return TDF_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -703,7 +762,28 @@ extern "C" int32_t tdf_decode(tdf_context* c, const tdf_batch* b) {
     ud.tile_off = ud.tile_tokens + (size_t)kQTile * n_tiles;
     ud.tile_nvis = ud.tile_off + n_tiles;
     ud.out_row0 = out_row;
-    rc = forward_ubatch(c, ud);
+    if (T <= kDecodeMaxT) {
+      // cells per split grow past 256 splits; the launched grid is the
+      // split count rounded up to a power of two (surplus blocks exit), so a
+      // captured launch sequence stays valid while the context grows
+      int chunk = (nvis_max + kChunkCapDecode - 1) / kChunkCapDecode;
+      chunk = std::max(64, (chunk + 63) / 64 * 64);
+      const int need = (nvis_max + chunk - 1) / chunk;
+      int grid = 1;
+      while (grid < need) grid *= 2;
+      ud.attn_chunk = chunk;
+      ud.attn_grid = std::min(grid, kChunkCapDecode);
+    } else {
+      int chunk = (nvis_max + kChunkCapPrefill - 1) / kChunkCapPrefill;
+      chunk = std::max(64, (chunk + 63) / 64 * 64);
+      ud.attn_chunk = chunk;
+      ud.attn_grid = (nvis_max + chunk - 1) / chunk;
+    }
+    if (c->use_graphs && T <= kDecodeMaxT) {
+      rc = run_graphed(c, ud);
+    } else {
+      rc = forward_ubatch(c, ud);
+    }
     if (rc != TDF_OK) return rc;
     out_row += ud.R;
     i32_off += (n32 + 3) & ~(size_t)3;
@@ -864,6 +944,13 @@ extern "C" int32_t tdf_profile_reset(tdf_context* c) {
     c->prof_n[i] = 0;
     c->prof_ms[i] = 0.0;
   }
+  return TDF_OK;
+}
+
+extern "C" int32_t tdf_graph_counts(const tdf_context* c, int64_t* captures, int64_t* replays) {
+  if (!c) return TDF_E_INVALID;
+  if (captures) *captures = c->n_graph_captures;
+  if (replays) *replays = c->n_graph_replays;
   return TDF_OK;
 }
 
