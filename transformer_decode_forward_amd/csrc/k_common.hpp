@@ -58,16 +58,33 @@ template <> struct KvStore<kv_f16> {
 
 // ---- wave64 reductions ---------------------------------------------------
 
+// All 64 lanes must be active.  Inside each row of 16 lanes: xor 1 and xor 2
+// (quad permutes), then the half-row and row mirrors (lane i <-> 7-i and
+// i <-> 15-i), after which every lane holds its row's result; the four rows
+// are then read out with readlane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_read(float v, float ident) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, ident),
+                                                               __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_read(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+  v += dpp_read<0xB1>(v, 0.f);
+  v += dpp_read<0x4E>(v, 0.f);
+  v += dpp_read<0x141>(v, 0.f);
+  v += dpp_read<0x140>(v, 0.f);
+  return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
+  v = fmaxf(v, dpp_read<0xB1>(v, -INFINITY));
+  v = fmaxf(v, dpp_read<0x4E>(v, -INFINITY));
+  v = fmaxf(v, dpp_read<0x141>(v, -INFINITY));
+  v = fmaxf(v, dpp_read<0x140>(v, -INFINITY));
+  return fmaxf(fmaxf(lane_read(v, 0), lane_read(v, 16)), fmaxf(lane_read(v, 32), lane_read(v, 48)));
 }
 
 // (value, index) max with the lowest index winning ties

@@ -272,7 +272,7 @@ __device__ __forceinline__ void kv_put(void* cache, int64_t idx, float v) {
   KvStore<KvT>::store((typename KvStore<KvT>::T*)cache, idx, v);
 }
 
-template <bool BF16, int NT, int EPI, typename KvT, bool NORM>
+template <bool BF16, int NT, int EPI, typename KvT, bool NORM, int U>
 __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt) {
   __shared__ float red[4][NT];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -305,6 +305,31 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
   }
   const float* act = a.act_f32 + (int64_t)t0 * K;
 
+  // RMSNorm consumer: the block's 256 threads fetch the producer's partial
+  // sums of x^2 together with the first batch of weights (same memory round
+  // trip) and add them up once per block after the row loop.  The loads use
+  // clamped indices and are masked by a multiply: a load under a divergent
+  // branch (or a select of a load, which becomes one) makes the compiler wait
+  // for every load in flight.
+  constexpr int kNormPer = 4;  // partials per thread fetched with the weights (1024 per block)
+  float nss[NORM ? NT : 1][kNormPer];
+#pragma unroll
+  for (int t = 0; t < (NORM ? NT : 1); ++t)
+#pragma unroll
+    for (int q = 0; q < kNormPer; ++q) nss[t][q] = 0.f;
+  auto norm_fetch = [&](float on) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < kNormPer; ++q) {
+        const int pidx = threadIdx.x + q * 256;
+        const int tc = t < nt ? t : nt - 1;
+        const float v = a.norm_ssp[(int64_t)(t0 + tc) * a.norm_stride + min(pidx, a.norm_nparts - 1)];
+        nss[t][q] += v * ((t < nt && pidx < a.norm_nparts) ? on : 0.f);
+      }
+  };
+  bool norm_fetched = false;
+
   float acc0[NT], acc1[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc0[t] = acc1[t] = 0.f;
@@ -312,36 +337,40 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
   if (active) {
     if ((K & 7) == 0) {
       // Batches of U chunks of 512 elements: every lane issues all 2*U weight
-      // loads (16 bytes of bf16 each) and the activation loads of the batch
-      // before it waits, so each wave keeps 2*U KB of weights in flight.
-      constexpr int U = BF16 ? 4 : 2;
+      // loads (16 bytes of bf16, or 2x16 of float32, each) and the activation
+      // loads of the batch before it waits, so each wave keeps 2*U KB of bf16
+      // weights in flight.  The
+      // last batch may be partial: its loads are clamped to the last chunk and
+      // the surplus chunks skipped (a wave-uniform test).
       constexpr int WV = BF16 ? 1 : 2;  // 16-byte vectors per 8 weights
       const int n_full = K / 512;
-      int it = 0;
-      for (; it + U <= n_full; it += U) {
+      for (int it = 0; it < n_full; it += U) {
         uint4 raw0[U][WV], raw1[U][WV];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int64_t k = (int64_t)(it + u) * 512 + lane * 8;
+          const int64_t k = (int64_t)min(it + u, n_full - 1) * 512 + lane * 8;
 #pragma unroll
           for (int v = 0; v < WV; ++v) {
             raw0[u][v] = *(const uint4*)((const char*)p0 + (off0 + k) * (BF16 ? 2 : 4) + 16 * v);
             raw1[u][v] = *(const uint4*)((const char*)p1 + (off1 + k) * (BF16 ? 2 : 4) + 16 * v);
           }
         }
+        // the norm partials ride with the first batch (counted once)
+        if (NORM) norm_fetch(it == 0 ? 1.f : 0.f);
         float4 xa[NT][U], xb[NT][U];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           if (t < nt) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-              const int k = (it + u) * 512 + lane * 8;
+              const int k = min(it + u, n_full - 1) * 512 + lane * 8;
               xa[t][u] = *(const float4*)(act + (int64_t)t * K + k);
               xb[t][u] = *(const float4*)(act + (int64_t)t * K + k + 4);
             }
           }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+          if (it + u >= n_full) break;
           float w0[8], w1[8];
           unpack_w<BF16>(raw0[u], w0);
           unpack_w<BF16>(raw1[u], w1);
@@ -358,8 +387,9 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
             }
         }
       }
-      // remaining chunks (fewer than U) and the ragged end of the row
-      for (int k = it * 512 + lane * 8; k < K; k += 512) {
+      norm_fetched = n_full > 0;
+      // the ragged end of the row (K not a multiple of 512)
+      for (int k = n_full * 512 + lane * 8; k < K; k += 512) {
         float w0[8], w1[8];
         load8<BF16>(p0, off0 + k, w0);
         load8<BF16>(p1, off1 + k, w1);
@@ -393,11 +423,27 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
   for (int t = 0; t < NT; ++t) {
     acc0[t] = wave_sum(acc0[t]);
     acc1[t] = wave_sum(acc1[t]);
-    if (NORM && t < nt) {
-      // RMS scale from the producer's partial sums of x^2
+  }
+  if (NORM) {
+    // RMS scale 1/sqrt(ss/K + eps), ss = sum of the producer's partials
+    if (!norm_fetched) norm_fetch(1.f);  // short or ragged rows, inactive waves
+    __shared__ float red_n[4][NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
       float ss = 0.f;
-      for (int p = lane; p < a.norm_nparts; p += 64) ss += a.norm_ssp[(int64_t)(t0 + t) * a.norm_stride + p];
-      const float r = 1.0f / sqrtf(wave_sum(ss) / (float)K + a.norm_eps);
+#pragma unroll
+      for (int q = 0; q < kNormPer; ++q) ss += nss[t][q];
+      if (t < nt)
+        for (int p = threadIdx.x + kNormPer * 256; p < a.norm_nparts; p += 256)
+          ss += a.norm_ssp[(int64_t)(t0 + t) * a.norm_stride + p];
+      ss = wave_sum(ss);
+      if (lane == 0) red_n[wid][t] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float ss = (red_n[0][t] + red_n[1][t]) + (red_n[2][t] + red_n[3][t]);
+      const float r = 1.0f / sqrtf(ss / (float)K + a.norm_eps);
       acc0[t] *= r;
       acc1[t] *= r;
     }
@@ -477,12 +523,20 @@ static hipError_t gemv_launch_t(const LinearArgs& a, hipStream_t s) {
   const int N = a.n0 + a.n1 + a.n2;
   const int waves = EPI == EPI_SWIGLU ? a.n0 : (N + 1) / 2;
   const int blocks = (waves + 3) / 4;
+  // chunks per batch: 8 for a single token on grids of at least 4 waves per
+  // SIMD (the large matrices), else 4 (2 for float32 weights)
+  constexpr int U_MANY = BF16 ? 4 : 2;
+  constexpr int U_BIG = BF16 && NT == 1 ? 8 : U_MANY;
+  const bool big = waves >= 4 * 1024;
   for (int t0 = 0; t0 < a.T; t0 += NT) {
     const int nt = a.T - t0 < NT ? a.T - t0 : NT;
-    if (a.norm_ssp)
-      gemv_kernel<BF16, NT, EPI, KvT, true><<<blocks, 256, 0, s>>>(a, t0, nt);
-    else
-      gemv_kernel<BF16, NT, EPI, KvT, false><<<blocks, 256, 0, s>>>(a, t0, nt);
+    if (a.norm_ssp) {
+      if (big) gemv_kernel<BF16, NT, EPI, KvT, true, U_BIG><<<blocks, 256, 0, s>>>(a, t0, nt);
+      else gemv_kernel<BF16, NT, EPI, KvT, true, U_MANY><<<blocks, 256, 0, s>>>(a, t0, nt);
+    } else {
+      if (big) gemv_kernel<BF16, NT, EPI, KvT, false, U_BIG><<<blocks, 256, 0, s>>>(a, t0, nt);
+      else gemv_kernel<BF16, NT, EPI, KvT, false, U_MANY><<<blocks, 256, 0, s>>>(a, t0, nt);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -517,10 +571,17 @@ hipError_t launch_linear_gemv(const LinearArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode attention.  Block (chunk j, kv head g, token t): the G = H/Hkv query
-// heads of the group share each K/V tile of 64 cells staged in LDS as
-// float32; online softmax (running max m, running sum l, rescaled
-// accumulator) per head.  Partials of all chunks are merged afterwards.
+// Decode attention.  Block (chunk j, kv head g, token t) runs the G = H/Hkv
+// query heads of the group over the chunk's cells, one tile of rows at a
+// time.  The cache is read in 16-byte pieces, PR = HD/E pieces per row, so a
+// row is PR adjacent lanes: each lane dots its E elements with the G queries
+// (held in registers), the PR lanes add their parts across the row (DPP), and
+// the same lanes apply the row's probabilities to their E elements of V.
+// Every row group (the PR lanes of a row) keeps its own online softmax
+// (running max m, sum l and rescaled accumulator per head), so the tile loop
+// needs no exchange between lanes beyond the row sums; the groups and the
+// four waves are combined once at the end.
+// Partials of several chunks are merged by attn_merge_kernel.
 
 constexpr int kTile = 64;
 
@@ -547,17 +608,32 @@ template <> __device__ __forceinline__ void unpack16<kv_f16>(uint4 u, float* out
   }
 }
 
+// sum over aligned groups of W adjacent lanes (W = 1..32), every lane of a
+// group receiving the group's sum: xor 1 and xor 2 inside quads, then the
+// half-row and row mirrors (lane i <-> 7-i, i <-> 15-i), then xor 16
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  if (W >= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  if (W >= 4) v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  if (W >= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  if (W >= 16) v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  if (W >= 32) v += __shfl_xor(v, 16, kWave);
+  return v;
+}
+
 template <typename KvT, int HD, int G>
 __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
   typedef typename KvStore<KvT>::T ST;
-  __shared__ float q_s[G][HD];
-  __shared__ float k_s[kTile][HD + 1];
-  __shared__ float v_s[kTile][HD];
-  __shared__ float p_s[G][kTile];
-  __shared__ float m_s[G], l_s[G], alpha_s[G];
+  constexpr int E = sizeof(ST) == 2 ? 8 : 4;          // elements per 16-byte piece
+  constexpr int PR = HD / E;                           // pieces per row: 2..32
+  constexpr int ROWS = 256 / PR;                       // rows per pass of the block
+  constexpr int TILE = ROWS > kTile ? ROWS : kTile;    // rows per tile
+  constexpr int PPER = TILE / ROWS;                    // passes per tile
+  __shared__ float acc_s[4][G][HD];
+  __shared__ float m_s[4][G], l_s[4][G];
 
   const int j = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nvis = a.n_vis[t];
   const int c_lo = j * a.chunk;
   if (c_lo >= nvis) return;
@@ -565,154 +641,244 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
   const int32_t* cells = a.cell_list + a.list_off[t];
   const ST* kc = (const ST*)a.k_cache + (int64_t)g * a.n_ctx * HD;
   const ST* vc = (const ST*)a.v_cache + (int64_t)g * a.n_ctx * HD;
-  const float scale = rsqrtf((float)HD);
+  const int r0 = tid / PR;        // row of this lane in each pass
+  const int dq = (tid % PR) * E;  // first element of this lane's piece
 
-  // q and the first K/V tile are requested together (one memory round trip)
-  constexpr int QPER = (G * HD + 255) / 256;
-  float qv[QPER];
+  // Loads come from clamped addresses, unconditionally: a load under a
+  // divergent branch makes the compiler wait for every load in flight.  The
+  // first tile's cell indices are requested together with q.
+  int row[PPER];
+  uint4 kr[PPER], vr[PPER];
 #pragma unroll
-  for (int o = 0; o < QPER; ++o) {
-    const int i = tid + o * 256;
-    qv[o] = i < G * HD ? a.q[((int64_t)t * a.H + g * G + i / HD) * HD + i % HD] * scale : 0.f;
-  }
-  if (tid < G) {
-    m_s[tid] = -INFINITY;
-    l_s[tid] = 0.f;
-  }
-  constexpr int OUT_PER = (G * HD + 255) / 256;
-  float acc[OUT_PER];
+  for (int pi = 0; pi < PPER; ++pi) row[pi] = cells[min(c_lo + r0 + pi * ROWS, c_hi - 1)];
+  float qr[G][E];
+  {
+    const float scale = rsqrtf((float)HD);
+    const float* qp = a.q + ((int64_t)t * a.H + g * G) * HD + dq;
 #pragma unroll
-  for (int o = 0; o < OUT_PER; ++o) acc[o] = 0.f;
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < E; e += 4) {
+        const float4 v = *(const float4*)(qp + h * HD + e);
+        qr[h][e] = v.x * scale; qr[h][e + 1] = v.y * scale;
+        qr[h][e + 2] = v.z * scale; qr[h][e + 3] = v.w * scale;
+      }
+  }
+#pragma unroll
+  for (int pi = 0; pi < PPER; ++pi) {
+    const int64_t off = (int64_t)row[pi] * HD + dq;
+    kr[pi] = *(const uint4*)(kc + off);
+    vr[pi] = *(const uint4*)(vc + off);
+  }
 
-  // 16-byte pieces: 8 elements of 16-bit caches, 4 of float caches
-  constexpr int E = sizeof(ST) == 2 ? 8 : 4;
-  constexpr int PIECES = kTile * HD / E;
-  constexpr int PPER = (PIECES + 255) / 256;
-  for (int c0 = c_lo; c0 < c_hi; c0 += kTile) {
-    const int nc = min(kTile, c_hi - c0);
-    uint4 kr[PPER], vr[PPER];
+  float m_w[G], l_w[G], acc[G][E];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_w[h] = -INFINITY;
+    l_w[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+  }
+
+  for (int c0 = c_lo; c0 < c_hi; c0 += TILE) {
+    const int nc = min(TILE, c_hi - c0);
+    uint4 kt[PPER], vt[PPER];
 #pragma unroll
     for (int pi = 0; pi < PPER; ++pi) {
-      const int i = tid + pi * 256;
-      const int c = i / (HD / E), d = (i % (HD / E)) * E;
-      if (i < PIECES && c < nc) {
-        const int64_t row = (int64_t)cells[c0 + c] * HD + d;
-        kr[pi] = *(const uint4*)(kc + row);
-        vr[pi] = *(const uint4*)(vc + row);
-      } else {
-        kr[pi] = vr[pi] = make_uint4(0, 0, 0, 0);
-      }
+      kt[pi] = kr[pi];
+      vt[pi] = vr[pi];
     }
-    __syncthreads();  // the previous tile's readers are done with the LDS
-    if (c0 == c_lo) {
+    if (c0 + TILE < c_hi) {  // block-uniform: request the next tile
 #pragma unroll
-      for (int o = 0; o < QPER; ++o) {
-        const int i = tid + o * 256;
-        if (i < G * HD) q_s[i / HD][i % HD] = qv[o];
+      for (int pi = 0; pi < PPER; ++pi) row[pi] = cells[min(c0 + TILE + r0 + pi * ROWS, c_hi - 1)];
+#pragma unroll
+      for (int pi = 0; pi < PPER; ++pi) {
+        const int64_t off = (int64_t)row[pi] * HD + dq;
+        kr[pi] = *(const uint4*)(kc + off);
+        vr[pi] = *(const uint4*)(vc + off);
       }
     }
+    // scores of this lane's rows, summed over the PR lanes of each row
+    float sc[PPER][G];
 #pragma unroll
     for (int pi = 0; pi < PPER; ++pi) {
-      const int i = tid + pi * 256;
-      if (i < PIECES) {
-        const int c = i / (HD / E), d = (i % (HD / E)) * E;
-        float kf[E], vf[E];
-        unpack16<KvT>(kr[pi], kf);
-        unpack16<KvT>(vr[pi], vf);
+      float kf[E];
+      unpack16<KvT>(kt[pi], kf);
+      const bool live = r0 + pi * ROWS < nc;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          k_s[c][d + e] = kf[e];
-          v_s[c][d + e] = vf[e];
+      for (int h = 0; h < G; ++h) {
+        float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+          x0 = fmaf(qr[h][e], kf[e], x0);
+          x1 = fmaf(qr[h][e + 1], kf[e + 1], x1);
         }
+        const float x = group_sum<PR>(x0 + x1);
+        sc[pi][h] = live ? x : -INFINITY;
       }
     }
-    __syncthreads();
-    // scores: wave w takes heads w, w+4, ...; lane = cell
-    const int lane = tid & 63, w = tid >> 6;
-    for (int h = w; h < G; h += 4) {
-      float sc = -INFINITY;
-      if (lane < nc) {
-        float s = 0.f;
-#pragma unroll 8
-        for (int d = 0; d < HD; ++d) s = fmaf(q_s[h][d], k_s[lane][d], s);
-        sc = s;
-      }
-      const float tmax = wave_max(sc);
-      const float m_old = m_s[h];
-      const float m_new = fmaxf(m_old, tmax);
-      const float p = lane < nc ? __expf(sc - m_new) : 0.f;
-      const float psum = wave_sum(p);
-      p_s[h][lane] = p;
-      if (lane == 0) {
-        const float al = __expf(m_old - m_new);
-        alpha_s[h] = al;
-        l_s[h] = l_s[h] * al + psum;
-        m_s[h] = m_new;
-      }
-    }
-    __syncthreads();
+    // online softmax per head over this lane's rows: the PR lanes of a row
+    // group hold identical scores, so each group keeps its own running max,
+    // sum and accumulator with no exchange between lanes
 #pragma unroll
-    for (int o = 0; o < OUT_PER; ++o) {
-      const int id = tid + o * 256;
-      if (id < G * HD) {
-        const int h = id / HD, d = id % HD;
-        float s = acc[o] * alpha_s[h];
-        for (int c = 0; c < nc; ++c) s = fmaf(p_s[h][c], v_s[c][d], s);
-        acc[o] = s;
+    for (int h = 0; h < G; ++h) {
+      float mx = sc[0][h];
+#pragma unroll
+      for (int pi = 1; pi < PPER; ++pi) mx = fmaxf(mx, sc[pi][h]);
+      const float m_new = fmaxf(m_w[h], mx);
+      // a group with no live row yet keeps m = -inf, l = 0, acc = 0
+      const float alpha = m_new == -INFINITY ? 1.f : __expf(m_w[h] - m_new);
+      float ps = 0.f;
+#pragma unroll
+      for (int pi = 0; pi < PPER; ++pi) {
+        const float p = sc[pi][h] == -INFINITY ? 0.f : __expf(sc[pi][h] - m_new);
+        sc[pi][h] = p;
+        ps += p;
       }
+      l_w[h] = fmaf(l_w[h], alpha, ps);
+      m_w[h] = m_new;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+    }
+    // probabilities times V (rows past the visible cells have p = 0)
+#pragma unroll
+    for (int pi = 0; pi < PPER; ++pi) {
+      float vf[E];
+      unpack16<KvT>(vt[pi], vf);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = fmaf(sc[pi][h], vf[e], acc[h][e]);
+    }
+  }
+
+  // combine the row groups of the wave (lanes with equal tid % PR): common
+  // max, rescale, then sum; afterwards the four waves through LDS
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float M = m_w[h];
+#pragma unroll
+    for (int o = PR; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+    const float w = m_w[h] == -INFINITY ? 0.f : __expf(m_w[h] - M);
+    float l = l_w[h] * w;
+#pragma unroll
+    for (int o = PR; o < 64; o <<= 1) l += __shfl_xor(l, o, kWave);
+    m_w[h] = M;
+    l_w[h] = l;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float v = acc[h][e] * w;
+#pragma unroll
+      for (int o = PR; o < 64; o <<= 1) v += __shfl_xor(v, o, kWave);
+      acc[h][e] = v;
+    }
+  }
+  if (lane < PR) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc_s[wv][h][dq + e] = acc[h][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m_s[wv][h] = m_w[h];
+      l_s[wv][h] = l_w[h];
     }
   }
   __syncthreads();
+  // the first row of the chunk is live and belongs to wave 0, so M is finite
   const int nch = (nvis + a.chunk - 1) / a.chunk;
-  if (nch == 1) {
-    // the whole visible range is in this block: normalise and write
-#pragma unroll
-    for (int o = 0; o < OUT_PER; ++o) {
-      const int id = tid + o * 256;
-      if (id < G * HD) {
-        const int h = id / HD, d = id % HD;
-        const float r = acc[o] / l_s[h];
-        const int64_t oi = ((int64_t)t * a.H + g * G + h) * HD + d;
-        if (a.out) a.out[oi] = r;
-        if (a.out_hi) split_bf16(r, a.out_hi[oi], a.out_lo[oi]);
-      }
-    }
-    return;
-  }
+  constexpr int OUT_PER = (G * HD + 255) / 256;
 #pragma unroll
   for (int o = 0; o < OUT_PER; ++o) {
     const int id = tid + o * 256;
     if (id < G * HD) {
       const int h = id / HD, d = id % HD;
-      const int64_t base = ((int64_t)t * a.H + g * G + h) * a.n_chunks + j;
-      a.part_acc[base * HD + d] = acc[o];
-      if (d == 0) {
-        a.part_ml[base * 2] = m_s[h];
-        a.part_ml[base * 2 + 1] = l_s[h];
+      const float M = fmaxf(fmaxf(m_s[0][h], m_s[1][h]), fmaxf(m_s[2][h], m_s[3][h]));
+      float L = 0.f, A = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float wt = __expf(m_s[w][h] - M);
+        L = fmaf(l_s[w][h], wt, L);
+        A = fmaf(acc_s[w][h][d], wt, A);
+      }
+      if (nch == 1) {
+        // the whole visible range is in this block: normalise and write
+        const float r = A / L;
+        const int64_t oi = ((int64_t)t * a.H + g * G + h) * HD + d;
+        if (a.out) a.out[oi] = r;
+        if (a.out_hi) split_bf16(r, a.out_hi[oi], a.out_lo[oi]);
+      } else {
+        const int64_t base = ((int64_t)t * a.H + g * G + h) * a.n_chunks + j;
+        a.part_acc[base * HD + d] = A;
+        if (d == 0) {
+          a.part_ml[base * 2] = M;
+          a.part_ml[base * 2 + 1] = L;
+        }
       }
     }
   }
 }
 
+// One block of 256 threads per (query head, token).  Wave 0 turns the
+// per-split maxima and sums into weights exp(m_j - M) and the total L; then
+// 256/HD thread groups each sum every (256/HD)-th split for all HD outputs,
+// 16 independent loads at a time, and the groups are added through LDS.
+constexpr int kMergeBatch = 16;
 template <int HD>
-__global__ void __launch_bounds__(HD) attn_merge_kernel(AttnArgs a) {
-  const int h = blockIdx.x, t = blockIdx.y, d = threadIdx.x;
+__global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a) {
+  constexpr int NP = 256 / HD;
+  __shared__ float w_s[kMergeMaxSplits];
+  __shared__ float part_s[NP][HD];
+  __shared__ float inv_l;
+  const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
   const int nch = (a.n_vis[t] + a.chunk - 1) / a.chunk;
   if (nch == 1 && !a.merge_single) return;  // the split kernel wrote this token already
   const int64_t base = ((int64_t)t * a.H + h) * a.n_chunks;
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int j = 0; j < nch; ++j) M = fmaxf(M, a.part_ml[(base + j) * 2]);
-  float L = 0.f, o = 0.f;
-#pragma unroll 8
-  for (int j = 0; j < nch; ++j) {
-    const float2 ml = *(const float2*)&a.part_ml[(base + j) * 2];
-    const float w = __expf(ml.x - M);
-    L = fmaf(ml.y, w, L);
-    o = fmaf(a.part_acc[(base + j) * HD + d], w, o);
+  if (tid < 64) {
+    constexpr int R = kMergeMaxSplits / 64;
+    float2 ml[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      ml[r] = *(const float2*)&a.part_ml[(base + min(tid + r * 64, nch - 1)) * 2];
+    float M = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < R; ++r) M = fmaxf(M, ml[r].x);
+    M = wave_max(M);
+    float L = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int jj = tid + r * 64;
+      const float w = jj < nch ? __expf(ml[r].x - M) : 0.f;
+      if (jj < nch) w_s[jj] = w;
+      L = fmaf(ml[r].y, w, L);
+    }
+    L = wave_sum(L);
+    if (tid == 0) inv_l = 1.f / L;
   }
-  const float r = o / L;
-  const int64_t oi = ((int64_t)t * a.H + h) * HD + d;
+  __syncthreads();
+  const int d = tid % HD, part = tid / HD;
+  const float* pa = a.part_acc + base * HD + d;
+  float o = 0.f;
+  for (int j0 = part; j0 < nch; j0 += NP * kMergeBatch) {
+    float v[kMergeBatch];
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b) v[b] = pa[(int64_t)min(j0 + b * NP, nch - 1) * HD];
+#pragma unroll
+    for (int b = 0; b < kMergeBatch; ++b) {
+      const int jj = j0 + b * NP;
+      o = fmaf(v[b], jj < nch ? w_s[jj] : 0.f, o);
+    }
+  }
+  part_s[part][d] = o;
+  __syncthreads();
+  if (tid >= HD) return;
+  float r = 0.f;
+#pragma unroll
+  for (int q = 0; q < NP; ++q) r += part_s[q][tid];
+  r *= inv_l;
+  const int64_t oi = ((int64_t)t * a.H + h) * HD + tid;
   if (a.out) a.out[oi] = r;
   if (a.out_hi) split_bf16(r, a.out_hi[oi], a.out_lo[oi]);
 }
@@ -737,12 +903,13 @@ static hipError_t attn_launch_hd(const AttnArgs& a, hipStream_t s) {
 
 hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
+  if (a.n_chunks > kMergeMaxSplits) return hipErrorInvalidValue;
   const dim3 grid(a.H, a.T);
   switch (a.hd) {
-    case 16: attn_merge_kernel<16><<<grid, 16, 0, s>>>(a); break;
-    case 32: attn_merge_kernel<32><<<grid, 32, 0, s>>>(a); break;
-    case 64: attn_merge_kernel<64><<<grid, 64, 0, s>>>(a); break;
-    case 128: attn_merge_kernel<128><<<grid, 128, 0, s>>>(a); break;
+    case 16: attn_merge_kernel<16><<<grid, 256, 0, s>>>(a); break;
+    case 32: attn_merge_kernel<32><<<grid, 256, 0, s>>>(a); break;
+    case 64: attn_merge_kernel<64><<<grid, 256, 0, s>>>(a); break;
+    case 128: attn_merge_kernel<128><<<grid, 256, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

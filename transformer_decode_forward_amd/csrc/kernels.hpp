@@ -88,6 +88,9 @@ hipError_t launch_argmax(const float* logits, int R, int V, int32_t* tok, hipStr
 // Attention of T tokens over their visible cells (split over cell chunks,
 // then merged).  q [T][H][hd] float32; caches [Hkv][n_ctx][hd]; cell lists
 // [n_seq_max][n_ctx]; list_off[t] = seq * n_ctx; n_vis[t] = visible cells.
+// most splits of one token's cell range that the attention merge combines
+constexpr int kMergeMaxSplits = 256;
+
 struct AttnArgs {
   const float* q = nullptr;
   const void* k_cache = nullptr;

@@ -58,6 +58,7 @@ constexpr int kGemvMaxT = 8;        // linear layers of up to this many rows str
 constexpr int kDecodeMaxT = 32;     // ubatches up to this size use the split-K decode attention
 constexpr int kChunkCapDecode = 256; // attention splits per token (decode)
 constexpr int kChunkCapPrefill = 32; // attention splits per token (larger ubatches)
+static_assert(kChunkCapDecode <= kMergeMaxSplits && kChunkCapPrefill <= kMergeMaxSplits, "merge width");
 
 constexpr int kQTile = 32;           // tokens per prefill attention query tile
 
