@@ -95,13 +95,25 @@ __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2)
   }
 }
 
+// (value, index) max over the wave (all 64 lanes active), same pattern as
+// wave_max; every lane receives the winner
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float v2 = dpp_read<CTRL>(v, -INFINITY);
+  const int i2 = __builtin_amdgcn_update_dpp(0x7FFFFFFF, i, CTRL, 0xF, 0xF, false);
+  argmax_merge(v, i, v2, i2);
+}
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_step<0xB1>(v, i);
+  argmax_step<0x4E>(v, i);
+  argmax_step<0x141>(v, i);
+  argmax_step<0x140>(v, i);
+  float bv = lane_read(v, 0);
+  int bi = __builtin_amdgcn_readlane(i, 0);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    float v2 = __shfl_xor(v, m, kWave);
-    int i2 = __shfl_xor(i, m, kWave);
-    argmax_merge(v, i, v2, i2);
-  }
+  for (int r = 16; r < 64; r += 16) argmax_merge(bv, bi, lane_read(v, r), __builtin_amdgcn_readlane(i, r));
+  v = bv;
+  i = bi;
 }
 
 // x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi): about 16 significant bits

@@ -184,40 +184,98 @@ hipError_t launch_gather_rows(const float* src, const int32_t* rows, int R, int 
   return hipGetLastError();
 }
 
-__global__ void __launch_bounds__(1024) argmax_kernel(const float* __restrict__ logits, int V,
-                                                      int32_t* __restrict__ tok) {
-  __shared__ float sv[16];
-  __shared__ int si[16];
-  const float* row = logits + (int64_t)blockIdx.x * V;
+// Greedy token: two passes.  Pass 1, block (split j, row r), reduces the
+// columns [j*L, j*L + L) of a row to (max, lowest index of the max); pass 2,
+// one block per row, reduces the splits.  L = 2048 * m with m the smallest
+// multiple that keeps the splits within kArgmaxMaxSplits.  Every thread
+// issues its loads up front; masked columns add -inf (an add, not a select,
+// so the loads stay out of branches).
+constexpr int kArgmaxCols = 2048;  // columns per split and multiple m (256 threads x 2 float4)
+
+__global__ void __launch_bounds__(256) argmax_split_kernel(const float* __restrict__ logits, int V, int m,
+                                                           float* __restrict__ pv, int32_t* __restrict__ pi,
+                                                           int n_split) {
+  const int j = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const float* row = logits + (int64_t)r * V;
+  const int lo = j * kArgmaxCols * m, hi = min(V, lo + kArgmaxCols * m);
   float best = -INFINITY;
   int bi = 0x7FFFFFFF;
-  const int V4 = (V & 3) == 0 ? V : 0;
-#pragma unroll 8
-  for (int n = threadIdx.x * 4; n < V4; n += 4096) {
-    const float4 v = *(const float4*)(row + n);
-    argmax_merge(best, bi, v.x, n);
-    argmax_merge(best, bi, v.y, n + 1);
-    argmax_merge(best, bi, v.z, n + 2);
-    argmax_merge(best, bi, v.w, n + 3);
+  if ((V & 3) == 0) {
+    for (int c = 0; c < m; ++c) {
+      const int n0 = lo + c * kArgmaxCols + tid * 4, n1 = n0 + 1024;
+      const float4 a = *(const float4*)(row + min(n0, V - 4));
+      const float4 b = *(const float4*)(row + min(n1, V - 4));
+      const float ma = n0 < hi ? 0.f : -INFINITY, mb = n1 < hi ? 0.f : -INFINITY;
+      argmax_merge(best, bi, a.x + ma, n0);
+      argmax_merge(best, bi, a.y + ma, n0 + 1);
+      argmax_merge(best, bi, a.z + ma, n0 + 2);
+      argmax_merge(best, bi, a.w + ma, n0 + 3);
+      argmax_merge(best, bi, b.x + mb, n1);
+      argmax_merge(best, bi, b.y + mb, n1 + 1);
+      argmax_merge(best, bi, b.z + mb, n1 + 2);
+      argmax_merge(best, bi, b.w + mb, n1 + 3);
+    }
+  } else {
+    for (int n = lo + tid; n < hi; n += 256) argmax_merge(best, bi, row[n], n);
   }
-  for (int n = V4 + threadIdx.x; n < V; n += 1024) argmax_merge(best, bi, row[n], n);
+  // a masked column can only win with best = -inf everywhere; keep its index valid
+  if (best == -INFINITY) bi = 0x7FFFFFFF;
+  __shared__ float sv[4];
+  __shared__ int si[4];
   wave_argmax(best, bi);
-  if ((threadIdx.x & 63) == 0) {
-    sv[threadIdx.x >> 6] = best;
-    si[threadIdx.x >> 6] = bi;
+  if ((tid & 63) == 0) {
+    sv[tid >> 6] = best;
+    si[tid >> 6] = bi;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    best = sv[0];
-    bi = si[0];
-    for (int w = 1; w < 16; ++w) argmax_merge(best, bi, sv[w], si[w]);
-    tok[blockIdx.x] = bi;
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w) argmax_merge(best, bi, sv[w], si[w]);
+    pv[(int64_t)r * n_split + j] = best;
+    pi[(int64_t)r * n_split + j] = bi;
   }
 }
 
-hipError_t launch_argmax(const float* logits, int R, int V, int32_t* tok, hipStream_t s) {
+__global__ void __launch_bounds__(256) argmax_final_kernel(const float* __restrict__ pv,
+                                                           const int32_t* __restrict__ pi, int n_split,
+                                                           int32_t* __restrict__ tok) {
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int k = min(tid, n_split - 1);
+  const float v = pv[(int64_t)r * n_split + k];
+  const int i = pi[(int64_t)r * n_split + k];
+  float best = v + (tid < n_split ? 0.f : -INFINITY);
+  int bi = tid < n_split ? i : 0x7FFFFFFF;
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  wave_argmax(best, bi);
+  if ((tid & 63) == 0) {
+    sv[tid >> 6] = best;
+    si[tid >> 6] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w) argmax_merge(best, bi, sv[w], si[w]);
+    // every logit -inf or NaN: fall back to token 0
+    tok[r] = bi == 0x7FFFFFFF ? 0 : bi;
+  }
+}
+
+int argmax_splits(int V) {
+  int m = 1;
+  while ((V + kArgmaxCols * m - 1) / (kArgmaxCols * m) > kArgmaxMaxSplits) ++m;
+  return (V + kArgmaxCols * m - 1) / (kArgmaxCols * m);
+}
+
+hipError_t launch_argmax(const float* logits, int R, int V, int32_t* tok, float* part_v, int32_t* part_i,
+                         hipStream_t s) {
   if (R <= 0) return hipSuccess;
-  argmax_kernel<<<R, 1024, 0, s>>>(logits, V, tok);
+  if (V <= 0) return hipErrorInvalidValue;
+  int m = 1;
+  while ((V + kArgmaxCols * m - 1) / (kArgmaxCols * m) > kArgmaxMaxSplits) ++m;
+  const int n_split = (V + kArgmaxCols * m - 1) / (kArgmaxCols * m);
+  argmax_split_kernel<<<dim3(n_split, R), 256, 0, s>>>(logits, V, m, part_v, part_i, n_split);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  argmax_final_kernel<<<R, 256, 0, s>>>(part_v, part_i, n_split, tok);
   return hipGetLastError();
 }
 

@@ -82,8 +82,13 @@ hipError_t launch_scatter(int32_t* dst, const int64_t* pairs, int n, hipStream_t
 // with g set also u[r] = g * src[rows[r]] and ssp[r * stride] = its sum of squares
 hipError_t launch_gather_rows(const float* src, const int32_t* rows, int R, int d, float* dst,
                               const float* g, float* u, float* ssp, int stride, hipStream_t s);
-// tok[r] = argmax_n logits[r][n] (lowest index on ties)
-hipError_t launch_argmax(const float* logits, int R, int V, int32_t* tok, hipStream_t s);
+// tok[r] = argmax_n logits[r][n] (lowest index on ties), in two passes over
+// argmax_splits(V) column splits; part_v / part_i hold R * argmax_splits(V)
+// partial results
+constexpr int kArgmaxMaxSplits = 256;
+int argmax_splits(int V);
+hipError_t launch_argmax(const float* logits, int R, int V, int32_t* tok, float* part_v, int32_t* part_i,
+                         hipStream_t s);
 
 // Attention of T tokens over their visible cells (split over cell chunks,
 // then merged).  q [T][H][hd] float32; caches [Hkv][n_ctx][hd]; cell lists

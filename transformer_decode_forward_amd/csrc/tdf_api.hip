@@ -112,6 +112,8 @@ struct tdf_context {
   char* ints_host = nullptr;        // pinned staging
   float* logits = nullptr;          // [cap][V]
   int32_t* d_tok = nullptr;         // [cap]
+  float* amax_v = nullptr;          // [cap][argmax_splits(V)] partial maxima
+  int32_t* amax_i = nullptr;        // [cap][argmax_splits(V)] their indices
   int32_t* h_tok = nullptr;         // pinned [cap]
   int logits_cap = 0;
   std::vector<void*> owned;
@@ -218,14 +220,19 @@ static void ctx_release(tdf_context* c) {
 static int ensure_logits(tdf_context* c, int rows) {
   if (rows <= c->logits_cap) return TDF_OK;
   const int V = c->m->hp.n_vocab;
-  void *lg = nullptr, *tk = nullptr;
+  void *lg = nullptr, *tk = nullptr, *av = nullptr, *ai = nullptr;
+  const size_t n_part = (size_t)rows * argmax_splits(V);
   hipError_t e = dev_alloc(&lg, (size_t)rows * V * sizeof(float));
   if (e == hipSuccess) e = dev_alloc(&tk, (size_t)rows * sizeof(int32_t));
+  if (e == hipSuccess) e = dev_alloc(&av, n_part * sizeof(float));
+  if (e == hipSuccess) e = dev_alloc(&ai, n_part * sizeof(int32_t));
   void* htk = nullptr;
   if (e == hipSuccess) e = hipHostMalloc(&htk, (size_t)rows * sizeof(int32_t), hipHostMallocDefault);
   if (e != hipSuccess) {
     if (lg) (void)hipFree(lg);
     if (tk) (void)hipFree(tk);
+    if (av) (void)hipFree(av);
+    if (ai) (void)hipFree(ai);
     set_err(std::string("logits allocation failed: ") + hipGetErrorString(e));
     return TDF_E_ALLOC;
   }
@@ -240,12 +247,18 @@ static int ensure_logits(tdf_context* c, int rows) {
   c->graphs.clear();
   drop(c->logits);
   drop(c->d_tok);
+  drop(c->amax_v);
+  drop(c->amax_i);
   if (c->h_tok) (void)hipHostFree(c->h_tok);
   c->logits = (float*)lg;
   c->d_tok = (int32_t*)tk;
+  c->amax_v = (float*)av;
+  c->amax_i = (int32_t*)ai;
   c->h_tok = (int32_t*)htk;
   c->owned.push_back(lg);
   c->owned.push_back(tk);
+  c->owned.push_back(av);
+  c->owned.push_back(ai);
   c->logits_cap = rows;
   return TDF_OK;
 }
@@ -793,7 +806,7 @@ extern "C" int32_t tdf_decode(tdf_context* c, const tdf_batch* b) {
   if (c->dry_run) return TDF_OK;
   if (n_out > 0) {
     const int ps = prof_begin(c, TDF_OP_ARGMAX, false);
-    TDF_HIP(launch_argmax(c->logits, n_out, c->m->hp.n_vocab, c->d_tok, c->stream));
+    TDF_HIP(launch_argmax(c->logits, n_out, c->m->hp.n_vocab, c->d_tok, c->amax_v, c->amax_i, c->stream));
     prof_end(c, ps);
     TDF_HIP(hipMemcpyAsync(c->h_tok, c->d_tok, (size_t)n_out * 4, hipMemcpyDeviceToHost, c->stream));
   }
