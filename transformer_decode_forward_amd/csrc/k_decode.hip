@@ -94,16 +94,45 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
   __shared__ float red[4];
   const int t = blockIdx.x;
   const float* xr = x + (int64_t)t * d;
-  float ss = 0.f;
-  if ((d & 3) == 0) {
-#pragma unroll 4
-    for (int k = threadIdx.x * 4; k < d; k += 1024) {
-      const float4 v = *(const float4*)(xr + k);
-      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  const int64_t ro = (int64_t)t * d;
+  if ((d & 3) == 0 && d <= 8 * 1024) {
+    // rows of up to 8192: the row stays in registers between the two passes;
+    // loads are clamped and masked by a multiply (no loads under branches)
+    constexpr int P = 8;  // float4 per thread
+    float4 xv[P];
+    float ss = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int k = threadIdx.x * 4 + p * 1024;
+      const float4 v = *(const float4*)(xr + min(k, d - 4));
+      const float on = k < d ? 1.f : 0.f;
+      xv[p] = make_float4(v.x * on, v.y * on, v.z * on, v.w * on);
+      ss += xv[p].x * xv[p].x + xv[p].y * xv[p].y + xv[p].z * xv[p].z + xv[p].w * xv[p].w;
     }
-  } else {
-    for (int k = threadIdx.x; k < d; k += 256) ss += xr[k] * xr[k];
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    ss = (red[0] + red[1]) + (red[2] + red[3]);
+    const float r = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int k = threadIdx.x * 4 + p * 1024;
+      if (k >= d) break;
+      const float4 gv = *(const float4*)(g + k);
+      const float v[4] = {xv[p].x * r * gv.x, xv[p].y * r * gv.y, xv[p].z * r * gv.z, xv[p].w * r * gv.w};
+      if (out_f32) *(float4*)(out_f32 + ro + k) = make_float4(v[0], v[1], v[2], v[3]);
+      if (out_hi) {
+        uint16_t h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_bf16(v[e], h[e], l[e]);
+        *(uint2*)(out_hi + ro + k) = make_uint2(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16);
+        *(uint2*)(out_lo + ro + k) = make_uint2(l[0] | (uint32_t)l[1] << 16, l[2] | (uint32_t)l[3] << 16);
+      }
+    }
+    return;
   }
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < d; k += 256) ss += xr[k] * xr[k];
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
@@ -111,8 +140,8 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
   const float r = 1.0f / sqrtf(ss / (float)d + eps);
   for (int k = threadIdx.x; k < d; k += 256) {
     float v = xr[k] * r * g[k];
-    if (out_f32) out_f32[(int64_t)t * d + k] = v;
-    if (out_hi) split_bf16(v, out_hi[(int64_t)t * d + k], out_lo[(int64_t)t * d + k]);
+    if (out_f32) out_f32[ro + k] = v;
+    if (out_hi) split_bf16(v, out_hi[ro + k], out_lo[ro + k]);
   }
 }
 
@@ -879,14 +908,17 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
   }
 }
 
-// One block of 256 threads per (query head, token).  Wave 0 turns the
-// per-split maxima and sums into weights exp(m_j - M) and the total L; then
-// 256/HD thread groups each sum every (256/HD)-th split for all HD outputs,
-// 16 independent loads at a time, and the groups are added through LDS.
+// One block of NTH threads (NTH >= 64, a multiple of HD) per (query head,
+// token).  Wave 0 turns the per-split maxima and sums into weights
+// exp(m_j - M) and the total L; then NTH/HD thread groups each sum every
+// (NTH/HD)-th split for all HD outputs, 16 independent loads at a time, and
+// the groups are added through LDS.  Decode ubatches (many splits, few
+// tokens) use 256 threads; larger ubatches (few splits, many tokens) the
+// smallest block.
 constexpr int kMergeBatch = 16;
-template <int HD>
-__global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a) {
-  constexpr int NP = 256 / HD;
+template <int HD, int NTH>
+__global__ void __launch_bounds__(NTH) attn_merge_kernel(AttnArgs a) {
+  constexpr int NP = NTH / HD;
   __shared__ float w_s[kMergeMaxSplits];
   __shared__ float part_s[NP][HD];
   __shared__ float inv_l;
@@ -963,11 +995,24 @@ hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   if (a.n_chunks > kMergeMaxSplits) return hipErrorInvalidValue;
   const dim3 grid(a.H, a.T);
+  const bool wide = a.n_chunks > 8;
   switch (a.hd) {
-    case 16: attn_merge_kernel<16><<<grid, 256, 0, s>>>(a); break;
-    case 32: attn_merge_kernel<32><<<grid, 256, 0, s>>>(a); break;
-    case 64: attn_merge_kernel<64><<<grid, 256, 0, s>>>(a); break;
-    case 128: attn_merge_kernel<128><<<grid, 256, 0, s>>>(a); break;
+    case 16:
+      if (wide) attn_merge_kernel<16, 256><<<grid, 256, 0, s>>>(a);
+      else attn_merge_kernel<16, 64><<<grid, 64, 0, s>>>(a);
+      break;
+    case 32:
+      if (wide) attn_merge_kernel<32, 256><<<grid, 256, 0, s>>>(a);
+      else attn_merge_kernel<32, 64><<<grid, 64, 0, s>>>(a);
+      break;
+    case 64:
+      if (wide) attn_merge_kernel<64, 256><<<grid, 256, 0, s>>>(a);
+      else attn_merge_kernel<64, 64><<<grid, 64, 0, s>>>(a);
+      break;
+    case 128:
+      if (wide) attn_merge_kernel<128, 256><<<grid, 256, 0, s>>>(a);
+      else attn_merge_kernel<128, 128><<<grid, 128, 0, s>>>(a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -244,26 +244,36 @@ static hipError_t gemm_launch_tile(const LinearArgs& a, int ksplit, hipStream_t 
   return hipGetLastError();
 }
 
-// Tile choice: the largest of 128x256, 128x128, 64x128 that gives at least
-// 384 blocks (1.5 per CU), counting K splits for the residual epilogue.
+// Tile choice.  Plain epilogues: the largest of 128x256, 128x128, 64x128
+// that gives at least 384 blocks (1.5 per CU).  Residual epilogue: the
+// smallest K split (1, 2, 4, 8) for which some tile reaches 512 blocks, with
+// the largest such tile; the atomic adds of deeper splits cost more than the
+// smaller tiles' extra operand traffic (at 512 x 4096 x 4096, 64x128 tiles
+// split in 2 run in about half the time of 128x256 tiles split in 8).
 template <int EPI, typename KvT>
 static hipError_t gemm_launch_t(const LinearArgs& a, hipStream_t s) {
   const int M = a.T;
   const int Ntot = EPI == EPI_SWIGLU ? 2 * a.n0 : a.n0 + a.n1 + a.n2;
   const int nkt = a.K / GBK;
-  auto splits = [&](int blocks) {
-    int ksplit = 1;
-    if (EPI == EPI_RESIDUAL)
-      while (blocks * ksplit < 512 && ksplit < 8 && nkt % (ksplit * 2) == 0 && nkt / (ksplit * 2) >= 4)
-        ksplit *= 2;
-    return ksplit;
-  };
   const int b24 = ((M + 127) / 128) * ((Ntot + 255) / 256);
   const int b22 = ((M + 127) / 128) * ((Ntot + 127) / 128);
-  if (b24 * splits(b24) >= 384) return gemm_launch_tile<EPI, KvT, 2, 4>(a, splits(b24), s);
-  if (b22 * splits(b22) >= 384) return gemm_launch_tile<EPI, KvT, 2, 2>(a, splits(b22), s);
   const int b12 = ((M + 63) / 64) * ((Ntot + 127) / 128);
-  return gemm_launch_tile<EPI, KvT, 1, 2>(a, splits(b12), s);
+  if (EPI == EPI_RESIDUAL) {
+    for (int ks = 1; ks <= 8; ks *= 2) {
+      // each split keeps at least 4 K tiles
+      if (ks > 1 && (nkt % ks != 0 || nkt / ks < 4)) break;
+      if (b24 * ks >= 512) return gemm_launch_tile<EPI, KvT, 2, 4>(a, ks, s);
+      if (b22 * ks >= 512) return gemm_launch_tile<EPI, KvT, 2, 2>(a, ks, s);
+      if (b12 * ks >= 512) return gemm_launch_tile<EPI, KvT, 1, 2>(a, ks, s);
+    }
+    // small problems: the deepest allowed split of the smallest tile
+    int ks = 1;
+    while (ks < 8 && nkt % (ks * 2) == 0 && nkt / (ks * 2) >= 4 && b12 * ks < 512) ks *= 2;
+    return gemm_launch_tile<EPI, KvT, 1, 2>(a, ks, s);
+  }
+  if (b24 >= 384) return gemm_launch_tile<EPI, KvT, 2, 4>(a, 1, s);
+  if (b22 >= 384) return gemm_launch_tile<EPI, KvT, 2, 2>(a, 1, s);
+  return gemm_launch_tile<EPI, KvT, 1, 2>(a, 1, s);
 }
 
 hipError_t launch_linear_gemm(const LinearArgs& a, hipStream_t s) {
