@@ -7,13 +7,19 @@ one token each, every step feeding back the GPU's own argmax.
 
 A timed "step" is one decode call: the whole forward pass for one token
 (embedding, 32 layers, output norm, LM head, device argmax, 4-byte token
-readback).  ``value`` is decode tokens/s; the prefill rate of the same model
-is reported beside it.  ``roofline`` covers the dominant decode kernel (the
-fused gate/up GEMV) and ``roofline_prefill`` the dominant prefill kernel (the
-gate/up MFMA GEMM); both take their average launch duration from HIP events
-recorded on the library's stream during a profiled repeat of the workload.
+readback), replayed as a HIP graph.  ``value`` is decode tokens/s; the
+prefill rate of the same model is reported beside it.  ``roofline`` covers
+the dominant decode kernel (the fused gate/up GEMV) and ``roofline_prefill``
+the dominant prefill kernel (the gate/up MFMA GEMM): their average launch
+durations come from tdf_time_op, back-to-back launches of that kernel on the
+library's stream between two HIP events, cycling over the 32 layers' weights.
+``traffic`` is read from the committed rocprofv3 counter summary of that
+kernel when the kernel source still matches it (else null).
+``kernels`` is a per-operation breakdown from an eager repeat with a HIP
+event pair around every launch (it includes the events' own overhead).
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-peaks]
+    python bench.py --calibrate-copy     # plain 1 GiB device copy, for counter scaling
 """
 from __future__ import annotations
 
@@ -30,6 +36,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16
+COPY_BYTES = 1 << 30         # calibration copy: 1 GiB read + 1 GiB written
+TRAFFIC_FILES = {"decode": "profiles/gemv_gate_up_decode_llama8b_traffic.json",
+                 "prefill": "profiles/gemm_gate_up_prefill512_llama8b_traffic.json"}
+KERNEL_SOURCES = {"decode": "transformer_decode_forward_amd/csrc/k_decode.hip",
+                  "prefill": "transformer_decode_forward_amd/csrc/k_gemm.hip"}
 
 
 def log(msg):
@@ -78,6 +89,69 @@ def prefill_flops(cfg, n_tok, n_ubatch, n_out_last=1):
     return fl
 
 
+def source_hash(rel):
+    import hashlib
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic(kind):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, TRAFFIC_FILES[kind])
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kind]):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of COPY_BYTES (4 launches), so that the
+    FETCH_SIZE / WRITE_SIZE counters can be scaled by a transfer of known size."""
+    import torch
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copied {COPY_BYTES} bytes 4 times")
+
+
+def measured_peaks():
+    """Practical peaks on this GPU: a device copy (bytes read + written) and a
+    large bf16 GEMM from the vendor library (torch.matmul), for context."""
+    import torch
+    a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        b.copy_(a)
+    s.record()
+    for _ in range(10):
+        b.copy_(a)
+    e.record()
+    e.synchronize()
+    copy_gbs = 10 * 2 * COPY_BYTES / (s.elapsed_time(e) * 1e-3) / 1e9
+    del a, b
+    n = 8192
+    x = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    y = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(2):
+        torch.matmul(x, y)
+    s.record()
+    for _ in range(10):
+        torch.matmul(x, y)
+    e.record()
+    e.synchronize()
+    gemm_tfs = 10 * 2 * n ** 3 / (s.elapsed_time(e) * 1e-3) / 1e12
+    return {"copy_GBs": round(copy_gbs, 1), "bf16_gemm_8192_TFLOPs": round(gemm_tfs, 1),
+            "note": "torch device copy (read + write bytes) and torch.matmul bf16 8192^3 (hipBLASLt)"}
+
+
 def cpu_baseline(cfg, host_weights, ctx_len):
     """The oracle, as it stands, on a bounded sample: one decode step of the
     same model at context ctx_len (the cache restored from synthetic
@@ -115,7 +189,12 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config", default="llama8b")
+    ap.add_argument("--no-peaks", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -156,6 +235,20 @@ def main():
     log("timed run")
     ctx = tdf.Context(model, n_ctx=n_ctx, n_ubatch=U, kv_dtype=cfg["kv_dtype"])
     t_pre, t_dec = run(ctx, args.steps, args.warmup)
+    # decode with the full fp32 logits row copied to the host every step
+    n_d2h = 32
+    tok = ctx.argmax_ith(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_d2h):
+        assert ctx.decode([tok]) == 0, tdf.tdf_last_error()
+        row = ctx.logits_ith(0)
+        tok = int(np.argmax(row))
+    t_d2h = time.perf_counter() - t0
+    # the dominant kernels, back to back on the library's stream (HIP events)
+    d, F = cfg["n_embd"], cfg["n_ff"]
+    gu_us = ctx.time_op("gate_up", 1, 64)
+    gg_us = ctx.time_op("gate_up", U, 16)
     ctx.close()
     ms_step = 1000.0 * t_dec / args.steps
     decode_tps = args.steps / t_dec
@@ -170,16 +263,12 @@ def main():
     run(pctx, args.steps, args.warmup)
     prof = pctx.profile()
     pctx.close()
-    d, F = cfg["n_embd"], cfg["n_ff"]
-    n_gu, ms_gu = prof[("gate_up", "decode")]
     # per decode launch: the gate and up matrices once, the normed input, the output
     gu_bytes = 2 * F * d * 2 + d * 4 + F * 4
-    gu_ms = ms_gu / n_gu
-    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
-    n_gg, ms_gg = prof[("gate_up", "mfma")]
+    gu_gbs = gu_bytes / (gu_us * 1e-6) / 1e9
     gg_flops = 2.0 * U * (2 * F) * d
-    gg_ms = ms_gg / n_gg
-    gg_tfs = gg_flops / (gg_ms * 1e-3) / 1e12
+    gg_tfs = gg_flops / (gg_us * 1e-6) / 1e12
+    peaks = None if args.no_peaks else measured_peaks()
     breakdown = {f"{k[0]}/{k[1]}": {"launches": v[0], "avg_us": round(1000.0 * v[1] / v[0], 2)}
                  for k, v in sorted(prof.items())}
 
@@ -205,6 +294,7 @@ def main():
                                f"(last-position logits), then greedy decode steps; KV bf16 {n_ctx} cells",
                    "d_model": d, "n_layer": cfg["n_layer"], "n_ff": F, "n_vocab": cfg["n_vocab"]},
         "decode": {"tok_s": round(decode_tps, 3), "mean_ctx": mean_ctx,
+                   "tok_s_with_logits_d2h": round(n_d2h / t_d2h, 3),
                    "algorithmic_bytes_per_step": int(step_bytes),
                    "achieved_GBs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                    "frac_hbm_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
@@ -214,12 +304,14 @@ def main():
                     "frac_mfma_peak": round(pre_flops / t_pre / 1e12 / MFMA_BF16_PEAK_TFS, 4)},
         "roofline": {"bound": "hbm", "kernel": "gate/up GEMV + SwiGLU (decode)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "avg_launch_us": round(1000 * gu_ms, 2), "bytes_per_launch": gu_bytes},
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic("decode"),
+                     "avg_launch_us": round(gu_us, 2), "bytes_per_launch": gu_bytes},
         "roofline_prefill": {"bound": "mfma", "kernel": "gate/up GEMM + SwiGLU (prefill ubatch 512)",
                              "achieved": round(gg_tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                             "frac": round(gg_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
-                             "avg_launch_us": round(1000 * gg_ms, 2), "flops_per_launch": gg_flops},
+                             "frac": round(gg_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic("prefill"),
+                             "avg_launch_us": round(gg_us, 2), "flops_per_launch": gg_flops,
+                             "executed_flops_per_launch": 2 * gg_flops},
+        "measured_peaks": peaks,
         "kernels": breakdown,
         "cpu_baseline": cpu,
     }

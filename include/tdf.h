@@ -194,6 +194,20 @@ int32_t tdf_kv_import(tdf_context *c, int32_t s, int32_t pos0, int32_t n,
 int32_t tdf_profile_read(const tdf_context *c, int32_t op, int32_t mfma, int64_t *launches, double *ms);
 int32_t tdf_profile_reset(tdf_context *c);
 
+/* Measurement hook: launch the linear layer of operation op (TDF_OP_GATE_UP,
+ * TDF_OP_DOWN or TDF_OP_LM_HEAD) for an ubatch of n_tokens rows (the decode
+ * GEMV up to 8 rows, the matrix-core GEMM above, as tdf_decode chooses)
+ * reps times back to back on the context's stream, cycling over the layers
+ * so that no launch finds its weights cached, and store the mean duration
+ * per launch in microseconds (HIP events on that stream) in *avg_us.  The
+ * inputs are whatever the context's scratch holds (run tdf_decode first);
+ * the outputs overwrite scratch, the residual rows and the logits, so the
+ * logits of the last tdf_decode are no longer valid afterwards.  The KV cache
+ * and the cell bookkeeping are untouched.  Returns TDF_OK, TDF_E_INVALID
+ * (bad op, n_tokens outside [1, n_ubatch], reps < 1, dry-run context) or
+ * TDF_E_DEVICE. */
+int32_t tdf_time_op(tdf_context *c, int32_t op, int32_t n_tokens, int32_t reps, double *avg_us);
+
 /* Launch replay (llama.cpp walkthrough, "Step 13": graph reuse for same-shape
  * ubatches): ubatches of up to 32 tokens run as a captured HIP graph, one per
  * shape, replayed on later calls.  Counts of captures and replays so far.

@@ -123,3 +123,13 @@ def test_kv_import_bookkeeping_matches_oracle():
     assert g.decode([9], seq_ids=[[0]]) == 0
     assert o.decode([9], seq_ids=[[0]]).positions == [14]
     assert_same_state(g, o, 2)
+
+
+def test_time_op_rejects_bookkeeping_contexts_and_bad_ops():
+    """The measurement hook launches nothing on a bookkeeping-only context and
+    checks its operation and row count before any launch."""
+    m = tdf.Model(HP, dry_run=True)
+    c = tdf.Context(m, n_ctx=32, dry_run=True)
+    for op, n, reps in (("gate_up", 1, 4), ("qkv", 1, 4), ("down", 0, 4), ("lm_head", 1, 0)):
+        with pytest.raises(RuntimeError, match=r"\(-1\)"):
+            c.time_op(op, n, reps)

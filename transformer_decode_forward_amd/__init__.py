@@ -85,6 +85,7 @@ def lib():
                                         ctypes.POINTER(ctypes.c_double)]),
             "tdf_profile_reset": (_i32, [_vp]),
             "tdf_graph_counts": (_i32, [_vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
+            "tdf_time_op": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_double)]),
             "tdf_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -297,6 +298,15 @@ class Context:
         cap, rep = ctypes.c_int64(), ctypes.c_int64()
         lib().tdf_graph_counts(self.handle, ctypes.byref(cap), ctypes.byref(rep))
         return cap.value, rep.value
+
+    def time_op(self, op: str, n_tokens: int, reps: int) -> float:
+        """Mean duration (us) of `reps` back-to-back launches of one linear layer
+        (op "gate_up", "down" or "lm_head") for n_tokens rows; tdf_time_op."""
+        us = ctypes.c_double()
+        rc = lib().tdf_time_op(self.handle, OPS.index(op), n_tokens, reps, ctypes.byref(us))
+        if rc != TDF_OK:
+            raise RuntimeError(f"tdf_time_op failed ({rc}): {tdf_last_error()}")
+        return us.value
 
     def profile_reset(self) -> int:
         return lib().tdf_profile_reset(self.handle)

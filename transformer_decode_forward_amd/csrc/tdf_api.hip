@@ -968,4 +968,76 @@ extern "C" int32_t tdf_graph_counts(const tdf_context* c, int64_t* captures, int
   return TDF_OK;
 }
 
+extern "C" int32_t tdf_time_op(tdf_context* c, int32_t op, int32_t n_tokens, int32_t reps, double* avg_us) {
+  if (!c || !avg_us || c->dry_run || reps < 1 || n_tokens < 1 || n_tokens > c->n_ubatch) {
+    set_err("tdf_time_op: invalid arguments");
+    return TDF_E_INVALID;
+  }
+  if (op != TDF_OP_GATE_UP && op != TDF_OP_DOWN && op != TDF_OP_LM_HEAD) {
+    set_err("tdf_time_op: op must be TDF_OP_GATE_UP, TDF_OP_DOWN or TDF_OP_LM_HEAD");
+    return TDF_E_INVALID;
+  }
+  const tdf_model* m = c->m;
+  const tdf_hparams& h = m->hp;
+  const int d = h.n_embd, F = h.n_ff, V = h.n_vocab, L = h.n_layer, T = n_tokens;
+  const bool wbf16 = h.weight_dtype == TDF_BF16;
+  if (op == TDF_OP_LM_HEAD && c->logits_cap < T) {
+    if (int rc = ensure_logits(c, T)) return rc;
+  }
+  if ((op != TDF_OP_LM_HEAD && L == 0)) {
+    set_err("tdf_time_op: model has no layers");
+    return TDF_E_INVALID;
+  }
+  const int K = op == TDF_OP_DOWN ? F : d;
+  const bool mfma = wbf16 && T > kGemvMaxT && K % 64 == 0;
+  auto args = [&](int l) {
+    LinearArgs a;
+    a.T = T; a.weight_bf16 = wbf16;
+    if (op == TDF_OP_GATE_UP) {
+      const tdf_layer_weights& W = m->layers[l];
+      a.w0 = W.w_gate; a.w1 = W.w_up; a.n0 = F; a.K = d;
+      a.act_f32 = c->u; a.act_hi = c->h_hi; a.act_lo = c->h_lo;
+      if (!mfma) {
+        a.norm_ssp = c->ssp; a.norm_nparts = gemv_residual_parts(d); a.norm_stride = c->ssp_stride;
+        a.norm_eps = h.rms_eps;
+      }
+      a.epi = EPI_SWIGLU; a.out = c->mb; a.out_hi = c->m_hi; a.out_lo = c->m_lo; a.ldo = F;
+    } else if (op == TDF_OP_DOWN) {
+      const tdf_layer_weights& W = m->layers[l];
+      a.w0 = W.w_down; a.n0 = d; a.K = F;
+      a.act_f32 = c->mb; a.act_hi = c->m_hi; a.act_lo = c->m_lo;
+      a.epi = EPI_RESIDUAL; a.out = c->x; a.ldo = d;
+    } else {
+      a.w0 = m->output; a.n0 = V; a.K = d;
+      a.act_f32 = c->u; a.act_hi = c->h_hi; a.act_lo = c->h_lo;
+      if (!mfma) {
+        a.norm_ssp = c->ssp; a.norm_nparts = gemv_residual_parts(d); a.norm_stride = c->ssp_stride;
+        a.norm_eps = h.rms_eps;
+      }
+      a.epi = EPI_STORE; a.out = c->logits; a.ldo = V;
+    }
+    return a;
+  };
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) e = hipEventRecord(e0, c->stream);
+  for (int i = 0; i < reps && e == hipSuccess; ++i) {
+    LinearArgs a = args(op == TDF_OP_LM_HEAD ? 0 : i % L);
+    e = mfma ? launch_linear_gemm(a, c->stream) : launch_linear_gemv(a, c->stream);
+  }
+  if (e == hipSuccess) e = hipEventRecord(e1, c->stream);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (e != hipSuccess) {
+    set_err(std::string("tdf_time_op: ") + hipGetErrorString(e));
+    return TDF_E_DEVICE;
+  }
+  *avg_us = 1000.0 * ms / reps;
+  return TDF_OK;
+}
+
 extern "C" const char* tdf_last_error(void) { return g_err.c_str(); }
