@@ -42,6 +42,13 @@ Readings where the pages are silent or inconsistent:
   first sequence id and whose position is <= the token's position; this
   includes itself and earlier tokens of its own ubatch.  Cached K is stored
   after RoPE.
+* Sliding-window attention (Ollama engine page, "KV Cache: memory for causal
+  attention": a windowed layer's mask is limited to the window, each layer
+  attending only to the most recent tokens): with ``n_swa = W > 0`` a
+  windowed layer (``swa_layers[l]`` nonzero, or every layer when
+  ``swa_layers`` is absent) lets a token at position p see only the cells
+  above with position > p - W, i.e. the W most recent positions including
+  its own.  Cells outside the window stay in the cache.
 * The cache holds K and V in its element type (the Ollama cache carries a
   DType; the llama.cpp walkthrough's KV-cache section names the cache type
   as a storage setting): with ``kv_dtype`` set, each stored value is the
@@ -58,7 +65,7 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 from .model import OracleModel, widen
-from .ops import attend, rms_norm, rope, swiglu_mlp
+from .ops import attend, rms_norm, rope, swiglu_mlp, window_visible
 
 OK, NO_SLOT, INVALID = 0, 1, -1
 MAX_SEQ = 64
@@ -263,11 +270,17 @@ class OracleContext:
         H, Hkv, hd = hp["n_head"], hp["n_head_kv"], hp["head_dim"]
         L, eps, theta = hp["n_layer"], hp["rms_eps"], hp["rope_theta"]
         T = len(toks)
-        # visible cells per token: same (first) sequence, position <= own
-        visible = []
+        # visible cells per token: same (first) sequence, position <= own;
+        # for windowed layers also position > own - W
+        W = int(hp.get("n_swa") or 0)
+        flags = hp.get("swa_layers")
+        windowed = [W > 0 and (flags is None or bool(flags[l])) for l in range(L)]
+        visible, visible_w = [], []
         for t in range(T):
             inseq = ((self.cell_seq >> np.uint64(seq0[t])) & np.uint64(1)).astype(bool)
-            visible.append(np.flatnonzero(inseq & (self.cell_pos >= 0) & (self.cell_pos <= pos[t])))
+            ok = inseq & (self.cell_pos >= 0) & (self.cell_pos <= pos[t])
+            visible.append(np.flatnonzero(ok))
+            visible_w.append(np.flatnonzero(ok & window_visible(self.cell_pos, pos[t], W)) if W > 0 else None)
         x = m.embed_rows(toks)
         for l in range(L):
             p = f"blk.{l}."
@@ -280,7 +293,8 @@ class OracleContext:
             kc, vc = self._layer_cache(l)
             kc[cells] = _round_storage(k, self.kv_dtype)
             vc[cells] = _round_storage(v, self.kv_dtype)
-            o = np.stack([attend(q[t], kc[visible[t]], vc[visible[t]]) for t in range(T)])
+            vis = visible_w if windowed[l] else visible
+            o = np.stack([attend(q[t], kc[vis[t]], vc[vis[t]]) for t in range(T)])
             x = x + o.reshape(T, H * hd) @ m.w(p + "attn_output.weight").T
             if l == L - 1:
                 if not sel:

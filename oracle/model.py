@@ -35,7 +35,8 @@ def widen(a: np.ndarray) -> np.ndarray:
 
 class OracleModel:
     """hparams: n_vocab, n_embd, n_layer, n_head, n_head_kv, head_dim, n_ff,
-    rms_eps, rope_theta, tied.
+    rms_eps, rope_theta, tied; optionally n_swa (attention window, 0 = none)
+    and swa_layers (per-layer flags, absent = every layer windowed).
 
     ``tensors`` is either a dict name -> stored array, or a callable
     ``provider(name) -> stored array`` (used to stream huge models).

@@ -20,6 +20,9 @@ Readings where the pages leave a step open:
 * Attention scale 1/sqrt(head_dim); query head j uses KV head
   ``j // (n_head / n_head_kv)`` (contiguous groups).
 * SwiGLU: ``silu(gate) * up`` with ``silu(z) = z / (1 + exp(-z))``.
+* Sliding window (Ollama engine page, "KV Cache: memory for causal
+  attention"): a windowed layer attends only to the ``window`` most recent
+  positions, the token's own included.
 """
 from __future__ import annotations
 
@@ -87,3 +90,10 @@ def attend(q: np.ndarray, k_vis: np.ndarray, v_vis: np.ndarray) -> np.ndarray:
     a = np.exp(s - np.max(s, axis=-1, keepdims=True))
     a /= np.sum(a, axis=-1, keepdims=True)
     return np.matmul(a, v_vis.transpose(1, 0, 2)).reshape(n_head, hd)  # [Hkv, group, hd]
+
+
+def window_visible(cell_pos: np.ndarray, pos: int, window: int) -> np.ndarray:
+    """Cells a token at position ``pos`` sees in a windowed layer, by cell
+    position: pos - window < p <= pos (the ``window`` most recent positions)."""
+    cell_pos = np.asarray(cell_pos)
+    return (cell_pos > pos - window) & (cell_pos <= pos)

@@ -153,7 +153,11 @@ CONFIGS = {
 def hparams(cfg: dict) -> dict:
     keys = ("n_vocab", "n_embd", "n_layer", "n_head", "n_head_kv", "head_dim", "n_ff",
             "rms_eps", "rope_theta", "tied", "weight_dtype")
-    return {k: cfg[k] for k in keys}
+    out = {k: cfg[k] for k in keys}
+    if cfg.get("n_swa"):
+        out["n_swa"] = int(cfg["n_swa"])
+        out["swa_layers"] = cfg.get("swa_layers")
+    return out
 
 
 def derive(cfg: dict, **overrides) -> dict:
