@@ -191,6 +191,8 @@ def main():
     ap.add_argument("--config", default="llama8b")
     ap.add_argument("--no-peaks", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--swa", type=int, default=0,
+                    help="sliding-window attention of this many positions on every layer (0: none)")
     args = ap.parse_args()
     if args.calibrate_copy:
         calibrate_copy()
@@ -205,6 +207,8 @@ def main():
     import transformer_decode_forward_amd as tdf
     assert torch.cuda.is_available(), "no GPU"
     cfg = dict(tdf_synth.CONFIGS[args.config])
+    if args.swa:
+        cfg["n_swa"] = args.swa
     P, U, n_ctx = cfg["prompt_len"], cfg["n_ubatch"], cfg["n_ctx"]
     assert P + args.warmup + args.steps < n_ctx, "steps exceed the KV capacity"
 
@@ -254,7 +258,7 @@ def main():
     decode_tps = args.steps / t_dec
     prefill_tps = P / t_pre
     mean_ctx = P + args.warmup + (args.steps + 1) / 2.0
-    step_bytes = decode_bytes(cfg, mean_ctx)
+    step_bytes = decode_bytes(cfg, min(mean_ctx, args.swa) if args.swa else mean_ctx)
     pre_flops = prefill_flops(cfg, P, U)
     log(f"prefill {prefill_tps:.0f} tok/s, decode {decode_tps:.1f} tok/s ({ms_step:.3f} ms/step)")
 
@@ -292,7 +296,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.config}: batch 1, {P}-token prompt in ubatches of {U} "
                                f"(last-position logits), then greedy decode steps; KV bf16 {n_ctx} cells",
-                   "d_model": d, "n_layer": cfg["n_layer"], "n_ff": F, "n_vocab": cfg["n_vocab"]},
+                   "d_model": d, "n_layer": cfg["n_layer"], "n_ff": F, "n_vocab": cfg["n_vocab"],
+                   "attention_window": args.swa or None},
         "decode": {"tok_s": round(decode_tps, 3), "mean_ctx": mean_ctx,
                    "tok_s_with_logits_d2h": round(n_d2h / t_d2h, 3),
                    "algorithmic_bytes_per_step": int(step_bytes),

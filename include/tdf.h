@@ -77,6 +77,15 @@ typedef struct {
   int32_t n_vocab, n_embd, n_layer, n_head, n_head_kv, head_dim, n_ff;
   float rms_eps, rope_theta;
   int32_t weight_dtype;
+  /* Sliding-window attention (Ollama engine page, "KV Cache: memory for
+   * causal attention": a windowed layer's mask keeps only the most recent
+   * tokens).  n_swa = W > 0: in a windowed layer a token at position p sees
+   * only its sequence's cells with position > p - W (the W most recent
+   * positions, its own included); 0 = no window.  swa_layers: HOST array of
+   * n_layer flags (nonzero = windowed), copied by tdf_model_create; NULL =
+   * every layer windowed.  Cells outside the window stay in the cache. */
+  int32_t n_swa;
+  const int8_t *swa_layers;
 } tdf_hparams;
 
 /* Device pointers of one layer (GGUF names blk.<i>.*): attn_norm, attn_q

@@ -133,3 +133,10 @@ def test_time_op_rejects_bookkeeping_contexts_and_bad_ops():
     for op, n, reps in (("gate_up", 1, 4), ("qkv", 1, 4), ("down", 0, 4), ("lm_head", 1, 0)):
         with pytest.raises(RuntimeError, match=r"\(-1\)"):
             c.time_op(op, n, reps)
+
+
+def test_window_hparams_accepted_and_checked():
+    tdf.Model(dict(HP, n_swa=8, swa_layers=[1] * HP["n_layer"]), dry_run=True)
+    tdf.Model(dict(HP, n_swa=8), dry_run=True)
+    with pytest.raises(Exception):
+        tdf.Model(dict(HP, n_swa=-1), dry_run=True)

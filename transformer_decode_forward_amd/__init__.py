@@ -33,7 +33,8 @@ _vp = ctypes.c_void_p
 class tdf_hparams(ctypes.Structure):
     _fields_ = [("n_vocab", _i32), ("n_embd", _i32), ("n_layer", _i32), ("n_head", _i32),
                 ("n_head_kv", _i32), ("head_dim", _i32), ("n_ff", _i32),
-                ("rms_eps", _f32), ("rope_theta", _f32), ("weight_dtype", _i32)]
+                ("rms_eps", _f32), ("rope_theta", _f32), ("weight_dtype", _i32),
+                ("n_swa", _i32), ("swa_layers", ctypes.POINTER(ctypes.c_int8))]
 
 
 class tdf_layer_weights(ctypes.Structure):
@@ -132,9 +133,14 @@ def tdf_last_error() -> str:
 # ---- convenience objects ---------------------------------------------------
 
 def _hparams(hp: dict) -> tdf_hparams:
-    return tdf_hparams(hp["n_vocab"], hp["n_embd"], hp["n_layer"], hp["n_head"], hp["n_head_kv"],
-                       hp["head_dim"], hp["n_ff"], hp["rms_eps"], hp["rope_theta"],
-                       DTYPES[hp["weight_dtype"]])
+    flags = hp.get("swa_layers")
+    arr = None if flags is None else (ctypes.c_int8 * max(1, len(flags)))(*[1 if f else 0 for f in flags])
+    h = tdf_hparams(hp["n_vocab"], hp["n_embd"], hp["n_layer"], hp["n_head"], hp["n_head_kv"],
+                    hp["head_dim"], hp["n_ff"], hp["rms_eps"], hp["rope_theta"],
+                    DTYPES[hp["weight_dtype"]], int(hp.get("n_swa") or 0),
+                    ctypes.cast(arr, ctypes.POINTER(ctypes.c_int8)) if arr is not None else None)
+    h._keep = arr  # the flags must outlive the create call
+    return h
 
 
 class Model:

@@ -151,4 +151,15 @@ int intake_batch(const KvBook& book, const tdf_batch* b, int n_vocab, int n_batc
   return TDF_OK;
 }
 
+int32_t KvBook::first_at_or_after(int s, int32_t n, int32_t pos_lo) const {
+  const std::vector<int32_t>& L = seq_cells_[s];
+  int32_t lo = 0, hi = std::min<int32_t>(n, (int32_t)L.size());
+  while (lo < hi) {
+    const int32_t mid = (lo + hi) / 2;
+    if (cell_pos_[L[mid]] < pos_lo) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
 }  // namespace tdf

@@ -49,6 +49,10 @@ class KvBook {
   // none, the n lowest-index free cells.  False if fewer than n are free.
   bool find_slots(int n, std::vector<int32_t>& out) const;
 
+  // Index in sequence s's list of its first cell with position >= pos_lo,
+  // searching the first n entries (the list is position-ordered).
+  int32_t first_at_or_after(int s, int32_t n, int32_t pos_lo) const;
+
   // Mark `cell` as holding (pos, seq_mask) and append it to each of its
   // sequences' lists; returns the cell's index in the list of sequence s0.
   int32_t place(int32_t cell, int32_t pos, uint64_t seq_mask, int s0,

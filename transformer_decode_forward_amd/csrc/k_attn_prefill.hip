@@ -16,7 +16,9 @@
 //   O^T += V^T P^T   (lane = query, registers = head dims)
 // with V staged transposed in LDS, read in the same cell order.  The rescale
 // by exp(m_old - m_new) is per lane.  Cells come from the sequence's
-// position-ordered cell list; token t sees the first n_vis[t] entries.
+// position-ordered cell list; token t sees the first n_vis[t] entries, or in
+// a windowed layer the entries [n_lo[t], n_vis[t]) (the block's cell range
+// then starts at the tile's smallest n_lo).
 //
 // K and V are exact in their cache type; Q and the probabilities P are split
 // into a pair hi + lo of the MFMA type (hi = round(x), lo = round(x - hi)),
@@ -68,8 +70,9 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))
   const int ql = lane & 31, qg = lane >> 5;
   const int t = a.tile_tokens[tile * kQT + ql];      // -1 for padding
   const int nvis = t >= 0 ? a.n_vis[t] : 0;
+  const int vis_lo = t >= 0 && a.n_lo ? a.n_lo[t] : 0;  // first visible entry (window)
   const int tile_nvis = a.tile_nvis_max[tile];
-  const int c_lo = split * a.chunk;
+  const int c_lo = (a.tile_lo ? a.tile_lo[tile] : 0) + split * a.chunk;
   if (c_lo >= tile_nvis) return;
   const int c_hi = min(tile_nvis, c_lo + a.chunk);
   const int32_t* cells = a.cell_list + a.tile_list_off[tile];
@@ -137,7 +140,7 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ci = c0 + sub * 32 + (r >> 2) * 8 + qg * 4 + (r & 3);
-        if (ci >= nvis || ci >= c_hi) s[sub][r] = -INFINITY;
+        if (ci >= nvis || ci >= c_hi || ci < vis_lo) s[sub][r] = -INFINITY;
         tmax = fmaxf(tmax, s[sub][r]);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));

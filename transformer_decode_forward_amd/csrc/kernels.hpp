@@ -135,6 +135,10 @@ struct PrefillAttnArgs {
   const int32_t* tile_tokens = nullptr;
   const int32_t* tile_list_off = nullptr;
   const int32_t* tile_nvis_max = nullptr;
+  // windowed layers: token t sees list entries [n_lo[t], n_vis[t]); a tile's
+  // cell range starts at tile_lo (its smallest n_lo); NULL = from entry 0
+  const int32_t* n_lo = nullptr;
+  const int32_t* tile_lo = nullptr;
   int n_tiles = 0, H = 0, Hkv = 0, hd = 0, n_ctx = 0;
   int chunk = 0, n_splits = 1;
   float* part_acc = nullptr;
@@ -142,7 +146,8 @@ struct PrefillAttnArgs {
   float* out = nullptr;
   uint16_t* out_hi = nullptr;
   uint16_t* out_lo = nullptr;
-  AttnArgs merge;  // used when n_splits > 1 (T, H, hd, chunk, n_chunks = n_splits, n_vis, parts, outs)
+  AttnArgs merge;  // used when n_splits > 1 (T, H, hd, chunk, n_chunks = n_splits, parts, outs; its
+                   // n_vis counts entries from the tile's first entry)
 };
 bool prefill_attention_supported(int kv_dtype, int head_dim);
 hipError_t launch_attention_prefill(const PrefillAttnArgs& a, hipStream_t s);

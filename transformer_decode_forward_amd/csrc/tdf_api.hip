@@ -63,13 +63,14 @@ static_assert(kChunkCapDecode <= kMergeMaxSplits && kChunkCapPrefill <= kMergeMa
 constexpr int kQTile = 32;           // tokens per prefill attention query tile
 
 // int32 entries of the per-call staging area.  A ubatch of U tokens stores 5
-// per token, its selected rows (<= U) and its query tiles (at most
-// U/32 + 1 + min(U, n_seq_max) tiles of 34 entries), rounded up to 4.
+// per token, its selected rows (<= U), its query tiles (at most
+// U/32 + 1 + min(U, n_seq_max) tiles of 34 entries) and, for windowed
+// attention, 4 more per token and 1 more per tile; rounded up to 4.
 size_t staging_i32(int n_batch, int n_ubatch, int n_seq_max) {
   const size_t U = (size_t)n_ubatch;
   const size_t n_ub = ((size_t)n_batch + U - 1) / U;
   const size_t tiles = U / kQTile + 1 + std::min<size_t>(U, (size_t)n_seq_max);
-  return n_ub * (6 * U + (kQTile + 2) * tiles + 4) + 16;
+  return n_ub * (10 * U + (kQTile + 3) * tiles + 4) + 16;
 }
 size_t staging_i64_base(int n_batch, int n_ubatch, int n_seq_max) {
   return (staging_i32(n_batch, n_ubatch, n_seq_max) * 4 + 15) & ~(size_t)15;
@@ -78,7 +79,9 @@ size_t staging_i64_base(int n_batch, int n_ubatch, int n_seq_max) {
 }  // namespace
 
 struct tdf_model {
-  tdf_hparams hp;
+  tdf_hparams hp;               // swa_layers cleared; the flags live in `windowed`
+  std::vector<uint8_t> windowed;  // per layer: attention limited to the n_swa window
+  bool any_window = false;
   const void* token_embd;
   const float* output_norm;
   const void* output;
@@ -128,7 +131,7 @@ struct tdf_context {
 
   // launch replay: one instantiated graph per decode ubatch shape
   bool use_graphs = true;
-  std::map<std::tuple<int, int, int, int, int, const void*, const void*, int, int>, hipGraphExec_t> graphs;
+  std::map<std::tuple<int, int, int, int, int, const void*, const void*, int, int, int, int>, hipGraphExec_t> graphs;
   int64_t n_graph_captures = 0, n_graph_replays = 0;
 
   // results of the last decode
@@ -285,6 +288,7 @@ extern "C" tdf_model* tdf_model_create(const tdf_hparams* hp, const tdf_weights*
     set_err("head_dim must be 16, 32, 64 or 128");
     return nullptr;
   }
+  if (h.n_swa < 0) { set_err("n_swa must be >= 0"); return nullptr; }
   if (!w->token_embd || !w->output_norm || (h.n_layer > 0 && !w->layers)) { set_err("missing weight pointer"); return nullptr; }
   for (int l = 0; l < h.n_layer; ++l) {
     const tdf_layer_weights& L = w->layers[l];
@@ -295,6 +299,12 @@ extern "C" tdf_model* tdf_model_create(const tdf_hparams* hp, const tdf_weights*
   }
   tdf_model* m = new tdf_model();
   m->hp = h;
+  m->hp.swa_layers = nullptr;
+  m->windowed.assign(h.n_layer, 0);
+  for (int l = 0; l < h.n_layer; ++l) {
+    m->windowed[l] = h.n_swa > 0 && (!h.swa_layers || h.swa_layers[l] != 0);
+    m->any_window = m->any_window || m->windowed[l];
+  }
   m->token_embd = w->token_embd;
   m->output_norm = (const float*)w->output_norm;
   m->output = w->output ? w->output : w->token_embd;
@@ -416,6 +426,12 @@ struct UbatchDev {
   bool sel_identity = false;  // selected rows are exactly 0..T-1
   int attn_chunk = 64, attn_grid = 1;  // split-K decode attention: cells per split, splits launched
   int nvis_max = 0;
+  // windowed layers: first visible list entry per token (n_lo), the shifted
+  // list start and count (decode attention), per-tile first entry and the
+  // per-token count from it (matrix-core attention and its merge)
+  const int32_t *n_lo = nullptr, *list_off_w = nullptr, *n_vis_w = nullptr;
+  const int32_t *n_vis_rel = nullptr, *tile_lo = nullptr;
+  int attn_chunk_w = 64, attn_grid_w = 1, nvis_max_w = 0, span_max_w = 0;
   int out_row0 = 0;  // first logits row of this ubatch
 };
 
@@ -489,6 +505,7 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     if (int rc = run_linear(c, qa, big, TDF_OP_QKV)) return rc;
     u_parts = 0;
 
+    const bool win = m->windowed[l] != 0;
     if (T > kDecodeMaxT && prefill_attention_supported(c->kv_dtype, hd)) {
       PrefillAttnArgs pa;
       pa.q = c->q;
@@ -497,19 +514,21 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
       pa.cell_list = c->cell_list; pa.n_vis = u.n_vis;
       pa.tile_tokens = u.tile_tokens; pa.tile_list_off = u.tile_off; pa.tile_nvis_max = u.tile_nvis;
       pa.n_tiles = u.n_tiles; pa.H = H; pa.Hkv = Hkv; pa.hd = hd; pa.n_ctx = c->n_ctx;
+      if (win) { pa.n_lo = u.n_lo; pa.tile_lo = u.tile_lo; }
       // split the cell range only when the tiles alone leave CUs idle; at
       // least 256 cells per split, at most kChunkCapPrefill splits
+      const int span = win ? u.span_max_w : u.nvis_max;
       const int blocks = u.n_tiles * Hkv;
       int want = std::max(1, (512 + blocks - 1) / blocks);
-      int chunk = std::max(256, (u.nvis_max + want - 1) / want);
-      chunk = std::max(chunk, (u.nvis_max + kChunkCapPrefill - 1) / kChunkCapPrefill);
+      int chunk = std::max(256, (span + want - 1) / want);
+      chunk = std::max(chunk, (span + kChunkCapPrefill - 1) / kChunkCapPrefill);
       chunk = (chunk + 63) / 64 * 64;
       pa.chunk = chunk;
-      pa.n_splits = (u.nvis_max + chunk - 1) / chunk;
+      pa.n_splits = (span + chunk - 1) / chunk;
       pa.part_acc = c->part_acc; pa.part_ml = c->part_ml;
       pa.out = c->o; pa.out_hi = c->o_hi; pa.out_lo = c->o_lo;
       pa.merge.T = T; pa.merge.H = H; pa.merge.Hkv = Hkv; pa.merge.hd = hd;
-      pa.merge.n_vis = u.n_vis; pa.merge.chunk = chunk; pa.merge.n_chunks = pa.n_splits;
+      pa.merge.n_vis = win ? u.n_vis_rel : u.n_vis; pa.merge.chunk = chunk; pa.merge.n_chunks = pa.n_splits;
       pa.merge.merge_single = 1;
       pa.merge.part_acc = c->part_acc; pa.merge.part_ml = c->part_ml;
       pa.merge.out = c->o; pa.merge.out_hi = c->o_hi; pa.merge.out_lo = c->o_lo;
@@ -521,10 +540,12 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
       at.q = c->q;
       at.k_cache = kv_k(c, l); at.v_cache = kv_v(c, l);
       at.kv_dtype = c->kv_dtype;
-      at.cell_list = c->cell_list; at.list_off = u.list_off; at.n_vis = u.n_vis;
+      at.cell_list = c->cell_list;
+      at.list_off = win ? u.list_off_w : u.list_off;
+      at.n_vis = win ? u.n_vis_w : u.n_vis;
       at.T = T; at.H = H; at.Hkv = Hkv; at.hd = hd; at.n_ctx = c->n_ctx;
-      at.chunk = u.attn_chunk;
-      at.n_chunks = u.attn_grid;
+      at.chunk = win ? u.attn_chunk_w : u.attn_chunk;
+      at.n_chunks = win ? u.attn_grid_w : u.attn_grid;
       at.part_acc = c->part_acc; at.part_ml = c->part_ml;
       at.out = c->o;
       at.out_hi = big ? c->o_hi : nullptr;
@@ -622,7 +643,7 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
 static int run_graphed(tdf_context* c, const UbatchDev& u) {
   const auto key = std::make_tuple(u.T, u.R, u.n_list_writes, u.attn_chunk, u.attn_grid,
                                    (const void*)c->logits, (const void*)u.tokens, u.out_row0,
-                                   (int)u.sel_identity);
+                                   (int)u.sel_identity, u.attn_chunk_w, u.attn_grid_w);
   auto it = c->graphs.find(key);
   if (it == c->graphs.end()) {
     if (c->graphs.size() >= 64) {
@@ -704,14 +725,18 @@ extern "C" int32_t tdf_decode(tdf_context* c, const tdf_batch* b) {
       return TDF_E_DEVICE;
     }
     writes.clear();
-    std::vector<int32_t> list_off(T), n_vis(T), sel;
+    std::vector<int32_t> list_off(T), n_vis(T), sel, n_lo;
     int nvis_max = 0;
+    const bool win = c->m->any_window;
+    if (win) n_lo.resize(T);
     for (int i = 0; i < T; ++i) {
       const int t = u0 + i;
       const int32_t idx = c->book.place(slots[i], in.pos[t], in.seq_mask[t], in.seq0[t], &writes);
       list_off[i] = in.seq0[t] * c->n_ctx;
       n_vis[i] = idx + 1;
       nvis_max = std::max(nvis_max, n_vis[i]);
+      // first list entry inside the window: position > pos - n_swa
+      if (win) n_lo[i] = c->book.first_at_or_after(in.seq0[t], n_vis[i], in.pos[t] - c->m->hp.n_swa + 1);
       c->last_slots[t] = slots[i];
       if (in.output[t]) sel.push_back(i);
     }
@@ -727,7 +752,7 @@ extern "C" int32_t tdf_decode(tdf_context* c, const tdf_batch* b) {
     if (!sel.empty()) memcpy(h32 + 5 * T, sel.data(), sel.size() * 4);
     // query tiles for the matrix-core attention: tokens of one sequence in
     // batch order, 32 at a time
-    std::vector<int32_t> tile_tok, tile_off, tile_nvis;
+    std::vector<int32_t> tile_tok, tile_off, tile_nvis, tile_lo;
     if (T > kDecodeMaxT) {
       std::vector<int> order(T);
       for (int i = 0; i < T; ++i) order[i] = i;
@@ -738,13 +763,16 @@ extern "C" int32_t tdf_decode(tdf_context* c, const tdf_batch* b) {
         int nmax = 0, cnt = 0;
         const size_t base = tile_tok.size();
         tile_tok.resize(base + kQTile, -1);
+        int lmin = INT32_MAX;
         while (k < T && cnt < kQTile && in.seq0[u0 + order[k]] == s0) {
           tile_tok[base + cnt++] = order[k];
           nmax = std::max(nmax, n_vis[order[k]]);
+          if (win) lmin = std::min(lmin, n_lo[order[k]]);
           ++k;
         }
         tile_off.push_back(s0 * c->n_ctx);
         tile_nvis.push_back(nmax);
+        if (win) tile_lo.push_back(lmin);
       }
     }
     const int n_tiles = (int)tile_off.size();
@@ -754,7 +782,32 @@ extern "C" int32_t tdf_decode(tdf_context* c, const tdf_batch* b) {
       memcpy(tp + tile_tok.size(), tile_off.data(), n_tiles * 4);
       memcpy(tp + tile_tok.size() + n_tiles, tile_nvis.data(), n_tiles * 4);
     }
-    const size_t n32 = 5 * (size_t)T + sel.size() + (size_t)(kQTile + 2) * n_tiles;
+    size_t n32 = 5 * (size_t)T + sel.size() + (size_t)(kQTile + 2) * n_tiles;
+    // windowed attention: n_lo, list_off_w, n_vis_w, n_vis_rel per token, tile_lo per tile
+    int nvis_max_w = 0, span_max_w = 0;
+    const size_t w_base = n32;
+    if (win) {
+      std::vector<int32_t> rel(T, 0), tile_of(T, -1);
+      for (int k = 0; k < n_tiles; ++k)
+        for (int q = 0; q < kQTile; ++q) {
+          const int tt = tile_tok[(size_t)k * kQTile + q];
+          if (tt >= 0) tile_of[tt] = k;
+        }
+      int32_t* wp = h32 + w_base;
+      for (int i = 0; i < T; ++i) {
+        wp[i] = n_lo[i];
+        wp[T + i] = list_off[i] + n_lo[i];
+        wp[2 * T + i] = n_vis[i] - n_lo[i];
+        nvis_max_w = std::max(nvis_max_w, n_vis[i] - n_lo[i]);
+        rel[i] = tile_of[i] >= 0 ? n_vis[i] - tile_lo[tile_of[i]] : n_vis[i] - n_lo[i];
+        wp[3 * T + i] = rel[i];
+      }
+      for (int k = 0; k < n_tiles; ++k) {
+        wp[4 * T + k] = tile_lo[k];
+        span_max_w = std::max(span_max_w, tile_nvis[k] - tile_lo[k]);
+      }
+      n32 += 4 * (size_t)T + n_tiles;
+    }
     int64_t* h64 = (int64_t*)(c->ints_host + i64_base + i64_off * 8);
     int64_t* d64 = (int64_t*)((char*)c->ints + i64_base + i64_off * 8);
     if (!writes.empty()) memcpy(h64, writes.data(), writes.size() * 8);
@@ -776,23 +829,36 @@ extern "C" int32_t tdf_decode(tdf_context* c, const tdf_batch* b) {
     ud.tile_off = ud.tile_tokens + (size_t)kQTile * n_tiles;
     ud.tile_nvis = ud.tile_off + n_tiles;
     ud.out_row0 = out_row;
-    if (T <= kDecodeMaxT) {
-      // cells per split grow past 256 splits; the launched grid is the
-      // split count rounded up to a power of two (surplus blocks exit), so a
-      // captured launch sequence stays valid while the context grows
-      int chunk = (nvis_max + kChunkCapDecode - 1) / kChunkCapDecode;
-      chunk = std::max(64, (chunk + 63) / 64 * 64);
-      const int need = (nvis_max + chunk - 1) / chunk;
-      int grid = 1;
-      while (grid < need) grid *= 2;
-      ud.attn_chunk = chunk;
-      ud.attn_grid = std::min(grid, kChunkCapDecode);
-    } else {
-      int chunk = (nvis_max + kChunkCapPrefill - 1) / kChunkCapPrefill;
-      chunk = std::max(64, (chunk + 63) / 64 * 64);
-      ud.attn_chunk = chunk;
-      ud.attn_grid = (nvis_max + chunk - 1) / chunk;
+    if (win) {
+      ud.n_lo = d32 + w_base;
+      ud.list_off_w = ud.n_lo + T;
+      ud.n_vis_w = ud.n_lo + 2 * T;
+      ud.n_vis_rel = ud.n_lo + 3 * T;
+      ud.tile_lo = ud.n_lo + 4 * T;
+      ud.nvis_max_w = nvis_max_w;
+      ud.span_max_w = span_max_w;
     }
+    auto split_cells = [&](int nmax, int& chunk_out, int& grid_out) {
+      if (T <= kDecodeMaxT) {
+        // cells per split grow past 256 splits; the launched grid is the
+        // split count rounded up to a power of two (surplus blocks exit), so
+        // a captured launch sequence stays valid while the context grows
+        int chunk = (nmax + kChunkCapDecode - 1) / kChunkCapDecode;
+        chunk = std::max(64, (chunk + 63) / 64 * 64);
+        const int need = (nmax + chunk - 1) / chunk;
+        int grid = 1;
+        while (grid < need) grid *= 2;
+        chunk_out = chunk;
+        grid_out = std::min(grid, kChunkCapDecode);
+      } else {
+        int chunk = (nmax + kChunkCapPrefill - 1) / kChunkCapPrefill;
+        chunk = std::max(64, (chunk + 63) / 64 * 64);
+        chunk_out = chunk;
+        grid_out = (nmax + chunk - 1) / chunk;
+      }
+    };
+    split_cells(nvis_max, ud.attn_chunk, ud.attn_grid);
+    if (win) split_cells(nvis_max_w, ud.attn_chunk_w, ud.attn_grid_w);
     if (c->use_graphs && T <= kDecodeMaxT) {
       rc = run_graphed(c, ud);
     } else {
