@@ -234,6 +234,59 @@ class OracleContext:
             res.tokens = np.argmax(res.logits, axis=1) if rows else np.zeros(0, dtype=np.int64)
         return res
 
+    def kv_seq_rm(self, seq: int, p0: int, p1: int) -> int:
+        """Remove sequence ``seq`` from its cells with position in [p0, p1)
+        (p1 < 0: no upper end); a cell left with no sequence becomes free.
+        This is the discarding half of sliding the context window forward
+        (Ollama engine page, "KV Cache: memory for causal attention": when
+        the cache is full the window slides instead of the whole context
+        being dropped)."""
+        if seq < 0 or seq >= self.n_seq_max or p0 < 0 or (p1 >= 0 and p1 < p0):
+            return INVALID
+        bit = np.uint64(1 << seq)
+        hit = ((self.cell_seq & bit) != 0) & (self.cell_pos >= p0)
+        if p1 >= 0:
+            hit &= self.cell_pos < p1
+        self.cell_seq[hit] &= ~bit
+        self.cell_pos[hit & (self.cell_seq == 0)] = -1
+        return OK
+
+    def kv_seq_shift(self, seq: int, p0: int, p1: int, delta: int) -> int:
+        """Add ``delta`` to the positions of sequence ``seq``'s cells with
+        position in [p0, p1) (p1 < 0: no upper end) and rotate their cached
+        keys by ``delta`` (Ollama engine page, "KV Cache: memory for causal
+        attention": the model's shift function adjusts the RoPE position
+        encoding of the cached keys).  Keys are stored after RoPE at position
+        p; rotating them by delta gives the keys of position p + delta,
+        because the rotations compose (R(a) R(b) = R(a + b)); the result is
+        stored in the cache's element type again.  The cells must belong to
+        ``seq`` alone, and ``seq``'s positions must keep their order and stay
+        distinct and >= 0; otherwise nothing changes and -1 is returned."""
+        if seq < 0 or seq >= self.n_seq_max or p0 < 0 or (p1 >= 0 and p1 < p0):
+            return INVALID
+        bit = np.uint64(1 << seq)
+        mine = np.flatnonzero((self.cell_seq & bit) != 0)
+        pos = self.cell_pos[mine]
+        hit = pos >= p0
+        if p1 >= 0:
+            hit &= pos < p1
+        if not hit.any() or delta == 0:
+            return OK
+        if np.any(self.cell_seq[mine[hit]] != bit):
+            return INVALID
+        new = pos + np.where(hit, delta, 0)
+        order = np.argsort(pos, kind="stable")
+        if np.any(new < 0) or np.any(np.diff(new[order]) <= 0):
+            return INVALID
+        cells = mine[hit]
+        self.cell_pos[cells] += delta
+        if self.compute:
+            theta = self.hp["rope_theta"]
+            for l in list(self.k_cache):
+                kc = self.k_cache[l]
+                kc[cells] = _round_storage(rope(kc[cells], np.full(cells.size, delta), theta), self.kv_dtype)
+        return OK
+
     def kv_import(self, seq: int, pos0: int, pos1: int, k_layers, v_layers) -> int:
         """Place positions [pos0, pos1) of sequence ``seq`` in cells (one chunk,
         same placement rule as a ubatch) holding the given post-RoPE K and V.
