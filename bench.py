@@ -253,6 +253,21 @@ def main():
     d, F = cfg["n_embd"], cfg["n_ff"]
     gu_us = ctx.time_op("gate_up", 1, 64)
     gg_us = ctx.time_op("gate_up", U, 16)
+    # one slide of the context window: drop the oldest half, shift the rest
+    # down (re-rotating their cached keys in every layer)
+    top = ctx.seq_pos_max(0)
+    half = (top + 1) // 2
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    assert ctx.kv_seq_rm(0, 0, half) == 0
+    t1 = time.perf_counter()
+    assert ctx.kv_seq_shift(0, half, -1, -half) == 0
+    t2 = time.perf_counter()
+    n_shift = top + 1 - half
+    shift_bytes = 2 * n_shift * cfg["n_layer"] * cfg["n_head_kv"] * cfg["head_dim"] * 2  # K read + written
+    slide = {"cells_dropped": half, "cells_shifted": n_shift, "rm_ms": round(1000 * (t1 - t0), 3),
+             "shift_ms": round(1000 * (t2 - t1), 3),
+             "shift_GBs": round(shift_bytes / (t2 - t1) / 1e9, 1)}
     ctx.close()
     ms_step = 1000.0 * t_dec / args.steps
     decode_tps = args.steps / t_dec
@@ -317,6 +332,7 @@ def main():
                              "avg_launch_us": round(gg_us, 2), "flops_per_launch": gg_flops,
                              "executed_flops_per_launch": 2 * gg_flops},
         "measured_peaks": peaks,
+        "kv_slide": slide,
         "kernels": breakdown,
         "cpu_baseline": cpu,
     }

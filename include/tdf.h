@@ -196,6 +196,24 @@ int32_t tdf_last_slots(const tdf_context *c, int32_t *slots);
 int32_t tdf_kv_import(tdf_context *c, int32_t s, int32_t pos0, int32_t n,
                       const void *const *k_layers, const void *const *v_layers);
 
+/* Sliding the context window (Ollama engine page, "KV Cache: memory for
+ * causal attention": when the cache is full, the model's shift function
+ * re-encodes the RoPE positions of the cached keys and the window moves
+ * forward instead of the context being dropped).
+ *
+ * tdf_kv_seq_rm: remove sequence seq from its cells with position in
+ * [p0, p1) (p1 < 0: no upper end); cells left with no sequence become free
+ * for later calls.  tdf_kv_seq_shift: add delta to the positions of seq's
+ * cells with position in [p0, p1) and rotate their cached keys (every layer
+ * and KV head) by delta, so that they equal keys computed at the new
+ * positions (RoPE rotations compose); the result is stored in the cache type
+ * again.  The shifted cells must belong to seq alone, and seq's positions
+ * must stay >= 0, distinct and in their order.  Both return TDF_OK or
+ * TDF_E_INVALID (bad arguments or a shift that breaks these rules: nothing
+ * changed) or TDF_E_DEVICE. */
+int32_t tdf_kv_seq_rm(tdf_context *c, int32_t seq, int32_t p0, int32_t p1);
+int32_t tdf_kv_seq_shift(tdf_context *c, int32_t seq, int32_t p0, int32_t p1, int32_t delta);
+
 /* Accumulated launches and GPU time (ms, HIP events) of operation class op
  * since the last reset, for the matrix-core path (mfma = 1: ubatches above
  * 32 tokens) or the decode path (mfma = 0).  Only for TDF_CTX_PROFILE

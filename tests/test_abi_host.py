@@ -140,3 +140,41 @@ def test_window_hparams_accepted_and_checked():
     tdf.Model(dict(HP, n_swa=8), dry_run=True)
     with pytest.raises(Exception):
         tdf.Model(dict(HP, n_swa=-1), dry_run=True)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_scripts_with_removal_and_shift_match_oracle(seed):
+    """Decode calls interleaved with range removals and shifts (valid and
+    invalid): return codes, cells and positions bit-exact with the oracle."""
+    rng = np.random.default_rng(100 + seed)
+    n_seq = int(rng.integers(1, 4))
+    g, o = pair(n_ctx=int(rng.integers(16, 48)), n_ubatch=int(rng.integers(1, 9)), n_seq_max=n_seq,
+                n_batch=int(rng.integers(8, 20)))
+    for step in range(40):
+        r = rng.random()
+        s = int(rng.integers(0, n_seq + (1 if step % 11 == 10 else 0)))  # sometimes an invalid id
+        if r < 0.5:
+            n = int(rng.integers(1, 8))
+            kw = {}
+            if rng.random() < 0.5:
+                kw["seq_ids"] = [list(rng.choice(n_seq, size=int(rng.integers(1, min(2, n_seq) + 1)),
+                                                 replace=False)) for _ in range(n)]
+            toks = list(rng.integers(0, 100, size=n))
+            rg, ro = g.decode(toks, **kw), o.decode(toks, **kw).status
+            if ro == 0:
+                pass
+        elif r < 0.75:
+            top = max(0, o.seq_pos_max(min(s, n_seq - 1)))
+            p0 = int(rng.integers(0, top + 2))
+            p1 = -1 if rng.random() < 0.3 else int(rng.integers(p0 - 1, top + 3))
+            rg, ro = g.kv_seq_rm(s, p0, p1), o.kv_seq_rm(s, p0, p1)
+        else:
+            top = max(0, o.seq_pos_max(min(s, n_seq - 1)))
+            p0 = int(rng.integers(0, top + 2))
+            p1 = -1 if rng.random() < 0.5 else int(rng.integers(p0, top + 3))
+            delta = int(rng.integers(-top - 2, top + 3))
+            rg, ro = g.kv_seq_shift(s, p0, p1, delta), o.kv_seq_shift(s, p0, p1, delta)
+        assert rg == ro, (step, r, rg, ro, tdf.tdf_last_error())
+        assert_same_state(g, o, n_seq)
+    # the device-side lists were rewritten after removals: placements still agree
+    assert g.decode([1]) == o.decode([1]).status

@@ -87,6 +87,8 @@ def lib():
             "tdf_profile_reset": (_i32, [_vp]),
             "tdf_graph_counts": (_i32, [_vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
             "tdf_time_op": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_double)]),
+            "tdf_kv_seq_rm": (_i32, [_vp, _i32, _i32, _i32]),
+            "tdf_kv_seq_shift": (_i32, [_vp, _i32, _i32, _i32, _i32]),
             "tdf_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -304,6 +306,12 @@ class Context:
         cap, rep = ctypes.c_int64(), ctypes.c_int64()
         lib().tdf_graph_counts(self.handle, ctypes.byref(cap), ctypes.byref(rep))
         return cap.value, rep.value
+
+    def kv_seq_rm(self, seq: int, p0: int, p1: int) -> int:
+        return lib().tdf_kv_seq_rm(self.handle, seq, p0, p1)
+
+    def kv_seq_shift(self, seq: int, p0: int, p1: int, delta: int) -> int:
+        return lib().tdf_kv_seq_shift(self.handle, seq, p0, p1, delta)
 
     def time_op(self, op: str, n_tokens: int, reps: int) -> float:
         """Mean duration (us) of `reps` back-to-back launches of one linear layer

@@ -162,4 +162,51 @@ int32_t KvBook::first_at_or_after(int s, int32_t n, int32_t pos_lo) const {
   return lo;
 }
 
+void KvBook::seq_rm(int s, int32_t p0, int32_t p1) {
+  auto& lst = seq_cells_[s];
+  std::vector<int32_t> keep;
+  keep.reserve(lst.size());
+  const uint64_t bit = 1ull << s;
+  for (int32_t c : lst) {
+    const int32_t p = cell_pos_[c];
+    if (p >= p0 && (p1 < 0 || p < p1)) {
+      cell_seq_[c] &= ~bit;
+      if (cell_seq_[c] == 0) {
+        cell_pos_[c] = -1;
+        --n_used_;
+        first_free_hint_ = std::min(first_free_hint_, c);
+      }
+    } else {
+      keep.push_back(c);
+    }
+  }
+  lst.swap(keep);
+  seq_max_[s] = lst.empty() ? -1 : cell_pos_[lst.back()];
+}
+
+bool KvBook::shift_cells(int s, int32_t p0, int32_t p1, int32_t delta, std::vector<int32_t>& cells) const {
+  cells.clear();
+  const auto& lst = seq_cells_[s];
+  const uint64_t bit = 1ull << s;
+  int64_t prev = -1;  // new position of the previous list entry
+  for (int32_t c : lst) {
+    const int32_t p = cell_pos_[c];
+    const bool hit = p >= p0 && (p1 < 0 || p < p1);
+    const int64_t np = (int64_t)p + (hit ? delta : 0);
+    if (hit) {
+      if (cell_seq_[c] != bit) { cells.clear(); return false; }
+      cells.push_back(c);
+    }
+    if (np < 0 || np <= prev || np > INT32_MAX) { cells.clear(); return false; }
+    prev = np;
+  }
+  return true;
+}
+
+void KvBook::seq_shift(int s, int32_t delta, const std::vector<int32_t>& cells) {
+  for (int32_t c : cells) cell_pos_[c] += delta;
+  const auto& lst = seq_cells_[s];
+  seq_max_[s] = lst.empty() ? -1 : cell_pos_[lst.back()];
+}
+
 }  // namespace tdf

@@ -49,6 +49,20 @@ class KvBook {
   // none, the n lowest-index free cells.  False if fewer than n are free.
   bool find_slots(int n, std::vector<int32_t>& out) const;
 
+  // Remove sequence s from its cells with position in [p0, p1) (p1 < 0: no
+  // upper end); cells left with no sequence become free.  The list of s is
+  // compacted in order.  Arguments are checked by the caller.
+  void seq_rm(int s, int32_t p0, int32_t p1);
+
+  // Cells of sequence s with position in [p0, p1) (p1 < 0: no upper end)
+  // that a shift by delta would move, in list order; false (and nothing
+  // returned) if the shift is not allowed: a cell also holds another
+  // sequence, a position would become negative, or s's positions would lose
+  // their list order.
+  bool shift_cells(int s, int32_t p0, int32_t p1, int32_t delta, std::vector<int32_t>& cells) const;
+  // Apply a shift that shift_cells allowed.
+  void seq_shift(int s, int32_t delta, const std::vector<int32_t>& cells);
+
   // Index in sequence s's list of its first cell with position >= pos_lo,
   // searching the first n entries (the list is position-ordered).
   int32_t first_at_or_after(int s, int32_t n, int32_t pos_lo) const;

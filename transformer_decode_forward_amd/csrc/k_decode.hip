@@ -213,6 +213,42 @@ hipError_t launch_gather_rows(const float* src, const int32_t* rows, int R, int 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// cache shift: re-rotate the stored keys of some cells (see launch_kv_rotate)
+
+template <typename KvT>
+__global__ void __launch_bounds__(256) kv_rotate_kernel(char* kv, size_t layer_stride_bytes, int Hkv,
+                                                        int n_ctx, int hd, const int32_t* __restrict__ cells,
+                                                        int n_cells, const double2* __restrict__ cs) {
+  typedef typename KvStore<KvT>::T ST;
+  const int half = hd / 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)n_cells * Hkv * half) return;
+  const int i = (int)(idx % half);
+  const int h = (int)((idx / half) % Hkv);
+  const int c = cells[idx / half / Hkv];
+  ST* k = (ST*)(kv + (size_t)blockIdx.y * layer_stride_bytes);
+  const int64_t e = ((int64_t)h * n_ctx + c) * hd + 2 * i;
+  const double y0 = KvStore<KvT>::load(k, e), y1 = KvStore<KvT>::load(k, e + 1);
+  const double2 r = cs[i];
+  KvStore<KvT>::store(k, e, (float)(y0 * r.x - y1 * r.y));
+  KvStore<KvT>::store(k, e + 1, (float)(y0 * r.y + y1 * r.x));
+}
+
+hipError_t launch_kv_rotate(void* kv, int kv_dtype, size_t layer_stride_bytes, int L, int Hkv, int n_ctx, int hd,
+                            const int32_t* cells, int n_cells, const double2* cs, hipStream_t s) {
+  if (n_cells <= 0 || L <= 0) return hipSuccess;
+  const int64_t n = (int64_t)n_cells * Hkv * (hd / 2);
+  const dim3 grid((unsigned)((n + 255) / 256), (unsigned)L);
+  if (kv_dtype == TDF_BF16)
+    kv_rotate_kernel<kv_bf16><<<grid, 256, 0, s>>>((char*)kv, layer_stride_bytes, Hkv, n_ctx, hd, cells, n_cells, cs);
+  else if (kv_dtype == TDF_F16)
+    kv_rotate_kernel<kv_f16><<<grid, 256, 0, s>>>((char*)kv, layer_stride_bytes, Hkv, n_ctx, hd, cells, n_cells, cs);
+  else
+    kv_rotate_kernel<float><<<grid, 256, 0, s>>>((char*)kv, layer_stride_bytes, Hkv, n_ctx, hd, cells, n_cells, cs);
+  return hipGetLastError();
+}
+
 // Greedy token: two passes.  Pass 1, block (split j, row r), reduces the
 // columns [j*L, j*L + L) of a row to (max, lowest index of the max); pass 2,
 // one block per row, reduces the splits.  L = 2048 * m with m the smallest

@@ -82,6 +82,14 @@ hipError_t launch_scatter(int32_t* dst, const int64_t* pairs, int n, hipStream_t
 // with g set also u[r] = g * src[rows[r]] and ssp[r * stride] = its sum of squares
 hipError_t launch_gather_rows(const float* src, const int32_t* rows, int R, int d, float* dst,
                               const float* g, float* u, float* ssp, int stride, hipStream_t s);
+// Rotate the cached keys of n_cells cells (every layer and KV head) by the
+// per-pair angles whose (cos, sin) are cs[hd/2]: (k[2i], k[2i+1]) ->
+// (k[2i] c - k[2i+1] s, k[2i] s + k[2i+1] c), in double, stored back in the
+// cache type.  kv: cache base, layer_stride_bytes: distance between the K
+// arrays of consecutive layers; each K array is [Hkv][n_ctx][hd].
+hipError_t launch_kv_rotate(void* kv, int kv_dtype, size_t layer_stride_bytes, int L, int Hkv, int n_ctx, int hd,
+                            const int32_t* cells, int n_cells, const double2* cs, hipStream_t s);
+
 // tok[r] = argmax_n logits[r][n] (lowest index on ties), in two passes over
 // argmax_splits(V) column splits; part_v / part_i hold R * argmax_splits(V)
 // partial results

@@ -1010,6 +1010,66 @@ extern "C" int32_t tdf_kv_import(tdf_context* c, int32_t s, int32_t pos0, int32_
   return TDF_OK;
 }
 
+extern "C" int32_t tdf_kv_seq_rm(tdf_context* c, int32_t seq, int32_t p0, int32_t p1) {
+  if (!c || seq < 0 || seq >= c->n_seq_max || p0 < 0 || (p1 >= 0 && p1 < p0)) {
+    set_err("invalid kv_seq_rm arguments");
+    return TDF_E_INVALID;
+  }
+  c->book.seq_rm(seq, p0, p1);
+  if (c->dry_run) return TDF_OK;
+  // rewrite the device copy of seq's (compacted) cell list
+  const std::vector<int32_t>& lst = c->book.seq_cells(seq);
+  if (lst.empty()) return TDF_OK;
+  std::vector<int64_t> writes(2 * lst.size());
+  for (size_t i = 0; i < lst.size(); ++i) {
+    writes[2 * i] = (int64_t)seq * c->n_ctx + (int64_t)i;
+    writes[2 * i + 1] = lst[i];
+  }
+  void* dw = nullptr;
+  TDF_HIP(hipMallocAsync(&dw, writes.size() * 8, c->stream));
+  TDF_HIP(hipMemcpyAsync(dw, writes.data(), writes.size() * 8, hipMemcpyHostToDevice, c->stream));
+  TDF_HIP(launch_scatter(c->cell_list, (const int64_t*)dw, (int)lst.size(), c->stream));
+  TDF_HIP(hipFreeAsync(dw, c->stream));
+  TDF_HIP(hipStreamSynchronize(c->stream));
+  return TDF_OK;
+}
+
+extern "C" int32_t tdf_kv_seq_shift(tdf_context* c, int32_t seq, int32_t p0, int32_t p1, int32_t delta) {
+  if (!c || seq < 0 || seq >= c->n_seq_max || p0 < 0 || (p1 >= 0 && p1 < p0)) {
+    set_err("invalid kv_seq_shift arguments");
+    return TDF_E_INVALID;
+  }
+  if (delta == 0) return TDF_OK;
+  std::vector<int32_t> cells;
+  if (!c->book.shift_cells(seq, p0, p1, delta, cells)) {
+    set_err("kv_seq_shift: a shifted cell is shared, a position would be negative, or the order would change");
+    return TDF_E_INVALID;
+  }
+  if (cells.empty()) return TDF_OK;
+  c->book.seq_shift(seq, delta, cells);
+  if (c->dry_run) return TDF_OK;
+  const tdf_hparams& h = c->m->hp;
+  const int hd = h.head_dim, half = hd / 2;
+  // angles delta * theta^(-2i/hd), as the RoPE table of a ubatch
+  std::vector<double> cs(2 * half);
+  for (int i = 0; i < half; ++i) {
+    const double phi = (double)delta * std::pow((double)h.rope_theta, -2.0 * i / hd);
+    cs[2 * i] = std::cos(phi);
+    cs[2 * i + 1] = std::sin(phi);
+  }
+  void *dcells = nullptr, *dcs = nullptr;
+  TDF_HIP(hipMallocAsync(&dcells, cells.size() * 4, c->stream));
+  TDF_HIP(hipMallocAsync(&dcs, cs.size() * 8, c->stream));
+  TDF_HIP(hipMemcpyAsync(dcells, cells.data(), cells.size() * 4, hipMemcpyHostToDevice, c->stream));
+  TDF_HIP(hipMemcpyAsync(dcs, cs.data(), cs.size() * 8, hipMemcpyHostToDevice, c->stream));
+  TDF_HIP(launch_kv_rotate(c->kv, c->kv_dtype, 2 * c->kv_layer_bytes, h.n_layer, h.n_head_kv, c->n_ctx, hd,
+                           (const int32_t*)dcells, (int)cells.size(), (const double2*)dcs, c->stream));
+  TDF_HIP(hipFreeAsync(dcells, c->stream));
+  TDF_HIP(hipFreeAsync(dcs, c->stream));
+  TDF_HIP(hipStreamSynchronize(c->stream));
+  return TDF_OK;
+}
+
 extern "C" int32_t tdf_profile_read(const tdf_context* c, int32_t op, int32_t mfma, int64_t* launches, double* ms) {
   if (!c || !c->profile || op < 0 || op >= TDF_OP_COUNT) return TDF_E_INVALID;
   const int slot = 2 * op + (mfma ? 1 : 0);
