@@ -253,6 +253,19 @@ def main():
     d, F = cfg["n_embd"], cfg["n_ff"]
     gu_us = ctx.time_op("gate_up", 1, 64)
     gg_us = ctx.time_op("gate_up", U, 16)
+    # sampling chain on the last step's logits row (tdf_sample), per call
+    samp = {}
+    rng = np.random.default_rng(0)
+    for name, (t, k, tp, mp) in {"k40": (0.8, 40, 0.9, 0.05), "k1024": (1.0, 1024, 0.95, 0.0)}.items():
+        ts = []
+        for _ in range(20):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            rc, _ = ctx.sample(t, k, tp, mp, rng.random(1))
+            ts.append(time.perf_counter() - t0)
+            assert rc == 0, tdf.tdf_last_error()
+        samp[name] = {"temperature": t, "top_k": k, "top_p": tp, "min_p": mp,
+                      "us_per_call_median": round(1e6 * float(np.median(ts)), 1)}
     # one slide of the context window: drop the oldest half, shift the rest
     # down (re-rotating their cached keys in every layer)
     top = ctx.seq_pos_max(0)
@@ -333,6 +346,7 @@ def main():
                              "executed_flops_per_launch": 2 * gg_flops},
         "measured_peaks": peaks,
         "kv_slide": slide,
+        "sampling": samp,
         "kernels": breakdown,
         "cpu_baseline": cpu,
     }

@@ -196,6 +196,28 @@ int32_t tdf_last_slots(const tdf_context *c, int32_t *slots);
 int32_t tdf_kv_import(tdf_context *c, int32_t s, int32_t pos0, int32_t n,
                       const void *const *k_layers, const void *const *v_layers);
 
+/* Token sampling (Ollama engine page, "Token sampling pipeline"): for each
+ * output row i of the last tdf_decode (i in [0, tdf_n_outputs)), one token
+ * from its logits.  temperature <= 0: greedy (argmax, lowest index on ties;
+ * the other fields are ignored).  Otherwise the chain Top-K (the top_k
+ * highest logits, ties to the lower token id; 1 <= top_k <= 1024) ->
+ * temperature (logits divided by it) -> softmax -> Top-P (tokens in ranking
+ * order while the cumulative probability is <= top_p; the first always;
+ * top_p >= 1 keeps all) ->
+ * Min-P (probability >= min_p times the largest; 0 <= min_p <= 1) -> draw:
+ * the first survivor whose cumulative probability exceeds u[i] times the
+ * survivors' total.  u: HOST array of n_outputs uniform numbers in [0, 1)
+ * (the caller's seeded generator makes the draw reproducible); tokens: HOST
+ * array of n_outputs entries, written on success.  Returns TDF_OK,
+ * TDF_E_INVALID (bad parameters or u outside [0, 1); nothing written) or
+ * TDF_E_DEVICE. */
+typedef struct {
+  float temperature;
+  int32_t top_k;
+  float top_p, min_p;
+} tdf_sampling;
+int32_t tdf_sample(tdf_context *c, const tdf_sampling *p, const float *u, int32_t *tokens);
+
 /* Sliding the context window (Ollama engine page, "KV Cache: memory for
  * causal attention": when the cache is full, the model's shift function
  * re-encodes the RoPE positions of the cached keys and the window moves

@@ -15,7 +15,8 @@ Readings where the pages leave a step open:
 * Ordering: candidates are ranked by logit, larger first, ties to the lower
   token id; Top-K keeps the first K of that ranking (K in [1, V]).
 * Top-P: token i of the ranking survives when the cumulative probability of
-  tokens 0..i is <= p; the first token always survives.
+  tokens 0..i is <= p; the first token always survives; p >= 1 keeps every
+  token (the cumulative never exceeds 1, whatever the rounding).
 * Min-P: the threshold is min_p times the largest probability; tokens with
   probability >= threshold survive.
 * Draw: over the survivors in ranking order, the first token whose
@@ -46,6 +47,8 @@ def sample(logits: np.ndarray, temperature: float, top_k: int, top_p: float, min
     cum = np.cumsum(p)
     keep = cum <= top_p
     keep[0] = True
+    if top_p >= 1:
+        keep[:] = True
     n = int(np.argmin(keep)) if not keep.all() else keep.size  # survivors form a prefix
     n = min(n, int(np.count_nonzero(p >= min_p * p[0])))
     total = cum[n - 1]
@@ -55,9 +58,12 @@ def sample(logits: np.ndarray, temperature: float, top_k: int, top_p: float, min
 
 def sample_margin(logits: np.ndarray, temperature: float, top_k: int, top_p: float, min_p: float,
                   u: float) -> float:
-    """Smallest relative distance of any floating-point decision of the draw
-    from its boundary (Top-P cut, Min-P cut, the draw itself); results of
-    two implementations may differ only when this is tiny."""
+    """Smallest distance of a floating-point decision of the chain from its
+    boundary: the Top-P cut (|cumulative - p|), the Min-P cut (relative
+    |probability - threshold| / threshold), the draw (|cumulative - u total|)
+    and, for greedy, the top-2 logit gap.  Two implementations that compute
+    the probabilities in different precision or order may disagree only
+    where this is tiny."""
     z = np.asarray(logits, dtype=np.float64)
     if temperature <= 0:
         top2 = np.sort(z)[-2:]
@@ -68,15 +74,16 @@ def sample_margin(logits: np.ndarray, temperature: float, top_k: int, top_p: flo
     p = e / e.sum()
     cum = np.cumsum(p)
     m = np.inf
-    if cum.size > 1:
-        m = min(m, float(np.min(np.abs(cum[:-1] - top_p))))
-    m = min(m, float(np.min(np.abs(p - min_p * p[0])[1:])) if p.size > 1 else np.inf)
+    if cum.size > 1 and top_p < 1:
+        m = min(m, float(np.min(np.abs(cum[1:] - top_p))))
+    if p.size > 1 and min_p > 0:
+        thr = min_p * p[0]
+        m = min(m, float(np.min(np.abs(p[1:] - thr))) / thr)
     keep = cum <= top_p
     keep[0] = True
+    if top_p >= 1:
+        keep[:] = True
     n = int(np.argmin(keep)) if not keep.all() else keep.size
     n = min(n, int(np.count_nonzero(p >= min_p * p[0])))
     m = min(m, float(np.min(np.abs(cum[:n] - u * cum[n - 1]))))
-    if order.size < z.size:  # the K-th and (K+1)-th logits
-        full = rank(z)
-        m = min(m, float(abs(z[full[order.size - 1]] - z[full[order.size]])) or np.inf)
     return m

@@ -46,6 +46,10 @@ class tdf_weights(ctypes.Structure):
                 ("layers", ctypes.POINTER(tdf_layer_weights))]
 
 
+class tdf_sampling(ctypes.Structure):
+    _fields_ = [("temperature", _f32), ("top_k", _i32), ("top_p", _f32), ("min_p", _f32)]
+
+
 class tdf_context_params(ctypes.Structure):
     _fields_ = [("n_ctx", _i32), ("n_batch", _i32), ("n_ubatch", _i32), ("n_seq_max", _i32),
                 ("kv_dtype", _i32), ("output_all", _i32), ("flags", _i32), ("stream", _vp)]
@@ -88,6 +92,7 @@ def lib():
             "tdf_graph_counts": (_i32, [_vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]),
             "tdf_time_op": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_double)]),
             "tdf_kv_seq_rm": (_i32, [_vp, _i32, _i32, _i32]),
+            "tdf_sample": (_i32, [_vp, ctypes.POINTER(tdf_sampling), ctypes.POINTER(_f32), ctypes.POINTER(_i32)]),
             "tdf_kv_seq_shift": (_i32, [_vp, _i32, _i32, _i32, _i32]),
             "tdf_last_error": (ctypes.c_char_p, []),
         }
@@ -306,6 +311,17 @@ class Context:
         cap, rep = ctypes.c_int64(), ctypes.c_int64()
         lib().tdf_graph_counts(self.handle, ctypes.byref(cap), ctypes.byref(rep))
         return cap.value, rep.value
+
+    def sample(self, temperature: float, top_k: int = 40, top_p: float = 1.0, min_p: float = 0.0,
+               u: Optional[Sequence[float]] = None):
+        """One token per output row of the last decode (tdf_sample); u: one
+        uniform number in [0, 1) per row.  Returns (rc, tokens)."""
+        n = self.n_outputs()
+        ua = (_f32 * max(1, n))(*([0.0] * n if u is None else [float(x) for x in u]))
+        out = (_i32 * max(1, n))()
+        p = tdf_sampling(float(temperature), int(top_k), float(top_p), float(min_p))
+        rc = lib().tdf_sample(self.handle, ctypes.byref(p), ua, out)
+        return rc, list(out)[:n]
 
     def kv_seq_rm(self, seq: int, p0: int, p1: int) -> int:
         return lib().tdf_kv_seq_rm(self.handle, seq, p0, p1)

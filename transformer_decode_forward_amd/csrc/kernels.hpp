@@ -90,6 +90,19 @@ hipError_t launch_gather_rows(const float* src, const int32_t* rows, int R, int 
 hipError_t launch_kv_rotate(void* kv, int kv_dtype, size_t layer_stride_bytes, int L, int Hkv, int n_ctx, int hd,
                             const int32_t* cells, int n_cells, const double2* cs, hipStream_t s);
 
+// Sampling chain of one token per logits row (temperature > 0): Top-K
+// (1 <= top_k <= kMaxTopK), temperature, softmax, Top-P, Min-P, draw with
+// u[r] in [0, 1) (device array); tok[r] receives the token.
+constexpr int kMaxTopK = 1024;
+struct SampleParams {
+  float temperature = 1.f;
+  int top_k = 40;
+  float top_p = 1.f;
+  float min_p = 0.f;
+};
+hipError_t launch_sample(const float* logits, int R, int V, const SampleParams& sp, const float* u,
+                         int32_t* tok, hipStream_t s);
+
 // tok[r] = argmax_n logits[r][n] (lowest index on ties), in two passes over
 // argmax_splits(V) column splits; part_v / part_i hold R * argmax_splits(V)
 // partial results

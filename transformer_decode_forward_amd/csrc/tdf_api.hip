@@ -1010,6 +1010,44 @@ extern "C" int32_t tdf_kv_import(tdf_context* c, int32_t s, int32_t pos0, int32_
   return TDF_OK;
 }
 
+extern "C" int32_t tdf_sample(tdf_context* c, const tdf_sampling* p, const float* u, int32_t* tokens) {
+  if (!c || !p || !tokens || c->dry_run) {
+    set_err("tdf_sample: invalid arguments");
+    return TDF_E_INVALID;
+  }
+  const int R = c->n_outputs, V = c->m->hp.n_vocab;
+  if (R == 0) return TDF_OK;
+  const bool greedy = !(p->temperature > 0.f);
+  if (!greedy) {
+    if (!u || p->top_k < 1 || p->top_k > kMaxTopK || !(p->min_p >= 0.f && p->min_p <= 1.f) ||
+        !(p->top_p == p->top_p) || !std::isfinite(p->temperature)) {
+      set_err("tdf_sample: invalid sampling parameters");
+      return TDF_E_INVALID;
+    }
+    for (int i = 0; i < R; ++i)
+      if (!(u[i] >= 0.f && u[i] < 1.f)) {
+        set_err("tdf_sample: u must lie in [0, 1)");
+        return TDF_E_INVALID;
+      }
+  }
+  if (greedy) {
+    TDF_HIP(launch_argmax(c->logits, R, V, c->d_tok, c->amax_v, c->amax_i, c->stream));
+  } else {
+    // u goes through the argmax partials buffer (>= R floats)
+    TDF_HIP(hipMemcpyAsync(c->amax_v, u, (size_t)R * 4, hipMemcpyHostToDevice, c->stream));
+    SampleParams sp;
+    sp.temperature = p->temperature;
+    sp.top_k = p->top_k;
+    sp.top_p = p->top_p;
+    sp.min_p = p->min_p;
+    TDF_HIP(launch_sample(c->logits, R, V, sp, c->amax_v, c->d_tok, c->stream));
+  }
+  TDF_HIP(hipMemcpyAsync(c->h_tok, c->d_tok, (size_t)R * 4, hipMemcpyDeviceToHost, c->stream));
+  TDF_HIP(hipStreamSynchronize(c->stream));
+  memcpy(tokens, c->h_tok, (size_t)R * 4);
+  return TDF_OK;
+}
+
 extern "C" int32_t tdf_kv_seq_rm(tdf_context* c, int32_t seq, int32_t p0, int32_t p1) {
   if (!c || seq < 0 || seq >= c->n_seq_max || p0 < 0 || (p1 >= 0 && p1 < p0)) {
     set_err("invalid kv_seq_rm arguments");
