@@ -47,7 +47,7 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def build_model(cfg):
+def build_model(cfg, keep_host=True):
     import tdf_synth
     import transformer_decode_forward_amd as tdf
     from transformer_decode_forward_amd.device import to_device
@@ -58,7 +58,8 @@ def build_model(cfg):
     t0 = time.time()
     for i, (name, shape) in enumerate(names):
         a = tdf_synth.make_tensor(cfg, name, shape)
-        host[name] = a
+        if keep_host:
+            host[name] = a
         dev[name] = to_device(a)
         if i % 36 == 0:
             log(f"weights {i}/{len(names)} ({time.time() - t0:.0f}s)")
@@ -181,6 +182,138 @@ def cpu_baseline(cfg, host_weights, ctx_len):
                       f"from synthetic K/V), float64 numpy, {dt:.1f} s"}
 
 
+def decode_bytes_multi(cfg, ctxs):
+    """Algorithmic bytes of one decode step of len(ctxs) tokens (one per
+    sequence at the given contexts): weights once, each token's visible K/V,
+    the new K/V and the logits rows."""
+    d, H, Hkv, hd, F, V, L = (cfg[k] for k in ("n_embd", "n_head", "n_head_kv", "head_dim", "n_ff",
+                                             "n_vocab", "n_layer"))
+    p_layer = d * H * hd + 2 * d * Hkv * hd + H * hd * d + 3 * d * F
+    kv_cell = L * 2 * Hkv * hd * 2
+    return 2 * (L * p_layer + V * d) + kv_cell * (sum(ctxs) + len(ctxs)) + 4 * V * len(ctxs)
+
+
+def run_multiseq(args, cfg):
+    """32 sequences sharing one cache: prompts of 1024..8192 tokens prefilled
+    one call per sequence, then lock-step decode steps of 32 tokens (one per
+    sequence, its own position and id), logits for all 32 rows."""
+    import torch
+    import tdf_synth
+    import transformer_decode_forward_amd as tdf
+    S, lens = cfg["n_seqs"], tdf_synth.seq_lengths(cfg)
+    log(f"generating and uploading weights; {S} sequences, {int(lens.sum())} prompt tokens")
+    model, _ = build_model(cfg, keep_host=False)
+    ctx = tdf.Context(model, n_ctx=cfg["n_ctx"], n_batch=8192, n_ubatch=cfg["n_ubatch"], n_seq_max=S,
+                      kv_dtype=cfg["kv_dtype"])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(S):
+        toks = tdf_synth.prompt(cfg, s, int(lens[s]))
+        assert ctx.decode(toks, seq_ids=[[s]] * len(toks)) == 0, tdf.tdf_last_error()
+    t_pre = time.perf_counter() - t0
+    seq_ids = [[s] for s in range(S)]
+    flags = np.ones(S, dtype=np.int8)
+    toks = [ctx.argmax_ith(int(lens[S - 1]) - 1)] * S
+    for _ in range(args.warmup):
+        assert ctx.decode(toks, seq_ids=seq_ids, logits=flags) == 0, tdf.tdf_last_error()
+        toks = [ctx.argmax_ith(i) for i in range(S)]
+    ctx0 = [int(lens[s]) + args.warmup for s in range(S)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        assert ctx.decode(toks, seq_ids=seq_ids, logits=flags) == 0, tdf.tdf_last_error()
+        toks = [ctx.argmax_ith(i) for i in range(S)]
+    torch.cuda.synchronize()
+    t_dec = time.perf_counter() - t0
+    ctx.close()
+    mean = [c + (args.steps - 1) / 2.0 for c in ctx0]
+    step_bytes = decode_bytes_multi(cfg, mean)
+    ms = 1000.0 * t_dec / args.steps
+    tps = S * args.steps / t_dec
+    log(f"prefill {lens.sum() / t_pre:.0f} tok/s, decode {tps:.1f} tok/s ({ms:.3f} ms per 32-token step)")
+    return {
+        "metric": "decode tok/s (% HBM peak), 8B-shape bf16, 32 sequences",
+        "value": round(tps, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"llama8b_multiseq: {S} sequences, prompts {int(lens.min())}..{int(lens.max())} "
+                               f"tokens prefilled per sequence, then lock-step steps of {S} tokens, all rows' logits; "
+                               f"KV bf16 {cfg['n_ctx']} cells"},
+        "decode": {"tok_s": round(tps, 2), "sum_ctx_mean": round(sum(mean), 1),
+                   "algorithmic_bytes_per_step": int(step_bytes),
+                   "achieved_GBs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                   "frac_hbm_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "prefill": {"tok_s": round(float(lens.sum()) / t_pre, 1), "tokens": int(lens.sum()),
+                    "s": round(t_pre, 3)},
+        "roofline": None, "cpu_baseline": None,
+    }
+
+
+def run_70b(args, cfg):
+    """70B-class model on one GPU: 4096-token prompt in ubatches of 512, then
+    decode windows at positions 4096, 16384 and 32752 (the cache filled up to
+    each window start with synthetic N(0,1) post-RoPE K/V), 16 steps each."""
+    import torch
+    import tdf_synth
+    import transformer_decode_forward_amd as tdf
+    from transformer_decode_forward_amd.device import to_device
+    P, U, L = cfg["prompt_len"], cfg["n_ubatch"], cfg["n_layer"]
+    log("generating and uploading 70B weights (host copies dropped)")
+    model, _ = build_model(cfg, keep_host=False)
+    ctx = tdf.Context(model, n_ctx=cfg["n_ctx"], n_ubatch=U, kv_dtype=cfg["kv_dtype"])
+    prompt = tdf_synth.prompt(cfg, 0, P)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    assert ctx.decode(prompt) == 0, tdf.tdf_last_error()
+    t_pre = time.perf_counter() - t0
+    pre_flops = prefill_flops(cfg, P, U)
+    log(f"prefill {P / t_pre:.0f} tok/s ({pre_flops / t_pre / 1e12:.0f} TFLOP/s)")
+    tok = ctx.argmax_ith(P - 1)
+    windows = []
+    steps = cfg["window_steps"]
+    for w0 in cfg["decode_windows"]:
+        have = ctx.seq_pos_max(0) + 1
+        if w0 > have:
+            ks = [to_device(tdf_synth.kv_fill(cfg, l, "k", have, w0, "bf16")) for l in range(L)]
+            vs = [to_device(tdf_synth.kv_fill(cfg, l, "v", have, w0, "bf16")) for l in range(L)]
+            assert ctx.kv_import(0, have, w0 - have, [t.data_ptr() for t in ks], [t.data_ptr() for t in vs]) == 0
+            del ks, vs
+        for _ in range(2):  # warm-up at the window (positions w0, w0+1)
+            assert ctx.decode([tok]) == 0
+            tok = ctx.argmax_ith(0)
+        n = min(steps, cfg["n_ctx"] - (ctx.seq_pos_max(0) + 1))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            assert ctx.decode([tok]) == 0, tdf.tdf_last_error()
+            tok = ctx.argmax_ith(0)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        c_mean = w0 + 2 + (n - 1) / 2.0
+        b = decode_bytes(cfg, c_mean)
+        windows.append({"window_start": w0, "steps": n, "tok_s": round(n / dt, 2),
+                        "ms_per_step": round(1000 * dt / n, 3), "algorithmic_bytes_per_step": int(b),
+                        "frac_hbm_peak": round(b / (dt / n) / 1e9 / HBM_PEAK_GBS, 4)})
+        log(f"window {w0}: {n / dt:.2f} tok/s")
+    ctx.close()
+    first = windows[0]
+    return {
+        "metric": "decode tok/s (% HBM peak) + prefill tok/s (% MFMA peak), 70B-shape bf16",
+        "value": first["tok_s"], "unit": "tok/s", "n_gpus": 1, "steps": first["steps"], "warmup": 2,
+        "ms_per_step": first["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"llama70b: batch 1, {P}-token prompt in ubatches of {U}, decode windows at "
+                               f"{list(cfg['decode_windows'])} (cache filled with synthetic K/V), KV bf16 "
+                               f"{cfg['n_ctx']} cells"},
+        "decode_windows": windows,
+        "prefill": {"tok_s": round(P / t_pre, 1), "s": round(t_pre, 3),
+                    "algorithmic_tflop": round(pre_flops / 1e12, 3),
+                    "achieved_TFLOPs": round(pre_flops / t_pre / 1e12, 2),
+                    "frac_mfma_peak": round(pre_flops / t_pre / 1e12 / MFMA_BF16_PEAK_TFS, 4)},
+        "roofline": None, "cpu_baseline": None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +342,12 @@ def main():
     cfg = dict(tdf_synth.CONFIGS[args.config])
     if args.swa:
         cfg["n_swa"] = args.swa
+    if args.config == "llama8b_multiseq":
+        print(json.dumps(run_multiseq(args, cfg)), flush=True)
+        return
+    if args.config == "llama70b":
+        print(json.dumps(run_70b(args, cfg)), flush=True)
+        return
     P, U, n_ctx = cfg["prompt_len"], cfg["n_ubatch"], cfg["n_ctx"]
     assert P + args.warmup + args.steps < n_ctx, "steps exceed the KV capacity"
 
