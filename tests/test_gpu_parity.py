@@ -175,3 +175,21 @@ def test_graph_replay_matches_eager_launches(monkeypatch):
     cap, rep = graphed.graph_counts()
     assert rep >= 70 and cap >= 1, (cap, rep)
     assert eager.graph_counts() == (0, 0)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f16"])
+def test_mid_size_ubatches_matrix_cores_streaming(kv_dtype):
+    """Ubatches of 9..32 tokens (several sequences' decode steps) run the
+    matrix-core path that streams the weights once (K split into partial
+    sums, then the epilogue): 1B-class widths, two layers, three sequences
+    prefilled, then steps of 12, 24 and 32 tokens with every row's logits."""
+    cfg = dict(tdf_synth.CONFIGS["llama1b"])
+    cfg, w = make_weights(cfg, layers=2)
+    calls = []
+    for s in range(3):
+        toks = tdf_synth.prompt(cfg, 40 + s, 70 + 30 * s)
+        calls.append(dict(tokens=toks, seq_ids=[[s]] * len(toks)))
+    for k, n in enumerate((12, 24, 32)):
+        calls.append(dict(tokens=tdf_synth.prompt(cfg, 50 + k, n), seq_ids=[[j % 3] for j in range(n)],
+                          logits=np.ones(n, dtype=np.int8)))
+    run_pair(cfg, w, dict(n_ctx=512, n_ubatch=64, n_seq_max=3), calls, TOL_BF16, kv_dtype, "mid ubatch")

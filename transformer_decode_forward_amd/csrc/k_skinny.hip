@@ -1,0 +1,212 @@
+// Linear layers of ubatches of 9..32 tokens (decode steps of several
+// sequences): the weights are streamed once, so the kernel is built like a
+// GEMV with the matrix cores doing the dot products.
+//
+// Pass 1 (skinny_kernel): block = 4 waves = 128 weight rows x one slice of K.
+// A wave computes out[32 tokens][32 rows] on v_mfma_f32_32x32x16_bf16, the
+// activations (the hi/lo bf16 pair of the producers, as in the prefill GEMM)
+// staged per 128-wide K chunk in LDS and shared by the 4 waves, the weights
+// read straight from memory as the B operand (lane = row, 16 contiguous
+// bytes of it).  Every lane requests the next chunk's weights before the
+// current chunk's MFMAs.  Partial sums of each K slice go to a float32
+// workspace [slice][32][N].
+// Pass 2 (skinny_epilogue_kernel): sums the slices and applies the epilogue
+// of the layer (store, residual add, SwiGLU as a hi/lo pair, or RoPE with
+// the K/V cache write), as the other linear kernels do.
+#include "k_common.hpp"
+#include "kernels.hpp"
+#include "tdf.h"
+
+namespace tdf {
+
+constexpr int kSkU = 8;              // 16-wide K steps per chunk
+constexpr int kSkChunk = 16 * kSkU;  // 128
+constexpr int kSkPitch = kSkChunk + 8;
+
+struct SkinnyArgs {
+  LinearArgs a;
+  int N = 0;        // stacked rows (SwiGLU: gate rows then up rows)
+  int ksplit = 1, kslice = 0;
+  float* part = nullptr;  // [ksplit][32][N]
+};
+
+__device__ __forceinline__ const uint16_t* sk_row(const LinearArgs& a, bool swiglu, int r) {
+  if (swiglu) return (const uint16_t*)(r < a.n0 ? a.w0 : a.w1) + (int64_t)(r < a.n0 ? r : r - a.n0) * a.K;
+  if (r < a.n0) return (const uint16_t*)a.w0 + (int64_t)r * a.K;
+  if (r < a.n0 + a.n1) return (const uint16_t*)a.w1 + (int64_t)(r - a.n0) * a.K;
+  return (const uint16_t*)a.w2 + (int64_t)(r - a.n0 - a.n1) * a.K;
+}
+
+template <bool SWIGLU>
+__global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs s) {
+  const LinearArgs& a = s.a;
+  __shared__ __attribute__((aligned(16))) uint16_t Ah[32 * kSkPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Al[32 * kSkPitch];
+  const int nrt = (s.N + 127) / 128;
+  const int rt = blockIdx.x % nrt, ks = blockIdx.x / nrt;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int K = a.K, T = a.T;
+  const int k0 = ks * s.kslice, k1 = min(K, k0 + s.kslice);
+  // this lane's weight row (clamped; rows past N are computed and dropped)
+  const int row = min(rt * 128 + w * 32 + (lane & 31), s.N - 1);
+  const uint16_t* wr = sk_row(a, SWIGLU, row) + (lane >> 5) * 8;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  // activation pieces: 32 tokens x 16 pieces of 8 = 512 per array, 2 per
+  // thread: token min(e/16, T-1), k offset (e%16)*8, e = tid + 256 i
+  constexpr int AP = 32 * (kSkChunk / 8) / 256;
+  bf16x8 bw[kSkU], ah[AP], al[AP];
+  const uint16_t* ahp[AP];
+  const uint16_t* alp[AP];
+#pragma unroll
+  for (int i = 0; i < AP; ++i) {
+    const int e = tid + i * 256;
+    const int64_t off = (int64_t)min(e >> 4, T - 1) * K + (e & 15) * 8;
+    ahp[i] = a.act_hi + off;
+    alp[i] = a.act_lo + off;
+  }
+#define SK_LOAD(kc_)                                                              \
+  do {                                                                            \
+    _Pragma("unroll") for (int u = 0; u < kSkU; ++u) bw[u] = *(const bf16x8*)(wr + (kc_) + u * 16); \
+    _Pragma("unroll") for (int i = 0; i < AP; ++i) {                              \
+      ah[i] = *(const bf16x8*)(ahp[i] + (kc_));                                   \
+      al[i] = *(const bf16x8*)(alp[i] + (kc_));                                   \
+    }                                                                             \
+  } while (0)
+  SK_LOAD(k0);
+  for (int kc = k0; kc < k1; kc += kSkChunk) {
+    __syncthreads();  // the previous chunk's readers are done
+#pragma unroll
+    for (int i = 0; i < AP; ++i) {
+      const int e = tid + i * 256;
+      const int off = (e >> 4) * kSkPitch + (e & 15) * 8;
+      *(bf16x8*)&Ah[off] = ah[i];
+      *(bf16x8*)&Al[off] = al[i];
+    }
+    bf16x8 b[kSkU];
+#pragma unroll
+    for (int u = 0; u < kSkU; ++u) b[u] = bw[u];
+    __syncthreads();
+    if (kc + kSkChunk < k1) SK_LOAD(kc + kSkChunk);
+#pragma unroll
+    for (int u = 0; u < kSkU; ++u) {
+      const int off = (lane & 31) * kSkPitch + u * 16 + (lane >> 5) * 8;
+      const bf16x8 xh = *(const bf16x8*)&Ah[off];
+      const bf16x8 xl = *(const bf16x8*)&Al[off];
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, b[u], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl, b[u], acc, 0, 0, 0);
+    }
+  }
+#undef SK_LOAD
+  // acc[r] <-> token (r/4)*8 + (lane/32)*4 + r%4, row rt*128 + w*32 + lane%32
+  const int n = rt * 128 + w * 32 + (lane & 31);
+  if (n >= s.N) return;
+  float* pp = s.part + (int64_t)ks * 32 * s.N + n;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int t = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+    if (t < T) pp[(int64_t)t * s.N] = acc[r];
+  }
+}
+
+template <int EPI, typename KvT>
+__global__ void __launch_bounds__(256) skinny_epilogue_kernel(SkinnyArgs s) {
+  const LinearArgs& a = s.a;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int T = a.T;
+  auto total = [&](int t, int n) {
+    float y = 0.f;
+    for (int ks = 0; ks < s.ksplit; ++ks) y += s.part[((int64_t)ks * 32 + t) * s.N + n];
+    return y;
+  };
+  if (EPI == EPI_SWIGLU) {
+    const int F = a.n0;
+    if (i >= (int64_t)T * F) return;
+    const int t = (int)(i / F), f = (int)(i % F);
+    const float v = silu(total(t, f)) * total(t, F + f);
+    const int64_t o = (int64_t)t * a.ldo + f;
+    if (a.out) a.out[o] = v;
+    if (a.out_hi) split_bf16(v, a.out_hi[o], a.out_lo[o]);
+    return;
+  }
+  // other epilogues: one thread per adjacent column pair (a RoPE pair)
+  const int NP = (s.N + 1) / 2;
+  if (i >= (int64_t)T * NP) return;
+  const int t = (int)(i / NP), n = 2 * (int)(i % NP);
+  const float y0 = total(t, n);
+  const float y1 = n + 1 < s.N ? total(t, n + 1) : 0.f;
+  if (EPI == EPI_STORE) {
+    a.out[(int64_t)t * a.ldo + n] = y0;
+    if (n + 1 < s.N) a.out[(int64_t)t * a.ldo + n + 1] = y1;
+  } else if (EPI == EPI_RESIDUAL) {
+    float* xo = a.out + (int64_t)t * a.ldo;
+    xo[n] += y0;
+    if (n + 1 < s.N) xo[n + 1] += y1;
+  } else if (EPI == EPI_QKV) {
+    const int hd = a.head_dim;
+    if (n < a.n0 + a.n1) {
+      const int lr = n < a.n0 ? n : n - a.n0;
+      const int pi = (lr % hd) >> 1;
+      const float2 cs = a.rope_cs[(int64_t)t * (hd >> 1) + pi];
+      const float z0 = y0 * cs.x - y1 * cs.y, z1 = y0 * cs.y + y1 * cs.x;
+      if (n < a.n0) {
+        a.q_out[(int64_t)t * a.n0 + lr] = z0;
+        a.q_out[(int64_t)t * a.n0 + lr + 1] = z1;
+      } else {
+        const int64_t ci = ((int64_t)(lr / hd) * a.n_ctx + a.slots[t]) * hd + (lr % hd);
+        KvStore<KvT>::store((typename KvStore<KvT>::T*)a.k_cache, ci, z0);
+        KvStore<KvT>::store((typename KvStore<KvT>::T*)a.k_cache, ci + 1, z1);
+      }
+    } else {
+      const int lr = n - a.n0 - a.n1;
+      const int64_t ci = ((int64_t)(lr / hd) * a.n_ctx + a.slots[t]) * hd + (lr % hd);
+      KvStore<KvT>::store((typename KvStore<KvT>::T*)a.v_cache, ci, y0);
+      if (n + 1 < s.N) KvStore<KvT>::store((typename KvStore<KvT>::T*)a.v_cache, ci + 1, y1);
+    }
+  }
+}
+
+bool skinny_supported(const LinearArgs& a) {
+  const int N = a.epi == EPI_SWIGLU ? 2 * a.n0 : a.n0 + a.n1 + a.n2;
+  return a.weight_bf16 && a.act_hi && a.act_lo && a.T > 0 && a.T <= 32 && a.K % kSkChunk == 0 &&
+         (int64_t)N * 32 <= kSkinnyPartFloats && (a.epi != EPI_QKV || (a.n0 % 2 == 0 && a.n1 % 2 == 0));
+}
+
+hipError_t launch_linear_skinny(const LinearArgs& a, float* part, hipStream_t st) {
+  if (!skinny_supported(a)) return hipErrorInvalidValue;
+  SkinnyArgs s;
+  s.a = a;
+  s.N = a.epi == EPI_SWIGLU ? 2 * a.n0 : a.n0 + a.n1 + a.n2;
+  s.part = part;
+  // K slices: enough blocks to fill the chip (>= 512), each slice a whole
+  // number of 128-wide chunks, within the workspace
+  const int nrt = (s.N + 127) / 128;
+  const int chunks = a.K / kSkChunk;
+  int ks = 1;
+  while (nrt * ks < 512 && ks * 2 <= chunks && (int64_t)s.N * 32 * ks * 2 <= kSkinnyPartFloats) ks *= 2;
+  s.kslice = ((chunks + ks - 1) / ks) * kSkChunk;
+  s.ksplit = (a.K + s.kslice - 1) / s.kslice;
+  if (a.epi == EPI_SWIGLU)
+    skinny_kernel<true><<<nrt * s.ksplit, 256, 0, st>>>(s);
+  else
+    skinny_kernel<false><<<nrt * s.ksplit, 256, 0, st>>>(s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n_thr = a.epi == EPI_SWIGLU ? (int64_t)a.T * a.n0 : (int64_t)a.T * ((s.N + 1) / 2);
+  const unsigned blocks = (unsigned)((n_thr + 255) / 256);
+  switch (a.epi) {
+    case EPI_STORE: skinny_epilogue_kernel<EPI_STORE, float><<<blocks, 256, 0, st>>>(s); break;
+    case EPI_RESIDUAL: skinny_epilogue_kernel<EPI_RESIDUAL, float><<<blocks, 256, 0, st>>>(s); break;
+    case EPI_SWIGLU: skinny_epilogue_kernel<EPI_SWIGLU, float><<<blocks, 256, 0, st>>>(s); break;
+    case EPI_QKV:
+      if (a.kv_dtype == TDF_BF16) skinny_epilogue_kernel<EPI_QKV, kv_bf16><<<blocks, 256, 0, st>>>(s);
+      else if (a.kv_dtype == TDF_F16) skinny_epilogue_kernel<EPI_QKV, kv_f16><<<blocks, 256, 0, st>>>(s);
+      else skinny_epilogue_kernel<EPI_QKV, float><<<blocks, 256, 0, st>>>(s);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tdf

@@ -62,6 +62,12 @@ struct LinearArgs {
 hipError_t launch_linear_gemv(const LinearArgs& a, hipStream_t s);
 hipError_t launch_linear_gemm(const LinearArgs& a, hipStream_t s);
 bool gemm_supported(const LinearArgs& a);
+// 9..32 tokens on the matrix cores with the weights streamed once (split
+// over K into the float32 workspace `part` of kSkinnyPartFloats floats,
+// then an epilogue pass); bf16 weights, hi/lo activations, K % 128 == 0
+constexpr int64_t kSkinnyPartFloats = 32ll * 65536;
+bool skinny_supported(const LinearArgs& a);
+hipError_t launch_linear_skinny(const LinearArgs& a, float* part, hipStream_t s);
 
 // x[t][:] = E[token[t]][:] (to float32); with g set also u = g * x and
 // ssp[t * stride] = sum x^2 (one partial per row)

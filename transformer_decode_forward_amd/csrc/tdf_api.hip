@@ -115,6 +115,7 @@ struct tdf_context {
   char* ints_host = nullptr;        // pinned staging
   float* logits = nullptr;          // [cap][V]
   int32_t* d_tok = nullptr;         // [cap]
+  float* skinny_part = nullptr;     // K-split partials of the 9..32-token linear layers
   float* amax_v = nullptr;          // [cap][argmax_splits(V)] partial maxima
   int32_t* amax_i = nullptr;        // [cap][argmax_splits(V)] their indices
   int32_t* h_tok = nullptr;         // pinned [cap]
@@ -381,6 +382,7 @@ extern "C" tdf_context* tdf_context_create(const tdf_model* m, const tdf_context
                           (size_t)U * H * kChunkCapPrefill);
   A((void**)&c->part_acc, c->part_rows * hd * 4);
   A((void**)&c->part_ml, c->part_rows * 2 * 4);
+  if (U > kGemvMaxT) A((void**)&c->skinny_part, (size_t)kSkinnyPartFloats * 4);
   // per-call integers: 5 int32 per token + selected rows, then int64 list writes
   c->ints_bytes = staging_i64_base(c->n_batch, c->n_ubatch, c->n_seq_max) +
                   (size_t)2 * c->n_batch * c->n_seq_max * 8;
@@ -437,7 +439,13 @@ struct UbatchDev {
 
 static int run_linear(tdf_context* c, LinearArgs& a, bool mfma, int op) {
   const int slot = prof_begin(c, op, mfma);
-  hipError_t e = mfma ? launch_linear_gemm(a, c->stream) : launch_linear_gemv(a, c->stream);
+  hipError_t e;
+  if (!mfma)
+    e = launch_linear_gemv(a, c->stream);
+  else if (a.T <= kDecodeMaxT && c->skinny_part && skinny_supported(a))
+    e = launch_linear_skinny(a, c->skinny_part, c->stream);
+  else
+    e = launch_linear_gemm(a, c->stream);
   prof_end(c, slot);
   if (e != hipSuccess) {
     set_err(std::string("linear launch failed: ") + hipGetErrorString(e));
