@@ -707,6 +707,7 @@ hipError_t launch_linear_gemv(const LinearArgs& a, hipStream_t s) {
 // Partials of several chunks are merged by attn_merge_kernel.
 
 constexpr int kTile = 64;
+constexpr int kCellStage = 1024;  // cell indices a block stages in LDS
 
 // 16 bytes of cache elements -> floats
 template <typename KvT> __device__ __forceinline__ void unpack16(uint4 u, float* out);
@@ -770,10 +771,25 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
   // Loads come from clamped addresses, unconditionally: a load under a
   // divergent branch makes the compiler wait for every load in flight.  The
   // first tile's cell indices are requested together with q.
+  // A chunk of several tiles stages its cell indices in LDS first (one
+  // round trip), so that each next tile's K/V requests need no index load.
+  __shared__ int32_t cell_s[kCellStage];
+  const int span = c_hi - c_lo;
+  const bool staged = span > TILE && span <= kCellStage;  // block-uniform
+  if (staged) {
+#pragma unroll
+    for (int i = 0; i < kCellStage / 256; ++i) {
+      const int e = tid + i * 256;
+      const int32_t v = cells[c_lo + min(e, span - 1)];
+      if (e < span) cell_s[e] = v;
+    }
+  }
   int row[PPER];
   uint4 kr[PPER], vr[PPER];
+  if (!staged) {
 #pragma unroll
-  for (int pi = 0; pi < PPER; ++pi) row[pi] = cells[min(c_lo + r0 + pi * ROWS, c_hi - 1)];
+    for (int pi = 0; pi < PPER; ++pi) row[pi] = cells[min(c_lo + r0 + pi * ROWS, c_hi - 1)];
+  }
   float qr[G][E];
   {
     const float scale = rsqrtf((float)HD);
@@ -786,6 +802,11 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
         qr[h][e] = v.x * scale; qr[h][e + 1] = v.y * scale;
         qr[h][e + 2] = v.z * scale; qr[h][e + 3] = v.w * scale;
       }
+  }
+  if (staged) {
+    __syncthreads();
+#pragma unroll
+    for (int pi = 0; pi < PPER; ++pi) row[pi] = cell_s[min(r0 + pi * ROWS, span - 1)];
   }
 #pragma unroll
   for (int pi = 0; pi < PPER; ++pi) {
@@ -813,7 +834,10 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
     }
     if (c0 + TILE < c_hi) {  // block-uniform: request the next tile
 #pragma unroll
-      for (int pi = 0; pi < PPER; ++pi) row[pi] = cells[min(c0 + TILE + r0 + pi * ROWS, c_hi - 1)];
+      for (int pi = 0; pi < PPER; ++pi) {
+        const int e = min(c0 + TILE + r0 + pi * ROWS, c_hi - 1);
+        row[pi] = staged ? cell_s[e - c_lo] : cells[e];
+      }
 #pragma unroll
       for (int pi = 0; pi < PPER; ++pi) {
         const int64_t off = (int64_t)row[pi] * HD + dq;
