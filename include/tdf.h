@@ -218,6 +218,17 @@ typedef struct {
 } tdf_sampling;
 int32_t tdf_sample(tdf_context *c, const tdf_sampling *p, const float *u, int32_t *tokens);
 
+/* The same chain (or greedy argmax) on the caller's logits: n_rows rows of
+ * n_vocab float32 values at the DEVICE pointer logits (row-major, rows
+ * n_vocab apart, read only), e.g. rows the caller edited after tdf_decode.
+ * Runs on the context's stream and synchronises it; u and tokens are HOST
+ * arrays of n_rows entries as for tdf_sample.  The context keeps small
+ * buffers for the rows' draws and tokens, grown on demand.  Returns TDF_OK,
+ * TDF_E_INVALID (bad arguments or parameters; nothing written), TDF_E_ALLOC
+ * or TDF_E_DEVICE. */
+int32_t tdf_sample_logits(tdf_context *c, const float *logits, int32_t n_rows, int32_t n_vocab,
+                          const tdf_sampling *p, const float *u, int32_t *tokens);
+
 /* Sliding the context window (Ollama engine page, "KV Cache: memory for
  * causal attention": when the cache is full, the model's shift function
  * re-encodes the RoPE positions of the cached keys and the window moves

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs shared by the CPU oracle and the GPU path's tests.
 
-This module only makes numbers: weights, prompts, lengths and cache fills,
-each a pure function of (seed, tensor name, element index).  It holds no step
+This module only makes numbers: weights, prompts, lengths, cache fills and
+logits rows, each a pure function of (seed, name, element index).  It holds no step
 of the decoder forward pass.  The generator itself is C (``synth.c``) so that
 an 8B- or 70B-shaped model can be produced in seconds with OpenMP; this file
 loads it with ctypes and wraps it in numpy.
@@ -238,3 +238,27 @@ def kv_fill(cfg: dict, layer: int, which: str, pos0: int, pos1: int, dtype: str)
     n = (pos1 - pos0) * Hkv * hd
     vals = normal(cfg["seed"], f"kvfill.{which}.{layer}", n, 1.0, dtype, first=pos0 * Hkv * hd)
     return vals.reshape(pos1 - pos0, Hkv, hd)
+
+
+def logit_rows(seed: int, kind: str, n_rows: int, n_vocab: int) -> np.ndarray:
+    """float32 rows of synthetic logits [n_rows][n_vocab] with a chosen
+    structure: "normal" N(0, 2); "coarse" N(0, 1) rounded to whole numbers
+    (large groups of equal values); "comb" N(0, 1) with 10 + N(0, 1) at the
+    evenly spaced ids floor(t * n_vocab / 1024), t < 1024; "masked" N(0, 2)
+    with every other id set to -inf."""
+    n = n_rows * n_vocab
+    z = normal(seed, f"logits.{kind}", n, 1.0).astype(np.float64).reshape(n_rows, n_vocab)
+    if kind == "normal":
+        out = 2.0 * z
+    elif kind == "coarse":
+        out = np.rint(z)
+    elif kind == "comb":
+        out = z.copy()
+        ids = (np.arange(1024, dtype=np.int64) * n_vocab) // 1024
+        out[:, ids] = 10.0 + normal(seed, "logits.comb.peaks", n_rows * ids.size, 1.0).reshape(n_rows, -1)
+    elif kind == "masked":
+        out = 2.0 * z
+        out[:, 1::2] = -np.inf
+    else:
+        raise ValueError(kind)
+    return out.astype(np.float32)

@@ -67,3 +67,60 @@ def test_sampling_rejects_bad_parameters():
                  (1.0, 40, 1.0, 0.0, [1.0])):
         rc, _ = gc.sample(*args[:4], u=args[4])
         assert rc == tdf.TDF_E_INVALID
+
+
+def _run_rows(kind, n_vocab, params, n_rows=3, seed=5):
+    """tdf_sample_logits on synthetic rows of a given structure against the
+    oracle's chain, token by token, where the decisions are clear."""
+    import transformer_decode_forward_amd as tdf
+    from transformer_decode_forward_amd.device import to_device
+    cfg, w = make_weights(SMALL)
+    gc = tdf.Context(device_model(cfg, w), n_ctx=64, kv_dtype="bf16")
+    rows = tdf_synth.logit_rows(seed, kind, n_rows, n_vocab)
+    d = to_device(rows)
+    rc, greedy = gc.sample_logits(d.data_ptr(), n_rows, n_vocab, 0.0)
+    assert rc == 0 and greedy == [int(np.argmax(r)) for r in rows]
+    rng = np.random.default_rng(11)
+    compared = total = 0
+    for (t, k, p, mp) in params:
+        for rep in range(4):
+            u = rng.random(n_rows).astype(np.float32)
+            rc, got = gc.sample_logits(d.data_ptr(), n_rows, n_vocab, t, k, p, mp, u)
+            assert rc == 0, tdf.tdf_last_error()
+            for i in range(n_rows):
+                z = rows[i].astype(np.float64)
+                total += 1
+                if sample_margin(z, t, k, p, mp, float(u[i])) <= MARGIN:
+                    continue
+                compared += 1
+                want = sample(z, t, k, p, mp, float(u[i]))
+                assert got[i] == want, (kind, n_vocab, t, k, p, mp, float(u[i]), i, got[i], want)
+    assert compared >= 0.6 * total, (compared, total)
+
+
+ROW_PARAMS = [(1.0, 1024, 1.0, 0.0), (0.8, 40, 0.9, 0.05), (1.0, 1, 1.0, 0.0), (3.0, 500, 0.98, 0.0)]
+
+
+@pytest.mark.parametrize("kind,n_vocab", [("normal", 128256), ("normal", 5000), ("normal", 8193),
+                                          ("masked", 128256), ("coarse", 128256), ("comb", 128256),
+                                          ("coarse", 3000)])
+def test_sampling_structured_rows(kind, n_vocab):
+    """Rows that take every path of the Top-K gather: whole rows that fit the
+    candidate list (5000, 3000), the sampled threshold (normal, masked, just
+    above the list size), heavy ties that overflow it or tie at the K-th place
+    (coarse: whole-number logits), and a comb of large values on evenly spaced
+    ids that a strided sample sees all of, so the gather falls short of K."""
+    _run_rows(kind, n_vocab, ROW_PARAMS)
+
+
+def test_sample_logits_rejects_bad_arguments():
+    import transformer_decode_forward_amd as tdf
+    from transformer_decode_forward_amd.device import to_device
+    cfg, w = make_weights(SMALL)
+    gc = tdf.Context(device_model(cfg, w), n_ctx=64, kv_dtype="bf16")
+    d = to_device(tdf_synth.logit_rows(1, "normal", 2, 100))
+    assert gc.sample_logits(d.data_ptr(), 2, 0, 1.0, 10, 1.0, 0.0, [0.5, 0.5])[0] == tdf.TDF_E_INVALID
+    assert gc.sample_logits(d.data_ptr(), -1, 100, 1.0, 10, 1.0, 0.0, [0.5])[0] == tdf.TDF_E_INVALID
+    assert gc.sample_logits(d.data_ptr(), 2, 100, 1.0, 0, 1.0, 0.0, [0.5, 0.5])[0] == tdf.TDF_E_INVALID
+    assert gc.sample_logits(0, 2, 100, 1.0, 10, 1.0, 0.0, [0.5, 0.5])[0] == tdf.TDF_E_INVALID
+    assert gc.sample_logits(d.data_ptr(), 0, 100, 1.0, 10)[0] == tdf.TDF_OK

@@ -93,6 +93,8 @@ def lib():
             "tdf_time_op": (_i32, [_vp, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_double)]),
             "tdf_kv_seq_rm": (_i32, [_vp, _i32, _i32, _i32]),
             "tdf_sample": (_i32, [_vp, ctypes.POINTER(tdf_sampling), ctypes.POINTER(_f32), ctypes.POINTER(_i32)]),
+            "tdf_sample_logits": (_i32, [_vp, ctypes.c_void_p, _i32, _i32, ctypes.POINTER(tdf_sampling),
+                                         ctypes.POINTER(_f32), ctypes.POINTER(_i32)]),
             "tdf_kv_seq_shift": (_i32, [_vp, _i32, _i32, _i32, _i32]),
             "tdf_last_error": (ctypes.c_char_p, []),
         }
@@ -321,6 +323,18 @@ class Context:
         out = (_i32 * max(1, n))()
         p = tdf_sampling(float(temperature), int(top_k), float(top_p), float(min_p))
         rc = lib().tdf_sample(self.handle, ctypes.byref(p), ua, out)
+        return rc, list(out)[:n]
+
+    def sample_logits(self, logits_ptr: int, n_rows: int, n_vocab: int, temperature: float, top_k: int = 40,
+                      top_p: float = 1.0, min_p: float = 0.0, u: Optional[Sequence[float]] = None):
+        """The same chain on n_rows rows of n_vocab float32 logits at the
+        device address logits_ptr (tdf_sample_logits).  Returns (rc, tokens)."""
+        n = int(n_rows)
+        ua = (_f32 * max(1, n))(*([0.0] * n if u is None else [float(x) for x in u]))
+        out = (_i32 * max(1, n))()
+        p = tdf_sampling(float(temperature), int(top_k), float(top_p), float(min_p))
+        rc = lib().tdf_sample_logits(self.handle, ctypes.c_void_p(int(logits_ptr)), n, int(n_vocab),
+                                     ctypes.byref(p), ua, out)
         return rc, list(out)[:n]
 
     def kv_seq_rm(self, seq: int, p0: int, p1: int) -> int:

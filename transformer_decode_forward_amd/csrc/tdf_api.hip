@@ -120,6 +120,13 @@ struct tdf_context {
   int32_t* amax_i = nullptr;        // [cap][argmax_splits(V)] their indices
   int32_t* h_tok = nullptr;         // pinned [cap]
   int logits_cap = 0;
+  // tdf_sample_logits buffers (caller's rows), grown on demand
+  float* ext_u = nullptr;           // [ext_rows]
+  int32_t* ext_tok = nullptr;       // [ext_rows]
+  int32_t* ext_htok = nullptr;      // pinned [ext_rows]
+  float* ext_pv = nullptr;          // [ext_parts] argmax partials
+  int32_t* ext_pi = nullptr;
+  size_t ext_rows = 0, ext_parts = 0;
   std::vector<void*> owned;
 
   // TDF_CTX_PROFILE: event pairs of the current call, totals per (op, path)
@@ -164,6 +171,13 @@ static int ctx_alloc(tdf_context* c, void** p, size_t bytes) {
   }
   c->owned.push_back(*p);
   return TDF_OK;
+}
+
+static void ctx_free(tdf_context* c, void* p) {
+  if (!p) return;
+  auto it = std::find(c->owned.begin(), c->owned.end(), p);
+  if (it != c->owned.end()) c->owned.erase(it);
+  (void)hipFree(p);
 }
 
 // ---- profiling (TDF_CTX_PROFILE) ----
@@ -215,8 +229,10 @@ static void ctx_release(tdf_context* c) {
   c->owned.clear();
   if (c->ints_host) (void)hipHostFree(c->ints_host);
   if (c->h_tok) (void)hipHostFree(c->h_tok);
+  if (c->ext_htok) (void)hipHostFree(c->ext_htok);
   c->ints_host = nullptr;
   c->h_tok = nullptr;
+  c->ext_htok = nullptr;
   if (c->own_stream && c->stream) (void)hipStreamDestroy(c->stream);
   c->stream = nullptr;
 }
@@ -1022,6 +1038,43 @@ extern "C" int32_t tdf_kv_import(tdf_context* c, int32_t s, int32_t pos0, int32_
   return TDF_OK;
 }
 
+static int check_sampling(const tdf_sampling* p, const float* u, int R, const char* who) {
+  if (!(p->temperature > 0.f)) return TDF_OK;  // greedy: the other fields are ignored
+  if (!u || p->top_k < 1 || p->top_k > kMaxTopK || !(p->min_p >= 0.f && p->min_p <= 1.f) ||
+      !(p->top_p == p->top_p) || !std::isfinite(p->temperature)) {
+    set_err(std::string(who) + ": invalid sampling parameters");
+    return TDF_E_INVALID;
+  }
+  for (int i = 0; i < R; ++i)
+    if (!(u[i] >= 0.f && u[i] < 1.f)) {
+      set_err(std::string(who) + ": u must lie in [0, 1)");
+      return TDF_E_INVALID;
+    }
+  return TDF_OK;
+}
+
+// greedy (argmax) or the sampling chain over R rows of V logits at the
+// device pointer lg; d_u, d_tok, pv, pi, h_tok are the context's buffers for
+// that many rows
+static int sample_rows(tdf_context* c, const float* lg, int R, int V, const tdf_sampling* p, const float* u,
+                       int32_t* tokens, float* d_u, int32_t* d_tok, float* pv, int32_t* pi, int32_t* h_tok) {
+  if (!(p->temperature > 0.f)) {
+    TDF_HIP(launch_argmax(lg, R, V, d_tok, pv, pi, c->stream));
+  } else {
+    TDF_HIP(hipMemcpyAsync(d_u, u, (size_t)R * 4, hipMemcpyHostToDevice, c->stream));
+    SampleParams sp;
+    sp.temperature = p->temperature;
+    sp.top_k = p->top_k;
+    sp.top_p = p->top_p;
+    sp.min_p = p->min_p;
+    TDF_HIP(launch_sample(lg, R, V, sp, d_u, d_tok, c->stream));
+  }
+  TDF_HIP(hipMemcpyAsync(h_tok, d_tok, (size_t)R * 4, hipMemcpyDeviceToHost, c->stream));
+  TDF_HIP(hipStreamSynchronize(c->stream));
+  memcpy(tokens, h_tok, (size_t)R * 4);
+  return TDF_OK;
+}
+
 extern "C" int32_t tdf_sample(tdf_context* c, const tdf_sampling* p, const float* u, int32_t* tokens) {
   if (!c || !p || !tokens || c->dry_run) {
     set_err("tdf_sample: invalid arguments");
@@ -1029,35 +1082,48 @@ extern "C" int32_t tdf_sample(tdf_context* c, const tdf_sampling* p, const float
   }
   const int R = c->n_outputs, V = c->m->hp.n_vocab;
   if (R == 0) return TDF_OK;
-  const bool greedy = !(p->temperature > 0.f);
-  if (!greedy) {
-    if (!u || p->top_k < 1 || p->top_k > kMaxTopK || !(p->min_p >= 0.f && p->min_p <= 1.f) ||
-        !(p->top_p == p->top_p) || !std::isfinite(p->temperature)) {
-      set_err("tdf_sample: invalid sampling parameters");
-      return TDF_E_INVALID;
+  if (int rc = check_sampling(p, u, R, "tdf_sample")) return rc;
+  // u goes through the argmax partials buffer (>= R floats)
+  return sample_rows(c, c->logits, R, V, p, u, tokens, c->amax_v, c->d_tok, c->amax_v, c->amax_i, c->h_tok);
+}
+
+extern "C" int32_t tdf_sample_logits(tdf_context* c, const float* logits, int32_t n_rows, int32_t n_vocab,
+                                     const tdf_sampling* p, const float* u, int32_t* tokens) {
+  if (!c || !p || !tokens || c->dry_run || !logits || n_rows < 0 || n_vocab < 1) {
+    set_err("tdf_sample_logits: invalid arguments");
+    return TDF_E_INVALID;
+  }
+  if (n_rows == 0) return TDF_OK;
+  if (int rc = check_sampling(p, u, n_rows, "tdf_sample_logits")) return rc;
+  const size_t parts = (size_t)n_rows * argmax_splits(n_vocab);
+  if ((size_t)n_rows > c->ext_rows) {
+    void *du = nullptr, *dt = nullptr, *ht = nullptr;
+    if (int rc = ctx_alloc(c, &du, (size_t)n_rows * 4)) return rc;
+    if (int rc = ctx_alloc(c, &dt, (size_t)n_rows * 4)) return rc;
+    if (hipHostMalloc(&ht, (size_t)n_rows * 4, hipHostMallocDefault) != hipSuccess) {
+      set_err("tdf_sample_logits: pinned allocation failed");
+      return TDF_E_ALLOC;
     }
-    for (int i = 0; i < R; ++i)
-      if (!(u[i] >= 0.f && u[i] < 1.f)) {
-        set_err("tdf_sample: u must lie in [0, 1)");
-        return TDF_E_INVALID;
-      }
+    if (c->ext_htok) (void)hipHostFree(c->ext_htok);
+    ctx_free(c, c->ext_u);  // the previous call synchronised the stream
+    ctx_free(c, c->ext_tok);
+    c->ext_u = (float*)du;
+    c->ext_tok = (int32_t*)dt;
+    c->ext_htok = (int32_t*)ht;
+    c->ext_rows = (size_t)n_rows;
   }
-  if (greedy) {
-    TDF_HIP(launch_argmax(c->logits, R, V, c->d_tok, c->amax_v, c->amax_i, c->stream));
-  } else {
-    // u goes through the argmax partials buffer (>= R floats)
-    TDF_HIP(hipMemcpyAsync(c->amax_v, u, (size_t)R * 4, hipMemcpyHostToDevice, c->stream));
-    SampleParams sp;
-    sp.temperature = p->temperature;
-    sp.top_k = p->top_k;
-    sp.top_p = p->top_p;
-    sp.min_p = p->min_p;
-    TDF_HIP(launch_sample(c->logits, R, V, sp, c->amax_v, c->d_tok, c->stream));
+  if (parts > c->ext_parts) {
+    void *pv = nullptr, *pi = nullptr;
+    if (int rc = ctx_alloc(c, &pv, parts * 4)) return rc;
+    if (int rc = ctx_alloc(c, &pi, parts * 4)) return rc;
+    ctx_free(c, c->ext_pv);
+    ctx_free(c, c->ext_pi);
+    c->ext_pv = (float*)pv;
+    c->ext_pi = (int32_t*)pi;
+    c->ext_parts = parts;
   }
-  TDF_HIP(hipMemcpyAsync(c->h_tok, c->d_tok, (size_t)R * 4, hipMemcpyDeviceToHost, c->stream));
-  TDF_HIP(hipStreamSynchronize(c->stream));
-  memcpy(tokens, c->h_tok, (size_t)R * 4);
-  return TDF_OK;
+  return sample_rows(c, logits, n_rows, n_vocab, p, u, tokens, c->ext_u, c->ext_tok, c->ext_pv, c->ext_pi,
+                     c->ext_htok);
 }
 
 extern "C" int32_t tdf_kv_seq_rm(tdf_context* c, int32_t seq, int32_t p0, int32_t p1) {
