@@ -11,6 +11,7 @@
 // GEMV streams each weight row once with 16-byte loads per lane and keeps the
 // activations in float32.
 #include <algorithm>
+#include <type_traits>
 
 #include "k_common.hpp"
 #include "kernels.hpp"
@@ -707,7 +708,7 @@ hipError_t launch_linear_gemv(const LinearArgs& a, hipStream_t s) {
 // Partials of several chunks are merged by attn_merge_kernel.
 
 constexpr int kTile = 64;
-constexpr int kCellStage = 1024;  // cell indices a block stages in LDS
+constexpr int kCellStage = kDecodeCellStage;  // cell indices a block stages in LDS
 
 // 16 bytes of cache elements -> floats
 template <typename KvT> __device__ __forceinline__ void unpack16(uint4 u, float* out);
@@ -968,6 +969,324 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
   }
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+// ---------------------------------------------------------------------------
+// Decode attention with the scores on the matrix cores (16-bit caches, head
+// dimension 64 or 128).  Block (chunk j, kv head g, token t) as above; each
+// wave takes every fourth 16-cell tile of the chunk.  Scores: the G query
+// heads (rows of a 16-row operand, the rest zero) times the tile's keys as
+// the 32-deep columns of v_mfma_f32_16x16x32, with the query split into a
+// 16-bit high part and a 16-bit remainder (two products per 32 dimensions),
+// so the scores keep about 16 significant bits of the query; the keys enter
+// exactly as stored.  The products leave head h of cell c in lane c + 16 (h / 4),
+// component h % 4: row reductions over 16 lanes give each head's tile
+// maximum and sum.  Probabilities go through 1 KB of LDS per wave to the
+// lanes that own V: each lane keeps 8 dimensions of the output for every
+// head and adds p * V over the cells of its row group (vector units, float32).
+// Per-wave running maxima and sums are wave-uniform, so the row groups of a
+// wave combine without rescaling; the four waves combine through LDS.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+template <typename KvT> struct Mfma16;
+template <> struct Mfma16<kv_bf16> {
+  typedef bf16x8 vec;
+  typedef __bf16 elem;
+  typedef s16x4 vec4;  // 4 bf16 bit patterns
+  __device__ __forceinline__ static f32x4 mma(vec a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4 mma4(vec4 a, vec4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+  // x ~= hi + lo, both as stored 16-bit patterns
+  __device__ __forceinline__ static void split(float x, short& hi, short& lo) {
+    const __bf16 h = (__bf16)x;
+    hi = __builtin_bit_cast(short, h);
+    lo = __builtin_bit_cast(short, (__bf16)(x - (float)h));
+  }
+};
+template <> struct Mfma16<kv_f16> {
+  typedef f16x8 vec;
+  typedef _Float16 elem;
+  typedef f16x4 vec4;
+  __device__ __forceinline__ static f32x4 mma(vec a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static f32x4 mma4(vec4 a, vec4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+  __device__ __forceinline__ static void split(float x, short& hi, short& lo) {
+    const _Float16 h = (_Float16)x;
+    hi = __builtin_bit_cast(short, h);
+    lo = __builtin_bit_cast(short, (_Float16)(x - (float)h));
+  }
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, -INFINITY),
+                                                                      __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false)));
+}
+// max / sum over each row of 16 lanes, every lane of the row receiving it
+__device__ __forceinline__ float row16_max(float v) {
+  v = dpp_max<0xB1>(v);
+  v = dpp_max<0x4E>(v);
+  v = dpp_max<0x141>(v);
+  return dpp_max<0x140>(v);
+}
+__device__ __forceinline__ float row16_sum(float v) { return group_sum<16>(v); }
+
+template <typename KvT, int HD, int G>
+__global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
+  typedef Mfma16<KvT> M;
+  typedef typename M::vec vec;
+  typedef typename M::elem elem;
+  typedef typename M::vec4 vec4;
+  typedef typename KvStore<KvT>::T ST;
+  static_assert(HD == 64 || HD == 128, "head_dim 64 or 128");
+  static_assert(G >= 1 && G <= 8, "at most 8 query heads per kv head");
+  constexpr int NKC = HD / 32;   // 32-deep slices of the head dimension (scores)
+  constexpr int NN = HD / 16;    // 16-wide output column blocks (P V)
+  constexpr int PR = HD / 8;     // V loads: lanes per row (8 dimensions each)
+  constexpr int RG = 64 / PR;    // V loads: row groups per wave
+  constexpr int CPL = 16 / RG;   // V loads: cells of a tile per lane
+  constexpr int VP = HD + 4;     // V tile row pitch in LDS (elements; breaks bank conflicts)
+  __shared__ int32_t cell_s[kCellStage];
+  __shared__ short v_s[4][16 * VP];
+  __shared__ float pt_s[4][G][16];
+  __shared__ float acc_s[4][G][HD];
+  __shared__ float m_s[4][G], l_s[4][G];
+
+  const int j = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nvis = a.n_vis[t];
+  const int c_lo = j * a.chunk;
+  if (c_lo >= nvis) return;
+  const int c_hi = min(nvis, c_lo + a.chunk);
+  const int span = c_hi - c_lo;  // <= kCellStage (checked at launch)
+  const int ntiles = (span + 15) >> 4;
+  const int32_t* cells = a.cell_list + a.list_off[t];
+  const ST* kc = (const ST*)a.k_cache + (int64_t)g * a.n_ctx * HD;
+  const ST* vc = (const ST*)a.v_cache + (int64_t)g * a.n_ctx * HD;
+  for (int e = tid; e < kCellStage; e += 256) {
+    const int32_t v = cells[c_lo + min(e, span - 1)];
+    cell_s[e] = v;  // entries past the span repeat its last cell
+  }
+  // query operand: lane l holds head l % 16 (zero past G), dimensions
+  // 32 kk + 8 (l / 16) .. + 8, scaled by 1/sqrt(HD), as a high part and the
+  // remainder
+  vec qh[NKC], ql[NKC];
+  {
+    const int hq = lane & 15;
+    const float scale = rsqrtf((float)HD);
+    const float* qp = a.q + ((int64_t)t * a.H + g * G + min(hq, G - 1)) * HD + (lane >> 4) * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKC; ++kk) {
+      const float4 x0 = *(const float4*)(qp + kk * 32), x1 = *(const float4*)(qp + kk * 32 + 4);
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = hq < G ? x[e] * scale : 0.f;
+        const elem h = (elem)v;
+        qh[kk][e] = h;
+        ql[kk][e] = (elem)(v - (float)h);
+      }
+    }
+  }
+  __syncthreads();
+
+  const int rg = lane / PR, pc = lane % PR;  // V loads: row group, 8-dimension piece
+  const int hrow = (lane >> 4) * 4;          // heads hrow .. hrow + 3 in the score layout
+  // Reference maxima per head (wave-uniform): probabilities are exp(s - m),
+  // and m moves only when a score exceeds it by more than kSlack, so the
+  // accumulators are rarely rescaled; p stays below e^kSlack.
+  constexpr float kSlack = 8.f;
+  float m_w[G];
+  f32x4 acc[NN], acc_l;
+#pragma unroll
+  for (int h = 0; h < G; ++h) m_w[h] = -INFINITY;
+#pragma unroll
+  for (int n = 0; n < NN; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  acc_l = f32x4{0.f, 0.f, 0.f, 0.f};
+  vec4 ones;
+  {
+    short one_hi, one_lo;
+    M::split(1.f, one_hi, one_lo);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ones[q] = __builtin_bit_cast(typename std::remove_reference<decltype(ones[0])>::type, one_hi);
+  }
+  short* vw = v_s[wv];
+  auto cell_of = [&](int tl, int r) { return cell_s[min(tl * 16 + r, span - 1)]; };
+  vec kn[NKC];
+  uint4 vn[CPL];
+  int tl = wv;
+  {
+    const int ck = cell_of(tl, lane & 15);
+#pragma unroll
+    for (int kk = 0; kk < NKC; ++kk) kn[kk] = *(const vec*)(kc + (int64_t)ck * HD + kk * 32 + (lane >> 4) * 8);
+#pragma unroll
+    for (int pi = 0; pi < CPL; ++pi) vn[pi] = *(const uint4*)(vc + (int64_t)cell_of(tl, rg * CPL + pi) * HD + pc * 8);
+  }
+  for (; tl < ntiles; tl += 4) {
+    const int nt = min(tl + 4, ntiles - 1);  // next tile of this wave (clamped)
+    // this tile's V rows into the wave's LDS tile (rows of VP elements), then
+    // the next tile's V requested into the same registers
+#pragma unroll
+    for (int pi = 0; pi < CPL; ++pi) {
+      uint2* dst = (uint2*)(vw + (rg * CPL + pi) * VP + pc * 8);
+      dst[0] = make_uint2(vn[pi].x, vn[pi].y);
+      dst[1] = make_uint2(vn[pi].z, vn[pi].w);
+    }
+#pragma unroll
+    for (int pi = 0; pi < CPL; ++pi) vn[pi] = *(const uint4*)(vc + (int64_t)cell_of(nt, rg * CPL + pi) * HD + pc * 8);
+    // scores: component i of lane l is head 4 (l / 16) + i of cell l % 16;
+    // then the next tile's K requested into the same registers
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NKC; ++kk) {
+      s = M::mma(qh[kk], kn[kk], s);
+      s = M::mma(ql[kk], kn[kk], s);
+    }
+    {
+      const int ck = cell_of(nt, lane & 15);
+#pragma unroll
+      for (int kk = 0; kk < NKC; ++kk) kn[kk] = *(const vec*)(kc + (int64_t)ck * HD + kk * 32 + (lane >> 4) * 8);
+    }
+    const bool live = tl * 16 + (lane & 15) < span;
+    float mr[4];  // reference max of this lane's heads
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[i] = (live && hrow + i < G) ? s[i] : -INFINITY;
+      float mh = m_w[i < G ? i : 0];
+      if (G > 4 && hrow >= 4) mh = m_w[(4 + i) < G ? 4 + i : 0];
+      mr[i] = mh;
+    }
+    bool over = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) over |= s[i] > mr[i] + kSlack;
+    if (__ballot(over)) {
+      // some score passed its reference by more than the slack: move the
+      // references of every head to the exact running max, rescale
+      float al[4];
+      float mnew[G], alpha[G];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mr[i] = row16_max(s[i]);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float th = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mr[h & 3]), (h >> 2) * 16));
+        mnew[h] = fmaxf(m_w[h], th);  // finite: the tile has a live cell
+        alpha[h] = __expf(m_w[h] - mnew[h]);
+        m_w[h] = mnew[h];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float mh = mnew[i < G ? i : 0], ah = alpha[i < G ? i : 0];
+        if (G > 4 && hrow >= 4) {
+          mh = mnew[(4 + i) < G ? 4 + i : 0];
+          ah = alpha[(4 + i) < G ? 4 + i : 0];
+        }
+        mr[i] = mh;
+        al[i] = ah;
+      }
+#pragma unroll
+      for (int n = 0; n < NN; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[n][i] *= al[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc_l[i] *= al[i];
+    }
+    float ps[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ps[i] = s[i] == -INFINITY ? 0.f : __expf(s[i] - mr[i]);
+    // probabilities to [head][cell] in LDS, read back as the 16 x 16 left
+    // operand of the value product: lane l takes head l % 16, cells
+    // 4 (l / 16) .. + 4, split into a high part and the remainder
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (hrow + i < G) pt_s[wv][hrow + i][lane & 15] = ps[i];
+    __builtin_amdgcn_wave_barrier();
+    vec4 ph, pl;
+    {
+      const int hp = lane & 15;
+      const float4 p4 = *(const float4*)&pt_s[wv][min(hp, G - 1)][hrow];
+      const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        short hi, lo;
+        M::split(hp < G ? pv[q] : 0.f, hi, lo);
+        ph[q] = __builtin_bit_cast(typename std::remove_reference<decltype(ph[0])>::type, hi);
+        pl[q] = __builtin_bit_cast(typename std::remove_reference<decltype(pl[0])>::type, lo);
+      }
+    }
+    // value product: right operand lane l = cells 4 (l / 16) .. + 4 of
+    // dimension 16 n + l % 16, read down the LDS tile's column; a column of
+    // ones gives the probability sums
+#pragma unroll
+    for (int n = 0; n < NN; ++n) {
+      vec4 b;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const short x = vw[(hrow + q) * VP + n * 16 + (lane & 15)];
+        b[q] = __builtin_bit_cast(typename std::remove_reference<decltype(b[0])>::type, x);
+      }
+      acc[n] = M::mma4(ph, b, acc[n]);
+      acc[n] = M::mma4(pl, b, acc[n]);
+    }
+    acc_l = M::mma4(ph, ones, acc_l);
+    acc_l = M::mma4(pl, ones, acc_l);
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // accumulator rows are heads: head hrow + i of this lane's row, dimension
+  // 16 n + l % 16; the waves combine through LDS
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (hrow + i < G) {
+#pragma unroll
+      for (int n = 0; n < NN; ++n) acc_s[wv][hrow + i][n * 16 + (lane & 15)] = acc[n][i];
+    }
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (hrow + i < G) l_s[wv][hrow + i] = acc_l[i];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) m_s[wv][h] = m_w[h];  // -inf for a wave without tiles
+  }
+  __syncthreads();
+  const int nch = (nvis + a.chunk - 1) / a.chunk;
+  constexpr int OUT_PER = (G * HD + 255) / 256;
+#pragma unroll
+  for (int o = 0; o < OUT_PER; ++o) {
+    const int id = tid + o * 256;
+    if (id < G * HD) {
+      const int h = id / HD, d = id % HD;
+      const float Mx = fmaxf(fmaxf(m_s[0][h], m_s[1][h]), fmaxf(m_s[2][h], m_s[3][h]));
+      float L = 0.f, A = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float wt = m_s[w][h] == -INFINITY ? 0.f : __expf(m_s[w][h] - Mx);
+        L = fmaf(l_s[w][h], wt, L);
+        A = fmaf(acc_s[w][h][d], wt, A);
+      }
+      if (nch == 1) {
+        const float r = A / L;
+        const int64_t oi = ((int64_t)t * a.H + g * G + h) * HD + d;
+        if (a.out) a.out[oi] = r;
+        if (a.out_hi) split_bf16(r, a.out_hi[oi], a.out_lo[oi]);
+      } else {
+        const int64_t base = ((int64_t)t * a.H + g * G + h) * a.n_chunks + j;
+        a.part_acc[base * HD + d] = A;
+        if (d == 0) {
+          a.part_ml[base * 2] = Mx;
+          a.part_ml[base * 2 + 1] = L;
+        }
+      }
+    }
+  }
+}
+
 // One block of NTH threads (NTH >= 64, a multiple of HD) per (query head,
 // token).  Wave 0 turns the per-split maxima and sums into weights
 // exp(m_j - M) and the total L; then NTH/HD thread groups each sum every
@@ -1037,7 +1356,22 @@ template <typename KvT, int HD>
 static hipError_t attn_launch_hd(const AttnArgs& a, hipStream_t s) {
   const int G = a.H / a.Hkv;
   dim3 grid(a.n_chunks, a.Hkv, a.T);
-  switch (G) {
+  // 16-bit caches with head_dim 64 or 128: scores and value products on the
+  // matrix cores (chunks of at most kCellStage cells)
+  bool done = false;
+  if constexpr (!std::is_same<KvT, float>::value && (HD == 64 || HD == 128)) {
+    if (a.chunk <= kCellStage) {
+      switch (G) {
+        case 1: attn_decode_mfma_kernel<KvT, HD, 1><<<grid, 256, 0, s>>>(a); break;
+        case 2: attn_decode_mfma_kernel<KvT, HD, 2><<<grid, 256, 0, s>>>(a); break;
+        case 4: attn_decode_mfma_kernel<KvT, HD, 4><<<grid, 256, 0, s>>>(a); break;
+        case 8: attn_decode_mfma_kernel<KvT, HD, 8><<<grid, 256, 0, s>>>(a); break;
+        default: return hipErrorInvalidValue;
+      }
+      done = true;
+    }
+  }
+  if (!done) switch (G) {
     case 1: attn_decode_kernel<KvT, HD, 1><<<grid, 256, 0, s>>>(a); break;
     case 2: attn_decode_kernel<KvT, HD, 2><<<grid, 256, 0, s>>>(a); break;
     case 4: attn_decode_kernel<KvT, HD, 4><<<grid, 256, 0, s>>>(a); break;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tdf.h"
+
 namespace tdf {
 
 enum Epilogue : int {
@@ -145,6 +147,13 @@ struct AttnArgs {
   uint16_t* out_lo = nullptr;
 };
 hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t s);
+// Decode attention stages a block's cell indices in LDS; with 16-bit caches
+// and head_dim 64 or 128 it runs on the matrix cores when a.chunk is at most
+// this many cells.
+constexpr int kDecodeCellStage = 1024;
+inline bool attn_decode_on_mfma(int kv_dtype, int hd) {
+  return (kv_dtype == TDF_F16 || kv_dtype == TDF_BF16) && (hd == 64 || hd == 128);
+}
 // merge of split partials only (part_* -> out / out_bf16)
 hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s);
 

@@ -869,10 +869,19 @@ extern "C" int32_t tdf_decode(tdf_context* c, const tdf_batch* b) {
         // a captured launch sequence stays valid while the context grows
         int chunk = (nmax + kChunkCapDecode - 1) / kChunkCapDecode;
         chunk = std::max(64, (chunk + 63) / 64 * 64);
-        // several tiles per block once there are blocks to spare (long
-        // contexts, many tokens): fewer partials, per-block costs amortised
         const int64_t heads = (int64_t)T * c->m->hp.n_head_kv;
-        while (chunk < 512 && heads * ((nmax + 2 * chunk - 1) / (2 * chunk)) >= 4096) chunk *= 2;
+        if (attn_decode_on_mfma(c->kv_dtype, c->m->hp.head_dim)) {
+          // matrix-core kernel: about 256 blocks in all, 128..1024 cells each
+          // (measured best from one sequence at 2k to 32 sequences at 8k)
+          const int64_t want = (nmax * heads + 255) / 256;
+          int ch = 128;
+          while (ch < kDecodeCellStage && ch < want) ch *= 2;
+          chunk = std::max(chunk, std::min(ch, std::max(64, (nmax + 63) / 64 * 64)));
+        } else {
+          // several tiles per block once there are blocks to spare (long
+          // contexts, many tokens): fewer partials, per-block costs amortised
+          while (chunk < 512 && heads * ((nmax + 2 * chunk - 1) / (2 * chunk)) >= 4096) chunk *= 2;
+        }
         const int need = (nmax + chunk - 1) / chunk;
         int grid = 1;
         while (grid < need) grid *= 2;
