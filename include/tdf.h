@@ -256,7 +256,8 @@ int32_t tdf_profile_reset(tdf_context *c);
 
 /* Measurement hook: launch the linear layer of operation op (TDF_OP_GATE_UP,
  * TDF_OP_DOWN or TDF_OP_LM_HEAD) for an ubatch of n_tokens rows (the decode
- * GEMV up to 8 rows, the matrix-core GEMM above, as tdf_decode chooses)
+ * GEMV up to 8 rows, the streaming matrix-core kernel with its epilogue pass
+ * for 9..32 rows, the matrix-core GEMM above, as tdf_decode chooses)
  * reps times back to back on the context's stream, cycling over the layers
  * so that no launch finds its weights cached, and store the mean duration
  * per launch in microseconds (HIP events on that stream) in *avg_us.  The

@@ -6,9 +6,10 @@
 // A wave computes out[32 tokens][32 rows] on v_mfma_f32_32x32x16_bf16, the
 // activations (the hi/lo bf16 pair of the producers, as in the prefill GEMM)
 // staged per 128-wide K chunk in LDS and shared by the 4 waves, the weights
-// read straight from memory as the B operand (lane = row, 16 contiguous
-// bytes of it).  Every lane requests the next chunk's weights before the
-// current chunk's MFMAs.  Partial sums of each K slice go to a float32
+// requested row-contiguously (each load covers whole 256-byte segments of
+// four rows) and passed through the wave's LDS tile into the B operand
+// layout (lane = row, 16 contiguous bytes of it).  Every lane requests the
+// next chunk before the current chunk's MFMAs.  Partial sums of each K slice go to a float32
 // workspace [slice][32][N].
 // Pass 2 (skinny_epilogue_kernel): sums the slices and applies the epilogue
 // of the layer (store, residual add, SwiGLU as a hi/lo pair, or RoPE with
@@ -42,14 +43,22 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs s) {
   const LinearArgs& a = s.a;
   __shared__ __attribute__((aligned(16))) uint16_t Ah[32 * kSkPitch];
   __shared__ __attribute__((aligned(16))) uint16_t Al[32 * kSkPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[4][32 * kSkPitch];
   const int nrt = (s.N + 127) / 128;
   const int rt = blockIdx.x % nrt, ks = blockIdx.x / nrt;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int K = a.K, T = a.T;
   const int k0 = ks * s.kslice, k1 = min(K, k0 + s.kslice);
-  // this lane's weight row (clamped; rows past N are computed and dropped)
-  const int row = min(rt * 128 + w * 32 + (lane & 31), s.N - 1);
-  const uint16_t* wr = sk_row(a, SWIGLU, row) + (lane >> 5) * 8;
+  // Weights of the wave's 32 rows are requested row by row (load u: rows
+  // 4u + lane/16, 16-byte piece lane%16 of the chunk, so each request covers
+  // whole 256-byte row segments) and pass through the wave's LDS tile into
+  // the MFMA operand layout (lane = row, 16 contiguous bytes of it).  Rows
+  // past N are clamped: computed and dropped.
+  const uint16_t* wr[kSkU];
+#pragma unroll
+  for (int u = 0; u < kSkU; ++u)
+    wr[u] = sk_row(a, SWIGLU, min(rt * 128 + w * 32 + 4 * u + (lane >> 4), s.N - 1)) + (lane & 15) * 8;
+  uint16_t* wsw = Ws[w];
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
@@ -68,7 +77,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs s) {
   }
 #define SK_LOAD(kc_)                                                              \
   do {                                                                            \
-    _Pragma("unroll") for (int u = 0; u < kSkU; ++u) bw[u] = *(const bf16x8*)(wr + (kc_) + u * 16); \
+    _Pragma("unroll") for (int u = 0; u < kSkU; ++u) bw[u] = *(const bf16x8*)(wr[u] + (kc_)); \
     _Pragma("unroll") for (int i = 0; i < AP; ++i) {                              \
       ah[i] = *(const bf16x8*)(ahp[i] + (kc_));                                   \
       al[i] = *(const bf16x8*)(alp[i] + (kc_));                                   \
@@ -84,9 +93,8 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs s) {
       *(bf16x8*)&Ah[off] = ah[i];
       *(bf16x8*)&Al[off] = al[i];
     }
-    bf16x8 b[kSkU];
 #pragma unroll
-    for (int u = 0; u < kSkU; ++u) b[u] = bw[u];
+    for (int u = 0; u < kSkU; ++u) *(bf16x8*)&wsw[(4 * u + (lane >> 4)) * kSkPitch + (lane & 15) * 8] = bw[u];
     __syncthreads();
     if (kc + kSkChunk < k1) SK_LOAD(kc + kSkChunk);
 #pragma unroll
@@ -94,8 +102,9 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs s) {
       const int off = (lane & 31) * kSkPitch + u * 16 + (lane >> 5) * 8;
       const bf16x8 xh = *(const bf16x8*)&Ah[off];
       const bf16x8 xl = *(const bf16x8*)&Al[off];
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, b[u], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl, b[u], acc, 0, 0, 0);
+      const bf16x8 b = *(const bf16x8*)&wsw[off];
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl, b, acc, 0, 0, 0);
     }
   }
 #undef SK_LOAD

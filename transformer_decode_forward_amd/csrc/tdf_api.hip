@@ -1275,7 +1275,13 @@ extern "C" int32_t tdf_time_op(tdf_context* c, int32_t op, int32_t n_tokens, int
   if (e == hipSuccess) e = hipEventRecord(e0, c->stream);
   for (int i = 0; i < reps && e == hipSuccess; ++i) {
     LinearArgs a = args(op == TDF_OP_LM_HEAD ? 0 : i % L);
-    e = mfma ? launch_linear_gemm(a, c->stream) : launch_linear_gemv(a, c->stream);
+    // the dispatch of the forward pass (GEMV, 9..32-token streaming kernel, GEMM)
+    if (!mfma)
+      e = launch_linear_gemv(a, c->stream);
+    else if (a.T <= kDecodeMaxT && c->skinny_part && skinny_supported(a))
+      e = launch_linear_skinny(a, c->skinny_part, c->stream);
+    else
+      e = launch_linear_gemm(a, c->stream);
   }
   if (e == hipSuccess) e = hipEventRecord(e1, c->stream);
   if (e == hipSuccess) e = hipEventSynchronize(e1);
