@@ -124,9 +124,17 @@ __global__ void __launch_bounds__(256) skinny_epilogue_kernel(SkinnyArgs s) {
   const LinearArgs& a = s.a;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int T = a.T;
+  // sum of the K slices, 8 requests in flight at a time (clamped slice
+  // indices, the surplus weighted by 0)
   auto total = [&](int t, int n) {
     float y = 0.f;
-    for (int ks = 0; ks < s.ksplit; ++ks) y += s.part[((int64_t)ks * 32 + t) * s.N + n];
+    for (int k0 = 0; k0 < s.ksplit; k0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = s.part[((int64_t)min(k0 + k, s.ksplit - 1) * 32 + t) * s.N + n];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y = fmaf(v[k], k0 + k < s.ksplit ? 1.f : 0.f, y);
+    }
     return y;
   };
   if (EPI == EPI_SWIGLU) {
