@@ -54,6 +54,7 @@ template <> struct MfmaOf<kv_f16> {
 
 constexpr int kQT = 32;   // queries per tile
 constexpr int kCT = 64;   // cells per K/V tile
+constexpr int kPrefStage = 2048;  // cell list entries a block stages in LDS
 
 template <typename KvT, int HD, int G>
 __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))) attn_prefill_kernel(PrefillAttnArgs a) {
@@ -102,21 +103,46 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))
   float m_run = -INFINITY, l_run = 0.f;
 
   constexpr int CHUNKS = kCT * HD / 8;  // 16-byte pieces of one K (or V) tile
+  constexpr int PPT = CHUNKS / (64 * G);  // pieces of each per thread
+  // The block's cell list entries go to LDS once (ranges up to kPrefStage
+  // entries); tile loads then need no index round trip.  Entries past the
+  // block's range repeat its last cell: their scores are masked and their
+  // probabilities zero.
+  __shared__ int32_t cell_s[kPrefStage];
+  const int span = c_hi - c_lo;
+  const bool staged = span <= kPrefStage;  // block-uniform
+  if (staged)
+    for (int e = tid; e < span; e += 64 * G) cell_s[e] = cells[c_lo + e];
+  __syncthreads();
+  // Requests go out SUB pieces at a time (requesting the next tile during
+  // the current one would need 32 more registers than the kernel has left:
+  // measured slower with the spills).
+  constexpr int SUB = PPT < 4 ? PPT : 4;
+  uint4 kreg[SUB], vreg[SUB];
+#define TILE_LOAD(c0_, i0_)                                                            \
+  do {                                                                                 \
+    _Pragma("unroll") for (int i = 0; i < SUB; ++i) {                                  \
+      const int ii = tid + ((i0_) + i) * 64 * G;                                       \
+      const int cc = min((c0_) + ii % kCT, c_hi - 1);                                  \
+      const int64_t row = (int64_t)(staged ? cell_s[cc - c_lo] : cells[cc]) * HD + (ii / kCT) * 8; \
+      kreg[i] = *(const uint4*)(kc + row);                                             \
+      vreg[i] = *(const uint4*)(vc + row);                                             \
+    }                                                                                  \
+  } while (0)
   for (int c0 = c_lo; c0 < c_hi; c0 += kCT) {
-    const int nc = min(kCT, c_hi - c0);
-    __syncthreads();
-    for (int i = tid; i < CHUNKS; i += 64 * G) {
-      const int c = i % kCT, dchunk = (i / kCT) * 8;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (c < nc) {
-        const int64_t row = (int64_t)cells[c0 + c] * HD + dchunk;
-        kv = *(const uint4*)(kc + row);
-        vv = *(const uint4*)(vc + row);
-      }
-      *(uint4*)&k_s[c * KP + dchunk] = kv;
-      const uint16_t* vh = (const uint16_t*)&vv;
+    __syncthreads();  // the previous tile's readers are done
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vt_s[(dchunk + e) * VP + c] = vh[e];
+    for (int i0 = 0; i0 < PPT; i0 += SUB) {
+      TILE_LOAD(c0, i0);
+#pragma unroll
+      for (int i = 0; i < SUB; ++i) {
+        const int ii = tid + (i0 + i) * 64 * G;
+        const int c = ii % kCT, dchunk = (ii / kCT) * 8;
+        *(uint4*)&k_s[c * KP + dchunk] = kreg[i];
+        const uint16_t* vh = (const uint16_t*)&vreg[i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vt_s[(dchunk + e) * VP + c] = vh[e];
+      }
     }
     __syncthreads();
 
@@ -184,6 +210,7 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))
     }
   }
 
+#undef TILE_LOAD
   // o[dt][r] <-> head dim dt*32 + (r/4)*8 + qg*4 + r%4 of this lane's query
   if (t < 0 || nvis <= c_lo) return;
   if (a.n_splits == 1) {
