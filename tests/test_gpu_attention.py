@@ -8,7 +8,6 @@ ragged last tile, then decodes single tokens and a multi-sequence step."""
 import numpy as np
 import pytest
 
-
 import tdf_synth
 
 from gpu_common import TOL_BF16, make_weights
