@@ -56,6 +56,7 @@ def _load():
         lib.tdfs_normal_bf16.argtypes = [u64, u64, i64, f64, vp]
         lib.tdfs_uniform_i32.argtypes = [u64, u64, i64, i64, i64, vp]
         lib.tdfs_f32_to_bf16.argtypes = [vp, i64, vp]
+        lib.tdfs_normal_q8_0.argtypes = [u64, i64, i64, f64, vp, vp]
         _lib = lib
     return _lib
 
@@ -86,6 +87,22 @@ def normal(seed: int, name: str, n: int, std: float = 1.0, dtype: str = "f32", f
         lib.tdfs_normal_bf16(key, first, n, std, out.ctypes.data)
     else:
         raise ValueError(f"unsupported dtype {dtype!r}")
+    return out
+
+
+def normal_q8_0(seed: int, name: str, rows: int, K: int, std: float) -> np.ndarray:
+    """The [rows][K] matrix of draws fp32(std * N(0,1)) of stream (seed, name)
+    (element (r, k) is draw r*K + k, as ``normal``) stored as Q8_0: per block
+    of 32 consecutive elements of a row a scale d = fp16(max|w| / 127) and
+    q = round-to-nearest-even(w / d) in [-127, 127].  Returned as one uint8
+    buffer: rows*K int8 values q (row-major) followed by rows*K/32 fp16 scales
+    (row-major [rows][K/32])."""
+    if K % 32:
+        raise ValueError("Q8_0 rows must be a multiple of 32 long")
+    lib = _load()
+    key = lib.tdfs_stream_key(seed, name.encode())
+    out = np.empty(rows * K + rows * (K // 32) * 2, dtype=np.uint8)
+    lib.tdfs_normal_q8_0(key, rows, K, std, out.ctypes.data, out[rows * K:].ctypes.data)
     return out
 
 
@@ -193,7 +210,8 @@ def tensor_shapes(cfg: dict, layer: int | None = None) -> dict:
 def make_tensor(cfg: dict, name: str, shape: tuple) -> np.ndarray:
     """One tensor: norm gains are exactly 1.0 (fp32) unless the config sets
     ``gain_std`` (then 1 + N(0, gain_std) in fp32); matrices N(0, weight_std)
-    (default 0.02) in the config's weight dtype (float32, or uint16 bf16 bits)."""
+    (default 0.02) in the config's weight dtype (float32, uint16 bf16 bits, or
+    the uint8 Q8_0 buffer of ``normal_q8_0``)."""
     n = int(np.prod(shape))
     if name.endswith("norm.weight"):
         gs = cfg.get("gain_std", 0.0)
@@ -201,6 +219,8 @@ def make_tensor(cfg: dict, name: str, shape: tuple) -> np.ndarray:
             return np.ones(shape, dtype=np.float32)
         return (1.0 + normal(cfg["seed"], name, n, gs, "f32").astype(np.float64)).astype(np.float32).reshape(shape)
     std = cfg.get("weight_std", WEIGHT_STD)
+    if cfg["weight_dtype"] == "q8_0":
+        return normal_q8_0(cfg["seed"], name, shape[0], shape[1], std)
     return normal(cfg["seed"], name, n, std, cfg["weight_dtype"]).reshape(shape)
 
 

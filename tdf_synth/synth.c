@@ -97,6 +97,72 @@ void tdfs_normal_bf16(uint64_t key, uint64_t first, int64_t n, double std, uint1
   FOR_EACH_NORMAL(key, first, n, out[i] = f32_to_bf16_rne((float)(std * v[e])));
 }
 
+static inline uint16_t f32_to_f16_rne(float f) {
+  /* normal and subnormal halves; values past the half range saturate to inf */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  const uint32_t sign = (u >> 16) & 0x8000u;
+  const uint32_t absu = u & 0x7FFFFFFFu;
+  if (absu >= 0x47800000u) return (uint16_t)(sign | 0x7C00u); /* >= 65536: inf */
+  if (absu < 0x33000000u) return (uint16_t)sign;              /* < 2^-25: zero */
+  int32_t exp = (int32_t)(absu >> 23) - 127;
+  uint32_t mant = (absu & 0x7FFFFFu) | 0x800000u;
+  int32_t shift = exp < -14 ? 13 + (-14 - exp) : 13; /* bits dropped from the 24-bit mantissa */
+  uint32_t half = mant >> shift, rem = mant & ((1u << shift) - 1u), mid = 1u << (shift - 1);
+  if (rem > mid || (rem == mid && (half & 1u))) ++half;
+  if (exp < -14) return (uint16_t)(sign | half);             /* subnormal (may round up to the min normal) */
+  return (uint16_t)(sign | (((uint32_t)(exp + 15) << 10) + (half - 0x400u)));
+}
+
+static inline float f16_to_f32(uint16_t h) {
+  const uint32_t sign = ((uint32_t)h & 0x8000u) << 16;
+  const uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
+  float v;
+  if (e == 0) v = (float)m * 5.9604644775390625e-08f; /* m * 2^-24 */
+  else {
+    uint32_t u = ((e + 112u) << 23) | (m << 13);
+    memcpy(&v, &u, 4);
+  }
+  uint32_t b;
+  memcpy(&b, &v, 4);
+  b |= sign;
+  memcpy(&v, &b, 4);
+  return v;
+}
+
+/* Q8_0 blocks of a row-major [rows][K] matrix (K a multiple of 32) whose
+ * element (r, k) is draw r*K + k of stream `key`, fp32(std * N(0,1)): per
+ * block of 32 consecutive elements of a row, scale d = fp16(max|w| / 127)
+ * and q = round-to-nearest-even(w / d) clamped to [-127, 127] (0 when d is
+ * 0).  q: [rows][K] int8; d: [rows][K/32] fp16 bit patterns. */
+void tdfs_normal_q8_0(uint64_t key, int64_t rows, int64_t K, double std, int8_t *q, uint16_t *d) {
+  const int64_t nb = K / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t blk = 0; blk < rows * nb; ++blk) {
+    const int64_t r = blk / nb, b = blk % nb;
+    const uint64_t first = (uint64_t)(r * K + b * 32);
+    float w[32];
+    /* draws come in pairs (Box-Muller); first is even */
+    for (int j = 0; j < 32; j += 2) {
+      double v[2];
+      normal_pair(key, (first + (uint64_t)j) / 2, v);
+      w[j] = (float)(std * v[0]);
+      w[j + 1] = (float)(std * v[1]);
+    }
+    float amax = 0.f;
+    for (int j = 0; j < 32; ++j) amax = fabsf(w[j]) > amax ? fabsf(w[j]) : amax;
+    const uint16_t dh = f32_to_f16_rne(amax / 127.0f);
+    const float dv = f16_to_f32(dh);
+    d[blk] = dh;
+    for (int j = 0; j < 32; ++j) {
+      float x = dv > 0.f ? nearbyintf(w[j] / dv) : 0.f;
+      if (x > 127.f) x = 127.f;
+      if (x < -127.f) x = -127.f;
+      q[r * K + b * 32 + j] = (int8_t)x;
+    }
+  }
+}
+
 static inline int64_t uniform_at(uint64_t key, uint64_t i, uint64_t range) {
   /* integer in [0, range) */
   uint64_t k = key;
