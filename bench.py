@@ -16,7 +16,8 @@ library's stream between two HIP events, cycling over the 32 layers' weights.
 ``traffic`` is read from the committed rocprofv3 counter summary of that
 kernel when the kernel source still matches it (else null).
 ``kernels`` is a per-operation breakdown from an eager repeat with a HIP
-event pair around every launch (it includes the events' own overhead).
+event pair around every launch (it includes the events' own overhead):
+``prefill`` covers the prompt, ``decode`` the timed single-token steps.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-peaks]
     python bench.py --calibrate-copy     # plain 1 GiB device copy, for counter scaling
@@ -66,13 +67,18 @@ def build_model(cfg, keep_host=True):
     return tdf.Model(tdf_synth.hparams(cfg), dev), host
 
 
+def weight_bytes_per_element(cfg):
+    """bf16: 2; float32: 4; Q8_0: 34 bytes per block of 32 (int8 + fp16 scale)."""
+    return {"bf16": 2.0, "f32": 4.0, "q8_0": 34.0 / 32.0}[cfg["weight_dtype"]]
+
+
 def decode_bytes(cfg, ctx_len):
     """Algorithmic HBM bytes of one single-token decode step at context ctx_len:
     every weight once, K/V of the visible cells, the new K/V, the logits."""
     d, H, Hkv, hd, F, V, L = (cfg[k] for k in ("n_embd", "n_head", "n_head_kv", "head_dim", "n_ff",
                                              "n_vocab", "n_layer"))
     p_layer = d * H * hd + 2 * d * Hkv * hd + H * hd * d + 3 * d * F
-    weights = 2 * (L * p_layer + V * d)
+    weights = weight_bytes_per_element(cfg) * (L * p_layer + V * d)
     kv_cell = L * 2 * Hkv * hd * 2
     return weights + kv_cell * ctx_len + kv_cell + 4 * V
 
@@ -324,6 +330,8 @@ def main():
     ap.add_argument("--config", default="llama8b")
     ap.add_argument("--no-peaks", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--weights", choices=["bf16", "q8_0"], default=None,
+                    help="weight storage of the single-sequence workload (default: the config's, bf16)")
     ap.add_argument("--swa", type=int, default=0,
                     help="sliding-window attention of this many positions on every layer (0: none)")
     args = ap.parse_args()
@@ -342,6 +350,9 @@ def main():
     cfg = dict(tdf_synth.CONFIGS[args.config])
     if args.swa:
         cfg["n_swa"] = args.swa
+    if args.weights:
+        cfg["weight_dtype"] = args.weights
+    q8 = cfg["weight_dtype"] == "q8_0"
     if args.config == "llama8b_multiseq":
         print(json.dumps(run_multiseq(args, cfg)), flush=True)
         return
@@ -355,19 +366,25 @@ def main():
     model, host = build_model(cfg)
     prompt = tdf_synth.prompt(cfg, 0, P)
 
-    def run(ctx, steps, warm):
+    def run(ctx, steps, warm, on_prefilled=None, on_warm=None):
         # prefill: repeated on a cleared cache, the last repetition timed
         for _ in range(args.prefill_reps + 1):
             ctx.kv_clear()
+            if on_prefilled:
+                on_prefilled(None)  # drop the earlier repetitions' records
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             assert ctx.decode(prompt) == 0, tdf.tdf_last_error()
             t_pre = time.perf_counter() - t0
+        if on_prefilled:
+            on_prefilled(ctx)
         tok = ctx.argmax_ith(P - 1)
         for _ in range(warm):
             assert ctx.decode([tok]) == 0, tdf.tdf_last_error()
             tok = ctx.argmax_ith(0)
         torch.cuda.synchronize()
+        if on_warm:
+            on_warm()
         t0 = time.perf_counter()
         for _ in range(steps):
             assert ctx.decode([tok]) == 0, tdf.tdf_last_error()
@@ -431,17 +448,26 @@ def main():
 
     log("profiled run (HIP events per launch)")
     pctx = tdf.Context(model, n_ctx=n_ctx, n_ubatch=U, kv_dtype=cfg["kv_dtype"], profile=True)
-    run(pctx, args.steps, args.warmup)
-    prof = pctx.profile()
+    prof_phase = {}
+
+    def prefilled(c):
+        if c is not None:
+            prof_phase["prefill"] = c.profile()
+        pctx.profile_reset()
+
+    run(pctx, args.steps, args.warmup, on_prefilled=prefilled, on_warm=pctx.profile_reset)
+    prof_phase["decode"] = pctx.profile()
     pctx.close()
     # per decode launch: the gate and up matrices once, the normed input, the output
-    gu_bytes = 2 * F * d * 2 + d * 4 + F * 4
+    gu_bytes = int(2 * F * d * weight_bytes_per_element(cfg)) + d * 4 + F * 4
     gu_gbs = gu_bytes / (gu_us * 1e-6) / 1e9
     gg_flops = 2.0 * U * (2 * F) * d
     gg_tfs = gg_flops / (gg_us * 1e-6) / 1e12
     peaks = None if args.no_peaks else measured_peaks()
-    breakdown = {f"{k[0]}/{k[1]}": {"launches": v[0], "avg_us": round(1000.0 * v[1] / v[0], 2)}
-                 for k, v in sorted(prof.items())}
+    breakdown = {phase: {f"{k[0]}/{k[1]}": {"launches": v[0], "avg_us": round(1000.0 * v[1] / v[0], 2),
+                                            "total_ms": round(v[1], 3)}
+                         for k, v in sorted(pr.items())}
+                 for phase, pr in prof_phase.items()}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -449,7 +475,8 @@ def main():
         cpu = cpu_baseline(cfg, host, P)
 
     out = {
-        "metric": "decode tok/s (% HBM peak) + prefill tok/s (% MFMA peak), 8B-shape bf16",
+        "metric": ("decode tok/s (% HBM peak) + prefill tok/s (% MFMA peak), 8B-shape bf16" if not q8 else
+                   "decode tok/s (% HBM peak) + prefill tok/s, 8B-shape Q8_0 weights"),
         "value": round(decode_tps, 3),
         "unit": "tok/s",
         "n_gpus": 1,
@@ -459,10 +486,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32 (q8_0 weights)" if q8 else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{args.config}: batch 1, {P}-token prompt in ubatches of {U} "
-                               f"(last-position logits), then greedy decode steps; KV bf16 {n_ctx} cells",
+                               f"(last-position logits), then greedy decode steps; KV bf16 {n_ctx} cells"
+                               + ("; Q8_0 weights" if q8 else ""),
                    "d_model": d, "n_layer": cfg["n_layer"], "n_ff": F, "n_vocab": cfg["n_vocab"],
                    "attention_window": args.swa or None},
         "decode": {"tok_s": round(decode_tps, 3), "mean_ctx": mean_ctx,
@@ -476,11 +504,11 @@ def main():
                     "frac_mfma_peak": round(pre_flops / t_pre / 1e12 / MFMA_BF16_PEAK_TFS, 4)},
         "roofline": {"bound": "hbm", "kernel": "gate/up GEMV + SwiGLU (decode)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic("decode"),
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None if q8 else traffic("decode"),
                      "avg_launch_us": round(gu_us, 2), "bytes_per_launch": gu_bytes},
         "roofline_prefill": {"bound": "mfma", "kernel": "gate/up GEMM + SwiGLU (prefill ubatch 512)",
                              "achieved": round(gg_tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                             "frac": round(gg_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic("prefill"),
+                             "frac": round(gg_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None if q8 else traffic("prefill"),
                              "avg_launch_us": round(gg_us, 2), "flops_per_launch": gg_flops,
                              "executed_flops_per_launch": 2 * gg_flops},
         "measured_peaks": peaks,

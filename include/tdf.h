@@ -34,7 +34,13 @@
 extern "C" {
 #endif
 
-typedef enum { TDF_F32 = 0, TDF_F16 = 1, TDF_BF16 = 2 } tdf_dtype;
+/* TDF_Q8_0 is a weight format only (llama.cpp walkthrough and the Ollama
+ * backends chapter name the "Q8_0" type without defining it; the common
+ * reading is taken): every block of 32 consecutive elements of a row is one
+ * fp16 scale d times 32 int8 values q, w = d * q.  A Q8_0 matrix [rows][K]
+ * (K a multiple of 32) is one buffer: rows*K int8 values q, row-major, then
+ * rows*K/32 fp16 scales, row-major [rows][K/32], starting at byte rows*K. */
+typedef enum { TDF_F32 = 0, TDF_F16 = 1, TDF_BF16 = 2, TDF_Q8_0 = 3 } tdf_dtype;
 
 /* Return codes of tdf_decode / tdf_kv_import (llama.cpp walkthrough,
  * "Steps 11-12": 0 success, 1 non-fatal, negative error). */
@@ -72,7 +78,9 @@ enum {
 /* Hyper-parameters (llama.cpp walkthrough, "Step 4": n_vocab, n_embd,
  * n_layer, n_head, n_head_kv, n_ff, rope base).  head_dim is given
  * explicitly; rope frequency scale is 1 and RMSNorm eps sits inside the
- * square root. weight_dtype is TDF_F32 or TDF_BF16. */
+ * square root. weight_dtype is TDF_F32, TDF_BF16 or TDF_Q8_0 (then n_embd,
+ * n_head*head_dim and n_ff must be multiples of 32); it applies to the
+ * matrices and the embedding table, never to the norm gains. */
 typedef struct {
   int32_t n_vocab, n_embd, n_layer, n_head, n_head_kv, head_dim, n_ff;
   float rms_eps, rope_theta;

@@ -142,6 +142,15 @@ def test_window_hparams_accepted_and_checked():
         tdf.Model(dict(HP, n_swa=-1), dry_run=True)
 
 
+def test_q8_0_weights_accepted_and_sizes_checked():
+    """Q8_0 blocks are 32 elements of a row: every inner size must be a
+    multiple of 32 (n_embd, n_head*head_dim, n_ff)."""
+    tdf.Model(dict(HP, weight_dtype="q8_0"), dry_run=True)
+    for bad in (dict(n_embd=48), dict(n_ff=144), dict(n_head=1, n_head_kv=1)):
+        with pytest.raises(RuntimeError, match="multiples of 32"):
+            tdf.Model(dict(HP, weight_dtype="q8_0", **bad), dry_run=True)
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_random_scripts_with_removal_and_shift_match_oracle(seed):
     """Decode calls interleaved with range removals and shifts (valid and

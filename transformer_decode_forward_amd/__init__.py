@@ -20,8 +20,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtdf.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "tdf.h")
 
-TDF_F32, TDF_F16, TDF_BF16 = 0, 1, 2
-DTYPES = {"f32": TDF_F32, "f16": TDF_F16, "bf16": TDF_BF16}
+TDF_F32, TDF_F16, TDF_BF16, TDF_Q8_0 = 0, 1, 2, 3
+DTYPES = {"f32": TDF_F32, "f16": TDF_F16, "bf16": TDF_BF16, "q8_0": TDF_Q8_0}
 TDF_OK, TDF_NO_SLOT, TDF_E_INVALID, TDF_E_ALLOC, TDF_E_DEVICE = 0, 1, -1, -2, -3
 TDF_CTX_DRY_RUN, TDF_CTX_PROFILE = 1, 2
 OPS = ["embed", "norm", "qkv", "attn", "wo", "gate_up", "down", "lm_head", "argmax"]

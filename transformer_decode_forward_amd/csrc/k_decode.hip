@@ -31,8 +31,27 @@ __device__ __forceinline__ float block_sum256(float v, float* red4) {
   return red4[0] + red4[1] + red4[2] + red4[3];
 }
 
-template <bool BF16>
-__global__ void __launch_bounds__(256) embed_kernel(const void* __restrict__ table,
+// Storage of the weight matrices and the embedding table.  A Q8_0 matrix
+// [rows][K] is rows*K int8 values q followed by its fp16 block scales
+// [rows][K/32]; element (r, k) is scale[(r*K + k) / 32] * q[r*K + k].
+enum WeightKind : int { W_F32 = 0, W_BF16 = 1, W_Q8 = 2 };
+
+__host__ __device__ __forceinline__ constexpr int weight_kind(int dtype) {
+  return dtype == TDF_BF16 ? W_BF16 : dtype == TDF_Q8_0 ? W_Q8 : W_F32;
+}
+
+// fp16 block scales of a Q8_0 matrix of `rows` rows of K elements
+__device__ __forceinline__ const uint16_t* q8_scales(const void* w, int64_t rows, int K) {
+  return (const uint16_t*)((const int8_t*)w + rows * K);
+}
+
+// signed byte b (0..3) of a 32-bit word, as float
+__device__ __forceinline__ float sbyte(uint32_t v, int b) {
+  return (float)((int32_t)(v << (24 - 8 * b)) >> 24);
+}
+
+template <int WT>
+__global__ void __launch_bounds__(256) embed_kernel(const void* __restrict__ table, int64_t n_rows,
                                                     const int32_t* __restrict__ tokens, int d,
                                                     float* __restrict__ x, const float* __restrict__ g,
                                                     float* __restrict__ u, float* __restrict__ ssp,
@@ -47,10 +66,15 @@ __global__ void __launch_bounds__(256) embed_kernel(const void* __restrict__ tab
 #pragma unroll 4
     for (int k = threadIdx.x * 4; k < d; k += 1024) {
       float4 v;
-      if (BF16) {
+      if (WT == W_BF16) {
         const uint2 q = *(const uint2*)((const uint16_t*)table + row + k);
         v = make_float4(__builtin_bit_cast(float, q.x << 16), __builtin_bit_cast(float, q.x & 0xFFFF0000u),
                         __builtin_bit_cast(float, q.y << 16), __builtin_bit_cast(float, q.y & 0xFFFF0000u));
+      } else if (WT == W_Q8) {
+        // four int8 of one 32-element block (d is a multiple of 32)
+        const uint32_t q = *(const uint32_t*)((const int8_t*)table + row + k);
+        const float sc = f16_to_f32(q8_scales(table, n_rows, d)[(row + k) >> 5]);
+        v = make_float4(sc * sbyte(q, 0), sc * sbyte(q, 1), sc * sbyte(q, 2), sc * sbyte(q, 3));
       } else {
         v = *(const float4*)((const float*)table + row + k);
       }
@@ -63,7 +87,7 @@ __global__ void __launch_bounds__(256) embed_kernel(const void* __restrict__ tab
     }
   } else {
     for (int k = threadIdx.x; k < d; k += 256) {
-      const float v = BF16 ? bf16_to_f32(((const uint16_t*)table)[row + k]) : ((const float*)table)[row + k];
+      const float v = WT == W_BF16 ? bf16_to_f32(((const uint16_t*)table)[row + k]) : ((const float*)table)[row + k];
       xr[k] = v;
       if (g) {
         ur[k] = g[k] * v;
@@ -77,13 +101,17 @@ __global__ void __launch_bounds__(256) embed_kernel(const void* __restrict__ tab
   }
 }
 
-hipError_t launch_embed(const void* table, int weight_bf16, const int32_t* tokens, int T, int d,
+hipError_t launch_embed(const void* table, int weight_dtype, int n_rows, const int32_t* tokens, int T, int d,
                         float* x, const float* g, float* u, float* ssp, int stride, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (weight_bf16)
-    embed_kernel<true><<<T, 256, 0, s>>>(table, tokens, d, x, g, u, ssp, stride);
+  const int wk = weight_kind(weight_dtype);
+  if (wk == W_Q8 && d % 32 != 0) return hipErrorInvalidValue;
+  if (wk == W_BF16)
+    embed_kernel<W_BF16><<<T, 256, 0, s>>>(table, n_rows, tokens, d, x, g, u, ssp, stride);
+  else if (wk == W_Q8)
+    embed_kernel<W_Q8><<<T, 256, 0, s>>>(table, n_rows, tokens, d, x, g, u, ssp, stride);
   else
-    embed_kernel<false><<<T, 256, 0, s>>>(table, tokens, d, x, g, u, ssp, stride);
+    embed_kernel<W_F32><<<T, 256, 0, s>>>(table, n_rows, tokens, d, x, g, u, ssp, stride);
   return hipGetLastError();
 }
 
@@ -346,39 +374,30 @@ hipError_t launch_argmax(const float* logits, int R, int V, int32_t* tok, float*
 }
 
 // ---------------------------------------------------------------------------
-// GEMV: one wave per output pair.  For EPI_SWIGLU the pair is (gate row n,
-// up row n); otherwise rows (2p, 2p+1), so that a RoPE pair (2i, 2i+1) of a
-// head lands in one wave.  Lanes stride the row in chunks of 8 elements
-// (16 bytes of bf16), all NT tokens reuse each weight chunk from registers.
+// GEMV: one wave per R/2 output pairs (R = 2 or 4 rows).  For EPI_SWIGLU a
+// pair is (gate row n, up row n); otherwise rows (2p, 2p+1), so that a RoPE
+// pair (2i, 2i+1) of a head lands in one wave.  Lanes stride the rows in
+// chunks of 16 bytes per lane, all NT tokens reuse each weight chunk from
+// registers and the R rows share each activation chunk.
 
-template <bool BF16>
-__device__ __forceinline__ void load8(const void* base, int64_t idx, float w[8]) {
-  if (BF16) {
-    const uint4 u = *(const uint4*)((const uint16_t*)base + idx);
-    const uint32_t p[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      w[2 * j] = __builtin_bit_cast(float, p[j] << 16);
-      w[2 * j + 1] = __builtin_bit_cast(float, p[j] & 0xFFFF0000u);
-    }
-  } else {
-    const float4 a = *(const float4*)((const float*)base + idx);
-    const float4 b = *(const float4*)((const float*)base + idx + 4);
-    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-  }
-}
-
-// 8 weights from raw 16-byte vectors (one for bf16, two for float32)
-template <bool BF16>
-__device__ __forceinline__ void unpack_w(const uint4* raw, float w[8]) {
-  if (BF16) {
+// EPL weights of one lane from raw 16-byte vectors: 8 bf16 (one vector), 8
+// float32 (two vectors) or 16 int8 of a Q8_0 block half (one vector; the
+// block scale is applied to the partial dot product by the caller)
+template <int WT>
+__device__ __forceinline__ void unpack_w(const uint4* raw, float* w) {
+  if (WT == W_BF16) {
     const uint32_t p[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       w[2 * j] = __builtin_bit_cast(float, p[j] << 16);
       w[2 * j + 1] = __builtin_bit_cast(float, p[j] & 0xFFFF0000u);
     }
+  } else if (WT == W_Q8) {
+    const uint32_t p[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) w[4 * j + b] = sbyte(p[j], b);
   } else {
     const uint32_t p[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
 #pragma unroll
@@ -386,9 +405,10 @@ __device__ __forceinline__ void unpack_w(const uint4* raw, float w[8]) {
   }
 }
 
-template <bool BF16>
+// one weight (rows whose length is not a multiple of 8; never Q8_0)
+template <int WT>
 __device__ __forceinline__ float load1(const void* base, int64_t idx) {
-  return BF16 ? bf16_to_f32(((const uint16_t*)base)[idx]) : ((const float*)base)[idx];
+  return WT == W_BF16 ? bf16_to_f32(((const uint16_t*)base)[idx]) : ((const float*)base)[idx];
 }
 
 template <typename KvT>
@@ -396,37 +416,57 @@ __device__ __forceinline__ void kv_put(void* cache, int64_t idx, float v) {
   KvStore<KvT>::store((typename KvStore<KvT>::T*)cache, idx, v);
 }
 
-template <bool BF16, int NT, int EPI, typename KvT, bool NORM, int U>
+template <int WT, int NT, int EPI, typename KvT, bool NORM, int U, int R>
 __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt) {
+  static_assert(R == 2 || R == 4, "rows per wave");
+  constexpr int P = R / 2;  // output pairs per wave
   __shared__ float red[4][NT];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wave = blockIdx.x * 4 + wid;
   const int N = a.n0 + a.n1 + a.n2;
   const int K = a.K;
-  // the two rows of this wave (inactive waves still join the block reduction)
-  int r0, r1;
-  const void *p0 = a.w0, *p1 = a.w0;
-  int64_t off0 = 0, off1 = 0;
-  bool active;
+  // The R rows of this wave.  Rows past the end are clamped to the last row
+  // for the loads (all in bounds) and their outputs dropped: rv[i] = 0.
+  // sc[i]: block scales of row i's matrix (Q8_0).  Inactive waves (no valid
+  // row) still join the block reductions.
+  int row[R];
+  bool rv[R];
+  const void* p[R];
+  const uint16_t* sc[R];
+  int64_t off[R];
   if (EPI == EPI_SWIGLU) {
-    active = wave < a.n0;
-    r0 = r1 = wave;
-    p0 = a.w0; p1 = a.w1;
-    off0 = off1 = (int64_t)wave * K;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int n = wave * P + j;
+      rv[2 * j] = rv[2 * j + 1] = n < a.n0;
+      const int nc = min(n, a.n0 - 1);
+      row[2 * j] = row[2 * j + 1] = n;
+      p[2 * j] = a.w0;
+      p[2 * j + 1] = a.w1;
+      off[2 * j] = off[2 * j + 1] = (int64_t)nc * K;
+      sc[2 * j] = WT == W_Q8 ? q8_scales(a.w0, a.n0, K) : nullptr;
+      sc[2 * j + 1] = WT == W_Q8 ? q8_scales(a.w1, a.n0, K) : nullptr;
+    }
   } else {
-    r0 = 2 * wave;
-    active = r0 < N;
-    r1 = r0 + 1 < N ? r0 + 1 : r0;
-    auto locate = [&](int r, const void*& p, int64_t& off) {
-      if (r < a.n0) { p = a.w0; off = (int64_t)r * K; }
-      else if (r < a.n0 + a.n1) { p = a.w1; off = (int64_t)(r - a.n0) * K; }
-      else { p = a.w2; off = (int64_t)(r - a.n0 - a.n1) * K; }
-    };
-    if (active) {
-      locate(r0, p0, off0);
-      locate(r1, p1, off1);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int r = R * wave + i;
+      rv[i] = r < N;
+      row[i] = r;
+      const int rc = min(r, N - 1);
+      if (rc < a.n0) {
+        p[i] = a.w0; off[i] = (int64_t)rc * K;
+        sc[i] = WT == W_Q8 ? q8_scales(a.w0, a.n0, K) : nullptr;
+      } else if (rc < a.n0 + a.n1) {
+        p[i] = a.w1; off[i] = (int64_t)(rc - a.n0) * K;
+        sc[i] = WT == W_Q8 ? q8_scales(a.w1, a.n1, K) : nullptr;
+      } else {
+        p[i] = a.w2; off[i] = (int64_t)(rc - a.n0 - a.n1) * K;
+        sc[i] = WT == W_Q8 ? q8_scales(a.w2, a.n2, K) : nullptr;
+      }
     }
   }
+  const bool active = rv[0];
   const float* act = a.act_f32 + (int64_t)t0 * K;
 
   // RMSNorm consumer: the block's 256 threads fetch the producer's partial
@@ -454,100 +494,122 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
   };
   bool norm_fetched = false;
 
-  float acc0[NT], acc1[NT];
+  float acc[R][NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc0[t] = acc1[t] = 0.f;
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[i][t] = 0.f;
+
+  // Each lane takes EPL consecutive elements of a chunk of 64 * EPL: 8 bf16
+  // or float32, or 16 int8 (half a Q8_0 block, one scale per lane)
+  constexpr int EPL = WT == W_Q8 ? 16 : 8;
+  constexpr int CH = 64 * EPL;
+  constexpr int WV = WT == W_F32 ? 2 : 1;                      // 16-byte vectors per lane and chunk
+  constexpr int ESZ = WT == W_F32 ? 4 : WT == W_BF16 ? 2 : 1;  // bytes per weight
+  constexpr int XV = EPL / 4;                                  // float4 activations per lane and chunk
+  // row i's partial dot product of one chunk into its accumulator (Q8_0: the
+  // int8 dot product times the block scale)
+#define TDF_GEMV_CHUNK(RAW, SCALE, XV4, T)                            \
+  {                                                                   \
+    float w_[EPL];                                                    \
+    unpack_w<WT>(RAW, w_);                                            \
+    const float* x_ = (const float*)(XV4);                            \
+    if (WT == W_Q8) {                                                 \
+      float d_ = 0.f;                                                 \
+      _Pragma("unroll") for (int j_ = 0; j_ < EPL; ++j_) d_ = fmaf(w_[j_], x_[j_], d_); \
+      acc[i][T] = fmaf(SCALE, d_, acc[i][T]);                         \
+    } else {                                                          \
+      _Pragma("unroll") for (int j_ = 0; j_ < EPL; ++j_) acc[i][T] = fmaf(w_[j_], x_[j_], acc[i][T]); \
+    }                                                                 \
+  }
 
   if (active) {
-    if ((K & 7) == 0) {
-      // Batches of U chunks of 512 elements: every lane issues all 2*U weight
-      // loads (16 bytes of bf16, or 2x16 of float32, each) and the activation
-      // loads of the batch before it waits, so each wave keeps 2*U KB of bf16
-      // weights in flight.  The
-      // last batch may be partial: its loads are clamped to the last chunk and
-      // the surplus chunks skipped (a wave-uniform test).
-      constexpr int WV = BF16 ? 1 : 2;  // 16-byte vectors per 8 weights
-      const int n_full = K / 512;
+    if ((K & (EPL - 1)) == 0) {
+      // Batches of U chunks: every lane issues all R*U weight loads (16 bytes
+      // of bf16 or int8, or 2x16 of float32, each) and the activation loads
+      // of the batch before it waits, so each wave keeps R*U*16 bytes per
+      // lane of weights in flight.  The last batch may be partial: its loads
+      // are clamped to the last chunk and the surplus chunks skipped (a
+      // wave-uniform test).
+      const int n_full = K / CH;
       for (int it = 0; it < n_full; it += U) {
-        uint4 raw0[U][WV], raw1[U][WV];
+        uint4 raw[U][R][WV];
+        float sw[U][R];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int64_t k = (int64_t)min(it + u, n_full - 1) * 512 + lane * 8;
+          const int64_t k = (int64_t)min(it + u, n_full - 1) * CH + lane * EPL;
 #pragma unroll
-          for (int v = 0; v < WV; ++v) {
-            raw0[u][v] = *(const uint4*)((const char*)p0 + (off0 + k) * (BF16 ? 2 : 4) + 16 * v);
-            raw1[u][v] = *(const uint4*)((const char*)p1 + (off1 + k) * (BF16 ? 2 : 4) + 16 * v);
+          for (int i = 0; i < R; ++i) {
+#pragma unroll
+            for (int v = 0; v < WV; ++v)
+              raw[u][i][v] = *(const uint4*)((const char*)p[i] + (off[i] + k) * ESZ + 16 * v);
+            sw[u][i] = WT == W_Q8 ? f16_to_f32(sc[i][(off[i] + k) >> 5]) : 1.f;
           }
         }
         // the norm partials ride with the first batch (counted once)
         if (NORM) norm_fetch(it == 0 ? 1.f : 0.f);
-        float4 xa[NT][U], xb[NT][U];
+        float4 xv[NT][U][XV];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           if (t < nt) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-              const int k = min(it + u, n_full - 1) * 512 + lane * 8;
-              xa[t][u] = *(const float4*)(act + (int64_t)t * K + k);
-              xb[t][u] = *(const float4*)(act + (int64_t)t * K + k + 4);
+              const int k = min(it + u, n_full - 1) * CH + lane * EPL;
+#pragma unroll
+              for (int v = 0; v < XV; ++v) xv[t][u][v] = *(const float4*)(act + (int64_t)t * K + k + 4 * v);
             }
           }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           if (it + u >= n_full) break;
-          float w0[8], w1[8];
-          unpack_w<BF16>(raw0[u], w0);
-          unpack_w<BF16>(raw1[u], w1);
 #pragma unroll
-          for (int t = 0; t < NT; ++t)
-            if (t < nt) {
-              const float x[8] = {xa[t][u].x, xa[t][u].y, xa[t][u].z, xa[t][u].w,
-                                  xb[t][u].x, xb[t][u].y, xb[t][u].z, xb[t][u].w};
+          for (int i = 0; i < R; ++i)
 #pragma unroll
-              for (int j = 0; j < 8; ++j) {
-                acc0[t] = fmaf(w0[j], x[j], acc0[t]);
-                acc1[t] = fmaf(w1[j], x[j], acc1[t]);
-              }
-            }
+            for (int t = 0; t < NT; ++t)
+              if (t < nt) TDF_GEMV_CHUNK(raw[u][i], sw[u][i], xv[t][u], t)
         }
       }
       norm_fetched = n_full > 0;
-      // the ragged end of the row (K not a multiple of 512)
-      for (int k = n_full * 512 + lane * 8; k < K; k += 512) {
-        float w0[8], w1[8];
-        load8<BF16>(p0, off0 + k, w0);
-        load8<BF16>(p1, off1 + k, w1);
+      // the ragged end of the row (K not a multiple of the chunk)
+      for (int k = n_full * CH + lane * EPL; k < K; k += CH) {
+        uint4 raw[R][WV];
+        float sw[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+#pragma unroll
+          for (int v = 0; v < WV; ++v) raw[i][v] = *(const uint4*)((const char*)p[i] + (off[i] + k) * ESZ + 16 * v);
+          sw[i] = WT == W_Q8 ? f16_to_f32(sc[i][(off[i] + k) >> 5]) : 1.f;
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           if (t < nt) {
-            const float4 x0 = *(const float4*)(act + (int64_t)t * K + k);
-            const float4 x1 = *(const float4*)(act + (int64_t)t * K + k + 4);
-            const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            float4 xv[XV];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              acc0[t] = fmaf(w0[j], x[j], acc0[t]);
-              acc1[t] = fmaf(w1[j], x[j], acc1[t]);
-            }
+            for (int v = 0; v < XV; ++v) xv[v] = *(const float4*)(act + (int64_t)t * K + k + 4 * v);
+#pragma unroll
+            for (int i = 0; i < R; ++i) TDF_GEMV_CHUNK(raw[i], sw[i], xv, t)
           }
       }
-    } else {
+    } else if (WT != W_Q8) {
       for (int k = lane; k < K; k += 64) {
-        const float w0 = load1<BF16>(p0, off0 + k), w1 = load1<BF16>(p1, off1 + k);
+        float w[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) w[i] = load1<WT>(p[i], off[i] + k);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           if (t < nt) {
             const float x = act[(int64_t)t * K + k];
-            acc0[t] = fmaf(w0, x, acc0[t]);
-            acc1[t] = fmaf(w1, x, acc1[t]);
+#pragma unroll
+            for (int i = 0; i < R; ++i) acc[i][t] = fmaf(w[i], x, acc[i][t]);
           }
       }
     }
   }
+#undef TDF_GEMV_CHUNK
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    acc0[t] = wave_sum(acc0[t]);
-    acc1[t] = wave_sum(acc1[t]);
-  }
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[i][t] = wave_sum(acc[i][t]);
   if (NORM) {
     // RMS scale 1/sqrt(ss/K + eps), ss = sum of the producer's partials
     if (!norm_fetched) norm_fetch(1.f);  // short or ragged rows, inactive waves
@@ -558,8 +620,8 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
 #pragma unroll
       for (int q = 0; q < kNormPer; ++q) ss += nss[t][q];
       if (t < nt)
-        for (int p = threadIdx.x + kNormPer * 256; p < a.norm_nparts; p += 256)
-          ss += a.norm_ssp[(int64_t)(t0 + t) * a.norm_stride + p];
+        for (int pi = threadIdx.x + kNormPer * 256; pi < a.norm_nparts; pi += 256)
+          ss += a.norm_ssp[(int64_t)(t0 + t) * a.norm_stride + pi];
       ss = wave_sum(ss);
       if (lane == 0) red_n[wid][t] = ss;
     }
@@ -568,61 +630,68 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
     for (int t = 0; t < NT; ++t) {
       const float ss = (red_n[0][t] + red_n[1][t]) + (red_n[2][t] + red_n[3][t]);
       const float r = 1.0f / sqrtf(ss / (float)K + a.norm_eps);
-      acc0[t] *= r;
-      acc1[t] *= r;
+#pragma unroll
+      for (int i = 0; i < R; ++i) acc[i][t] *= r;
     }
   }
-  // lane t writes token t
+  // lane t writes token t; pair j covers rows 2j and 2j+1 of the wave (r1 ==
+  // r0: a single row at the end of the matrix stack)
   const bool produce = EPI == EPI_RESIDUAL && a.next_g != nullptr;
   float sq[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     sq[t] = 0.f;
-    if (!active || lane != t || t >= nt) continue;
+    if (lane != t || t >= nt) continue;
     const int tg = t0 + t;
-    const float y0 = acc0[t], y1 = acc1[t];
-    if (EPI == EPI_STORE) {
-      a.out[(int64_t)tg * a.ldo + r0] = y0;
-      if (r1 != r0) a.out[(int64_t)tg * a.ldo + r1] = y1;
-    } else if (EPI == EPI_RESIDUAL) {
-      float* xo = a.out + (int64_t)tg * a.ldo;
-      const float x0 = xo[r0] + y0;
-      xo[r0] = x0;
-      if (produce) {
-        a.next_u[(int64_t)tg * a.ldo + r0] = a.next_g[r0] * x0;
-        sq[t] = x0 * x0;
-      }
-      if (r1 != r0) {
-        const float x1 = xo[r1] + y1;
-        xo[r1] = x1;
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      if (!rv[2 * j]) continue;
+      const int r0 = row[2 * j];
+      const int r1 = rv[2 * j + 1] ? row[2 * j + 1] : r0;
+      const float y0 = acc[2 * j][t], y1 = acc[2 * j + 1][t];
+      if (EPI == EPI_STORE) {
+        a.out[(int64_t)tg * a.ldo + r0] = y0;
+        if (r1 != r0) a.out[(int64_t)tg * a.ldo + r1] = y1;
+      } else if (EPI == EPI_RESIDUAL) {
+        float* xo = a.out + (int64_t)tg * a.ldo;
+        const float x0 = xo[r0] + y0;
+        xo[r0] = x0;
         if (produce) {
-          a.next_u[(int64_t)tg * a.ldo + r1] = a.next_g[r1] * x1;
-          sq[t] += x1 * x1;
+          a.next_u[(int64_t)tg * a.ldo + r0] = a.next_g[r0] * x0;
+          sq[t] += x0 * x0;
         }
-      }
-    } else if (EPI == EPI_SWIGLU) {
-      a.out[(int64_t)tg * a.ldo + r0] = silu(y0) * y1;
-    } else if (EPI == EPI_QKV) {
-      const int hd = a.head_dim;
-      if (r0 < a.n0 + a.n1) {
-        // q or k row pair (2i, 2i+1) of one head: rotate by pos * theta^(-2i/hd)
-        const int lr = r0 < a.n0 ? r0 : r0 - a.n0;
-        const int i = (lr % hd) >> 1;
-        const float2 cs = a.rope_cs[(int64_t)tg * (hd >> 1) + i];
-        const float z0 = y0 * cs.x - y1 * cs.y, z1 = y0 * cs.y + y1 * cs.x;
-        if (r0 < a.n0) {
-          a.q_out[(int64_t)tg * a.n0 + lr] = z0;
-          a.q_out[(int64_t)tg * a.n0 + lr + 1] = z1;
+        if (r1 != r0) {
+          const float x1 = xo[r1] + y1;
+          xo[r1] = x1;
+          if (produce) {
+            a.next_u[(int64_t)tg * a.ldo + r1] = a.next_g[r1] * x1;
+            sq[t] += x1 * x1;
+          }
+        }
+      } else if (EPI == EPI_SWIGLU) {
+        a.out[(int64_t)tg * a.ldo + r0] = silu(y0) * y1;
+      } else if (EPI == EPI_QKV) {
+        const int hd = a.head_dim;
+        if (r0 < a.n0 + a.n1) {
+          // q or k row pair (2i, 2i+1) of one head: rotate by pos * theta^(-2i/hd)
+          const int lr = r0 < a.n0 ? r0 : r0 - a.n0;
+          const int i = (lr % hd) >> 1;
+          const float2 cs = a.rope_cs[(int64_t)tg * (hd >> 1) + i];
+          const float z0 = y0 * cs.x - y1 * cs.y, z1 = y0 * cs.y + y1 * cs.x;
+          if (r0 < a.n0) {
+            a.q_out[(int64_t)tg * a.n0 + lr] = z0;
+            a.q_out[(int64_t)tg * a.n0 + lr + 1] = z1;
+          } else {
+            const int64_t ci = ((int64_t)(lr / hd) * a.n_ctx + a.slots[tg]) * hd + (lr % hd);
+            kv_put<KvT>(a.k_cache, ci, z0);
+            kv_put<KvT>(a.k_cache, ci + 1, z1);
+          }
         } else {
+          const int lr = r0 - a.n0 - a.n1;
           const int64_t ci = ((int64_t)(lr / hd) * a.n_ctx + a.slots[tg]) * hd + (lr % hd);
-          kv_put<KvT>(a.k_cache, ci, z0);
-          kv_put<KvT>(a.k_cache, ci + 1, z1);
+          kv_put<KvT>(a.v_cache, ci, y0);
+          if (r1 != r0) kv_put<KvT>(a.v_cache, ci + 1, y1);
         }
-      } else {
-        const int lr = r0 - a.n0 - a.n1;
-        const int64_t ci = ((int64_t)(lr / hd) * a.n_ctx + a.slots[tg]) * hd + (lr % hd);
-        kv_put<KvT>(a.v_cache, ci, y0);
-        if (r1 != r0) kv_put<KvT>(a.v_cache, ci + 1, y1);
       }
     }
   }
@@ -640,26 +709,34 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
   }
 }
 
+// Residual GEMVs always take two rows per wave: their per-block partial sums
+// of x^2 (8 rows per block) feed the next RMSNorm.
 int gemv_residual_parts(int N) { return ((N + 1) / 2 + 3) / 4; }
 
-template <bool BF16, int NT, int EPI, typename KvT>
-static hipError_t gemv_launch_t(const LinearArgs& a, hipStream_t s) {
+template <int WT, int NT, int EPI, typename KvT, int R>
+static hipError_t gemv_launch_r(const LinearArgs& a, hipStream_t s) {
   const int N = a.n0 + a.n1 + a.n2;
-  const int waves = EPI == EPI_SWIGLU ? a.n0 : (N + 1) / 2;
+  constexpr int P = R / 2;
+  const int waves = EPI == EPI_SWIGLU ? (a.n0 + P - 1) / P : (N + R - 1) / R;
   const int blocks = (waves + 3) / 4;
-  // chunks per batch: 8 for a single token on grids of at least 4 waves per
-  // SIMD (the large matrices), else 4 (2 for float32 weights)
-  constexpr int U_MANY = BF16 ? 4 : 2;
-  constexpr int U_BIG = BF16 && NT == 1 ? 8 : U_MANY;
-  const bool big = waves >= 4 * 1024;
+  // chunks per batch at two rows per wave: 8 for a single token on grids of
+  // at least 8192 rows (the large matrices), else 4 (2 for float32 weights);
+  // a Q8_0 chunk holds twice the elements of a bf16 one, so half as many per
+  // batch (one when several tokens' activations share the registers).  Four
+  // rows per wave take half as many chunks per batch.
+  constexpr int U_MANY2 = WT == W_BF16 ? 4 : WT == W_Q8 ? (NT == 1 ? 2 : 1) : 2;
+  constexpr int U_BIG2 = NT == 1 ? (WT == W_BF16 ? 8 : WT == W_Q8 ? 4 : U_MANY2) : U_MANY2;
+  constexpr int U_MANY = R == 2 ? U_MANY2 : (U_MANY2 > 1 ? U_MANY2 / 2 : 1);
+  constexpr int U_BIG = R == 2 ? U_BIG2 : (U_BIG2 > 1 ? U_BIG2 / 2 : 1);
+  const bool big = (int64_t)waves * R >= 8 * 1024;
   for (int t0 = 0; t0 < a.T; t0 += NT) {
     const int nt = a.T - t0 < NT ? a.T - t0 : NT;
     if (a.norm_ssp) {
-      if (big) gemv_kernel<BF16, NT, EPI, KvT, true, U_BIG><<<blocks, 256, 0, s>>>(a, t0, nt);
-      else gemv_kernel<BF16, NT, EPI, KvT, true, U_MANY><<<blocks, 256, 0, s>>>(a, t0, nt);
+      if (big) gemv_kernel<WT, NT, EPI, KvT, true, U_BIG, R><<<blocks, 256, 0, s>>>(a, t0, nt);
+      else gemv_kernel<WT, NT, EPI, KvT, true, U_MANY, R><<<blocks, 256, 0, s>>>(a, t0, nt);
     } else {
-      if (big) gemv_kernel<BF16, NT, EPI, KvT, false, U_BIG><<<blocks, 256, 0, s>>>(a, t0, nt);
-      else gemv_kernel<BF16, NT, EPI, KvT, false, U_MANY><<<blocks, 256, 0, s>>>(a, t0, nt);
+      if (big) gemv_kernel<WT, NT, EPI, KvT, false, U_BIG, R><<<blocks, 256, 0, s>>>(a, t0, nt);
+      else gemv_kernel<WT, NT, EPI, KvT, false, U_MANY, R><<<blocks, 256, 0, s>>>(a, t0, nt);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -667,31 +744,49 @@ static hipError_t gemv_launch_t(const LinearArgs& a, hipStream_t s) {
   return hipSuccess;
 }
 
-template <bool BF16, int NT>
+// rows per wave: 4 for the single-token Q8_0 GEMV of matrices with at least
+// 16384 rows (so that each wave still carries 16 bytes per lane and row for
+// each chunk of a bf16 wave), else 2
+template <int WT, int NT, int EPI, typename KvT>
+static hipError_t gemv_launch_t(const LinearArgs& a, hipStream_t s) {
+  if constexpr (WT == W_Q8 && NT == 1 && EPI != EPI_RESIDUAL) {
+    const int rows = EPI == EPI_SWIGLU ? 2 * a.n0 : a.n0 + a.n1 + a.n2;
+    if (rows >= 16 * 1024) return gemv_launch_r<WT, NT, EPI, KvT, 4>(a, s);
+  }
+  return gemv_launch_r<WT, NT, EPI, KvT, 2>(a, s);
+}
+
+template <int WT, int NT>
 static hipError_t gemv_dispatch_epi(const LinearArgs& a, hipStream_t s) {
   switch (a.epi) {
-    case EPI_STORE: return gemv_launch_t<BF16, NT, EPI_STORE, float>(a, s);
-    case EPI_RESIDUAL: return gemv_launch_t<BF16, NT, EPI_RESIDUAL, float>(a, s);
-    case EPI_SWIGLU: return gemv_launch_t<BF16, NT, EPI_SWIGLU, float>(a, s);
+    case EPI_STORE: return gemv_launch_t<WT, NT, EPI_STORE, float>(a, s);
+    case EPI_RESIDUAL: return gemv_launch_t<WT, NT, EPI_RESIDUAL, float>(a, s);
+    case EPI_SWIGLU: return gemv_launch_t<WT, NT, EPI_SWIGLU, float>(a, s);
     case EPI_QKV:
-      if (a.kv_dtype == TDF_BF16) return gemv_launch_t<BF16, NT, EPI_QKV, kv_bf16>(a, s);
-      if (a.kv_dtype == TDF_F16) return gemv_launch_t<BF16, NT, EPI_QKV, kv_f16>(a, s);
-      return gemv_launch_t<BF16, NT, EPI_QKV, float>(a, s);
+      if (a.kv_dtype == TDF_BF16) return gemv_launch_t<WT, NT, EPI_QKV, kv_bf16>(a, s);
+      if (a.kv_dtype == TDF_F16) return gemv_launch_t<WT, NT, EPI_QKV, kv_f16>(a, s);
+      return gemv_launch_t<WT, NT, EPI_QKV, float>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
+template <int WT>
+static hipError_t gemv_dispatch_tokens(const LinearArgs& a, hipStream_t s) {
+  // tokens per pass: 1 for the latency-critical single-token step, else 8
+  if (a.T == 1) return gemv_dispatch_epi<WT, 1>(a, s);
+  if (a.T <= 4) return gemv_dispatch_epi<WT, 4>(a, s);
+  return gemv_dispatch_epi<WT, 8>(a, s);
+}
+
 hipError_t launch_linear_gemv(const LinearArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  // tokens per pass: 1 for the latency-critical single-token step, else 8
-  if (a.weight_bf16) {
-    if (a.T == 1) return gemv_dispatch_epi<true, 1>(a, s);
-    if (a.T <= 4) return gemv_dispatch_epi<true, 4>(a, s);
-    return gemv_dispatch_epi<true, 8>(a, s);
+  switch (weight_kind(a.weight_dtype)) {
+    case W_BF16: return gemv_dispatch_tokens<W_BF16>(a, s);
+    case W_Q8:
+      if (a.K % 32 != 0) return hipErrorInvalidValue;
+      return gemv_dispatch_tokens<W_Q8>(a, s);
+    default: return gemv_dispatch_tokens<W_F32>(a, s);
   }
-  if (a.T == 1) return gemv_dispatch_epi<false, 1>(a, s);
-  if (a.T <= 4) return gemv_dispatch_epi<false, 4>(a, s);
-  return gemv_dispatch_epi<false, 8>(a, s);
 }
 
 }  // namespace tdf

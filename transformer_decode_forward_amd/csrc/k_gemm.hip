@@ -231,7 +231,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
 }
 
 bool gemm_supported(const LinearArgs& a) {
-  return a.weight_bf16 && a.act_hi && a.act_lo && a.K % GBK == 0 && a.K >= GBK;
+  return a.weight_dtype == TDF_BF16 && a.act_hi && a.act_lo && a.K % GBK == 0 && a.K >= GBK;
 }
 
 template <int EPI, typename KvT, int MT, int NT>

@@ -186,7 +186,7 @@ __global__ void __launch_bounds__(256) skinny_epilogue_kernel(SkinnyArgs s) {
 
 bool skinny_supported(const LinearArgs& a) {
   const int N = a.epi == EPI_SWIGLU ? 2 * a.n0 : a.n0 + a.n1 + a.n2;
-  return a.weight_bf16 && a.act_hi && a.act_lo && a.T > 0 && a.T <= 32 && a.K % kSkChunk == 0 &&
+  return a.weight_dtype == TDF_BF16 && a.act_hi && a.act_lo && a.T > 0 && a.T <= 32 && a.K % kSkChunk == 0 &&
          (int64_t)N * 32 <= kSkinnyPartFloats && (a.epi != EPI_QKV || (a.n0 % 2 == 0 && a.n1 % 2 == 0));
 }
 

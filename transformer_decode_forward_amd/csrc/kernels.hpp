@@ -25,7 +25,9 @@ struct LinearArgs {
   int n0 = 0, n1 = 0, n2 = 0;  // rows of each matrix
   int K = 0;                   // inner size (row length)
   int T = 0;                   // tokens (rows of act)
-  int weight_bf16 = 1;         // 1: bf16 weights, 0: float32
+  // TDF_BF16, TDF_F32 or TDF_Q8_0 (each matrix one buffer: rows*K int8, then
+  // its fp16 block scales [rows][K/32])
+  int weight_dtype = TDF_BF16;
   // activations: float32 [T][K] (GEMV), or a bf16 pair hi + lo [T][K] (GEMM)
   const float* act_f32 = nullptr;
   // GEMV RMSNorm consumer: when norm_ssp is set, act_f32 holds u = g * x (the
@@ -72,8 +74,9 @@ bool skinny_supported(const LinearArgs& a);
 hipError_t launch_linear_skinny(const LinearArgs& a, float* part, hipStream_t s);
 
 // x[t][:] = E[token[t]][:] (to float32); with g set also u = g * x and
-// ssp[t * stride] = sum x^2 (one partial per row)
-hipError_t launch_embed(const void* table, int weight_bf16, const int32_t* tokens, int T, int d,
+// ssp[t * stride] = sum x^2 (one partial per row).  n_rows: rows of the
+// table (a Q8_0 table's scales start at byte n_rows * d)
+hipError_t launch_embed(const void* table, int weight_dtype, int n_rows, const int32_t* tokens, int T, int d,
                         float* x, const float* g, float* u, float* ssp, int stride, hipStream_t s);
 // number of blocks (= partial sums) a residual GEMV writes for N rows
 int gemv_residual_parts(int N);

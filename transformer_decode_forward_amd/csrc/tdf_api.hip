@@ -298,7 +298,14 @@ extern "C" tdf_model* tdf_model_create(const tdf_hparams* hp, const tdf_weights*
     set_err("invalid hparams");
     return nullptr;
   }
-  if (h.weight_dtype != TDF_F32 && h.weight_dtype != TDF_BF16) { set_err("weight_dtype must be F32 or BF16"); return nullptr; }
+  if (h.weight_dtype != TDF_F32 && h.weight_dtype != TDF_BF16 && h.weight_dtype != TDF_Q8_0) {
+    set_err("weight_dtype must be F32, BF16 or Q8_0");
+    return nullptr;
+  }
+  if (h.weight_dtype == TDF_Q8_0 && (h.n_embd % 32 || (h.n_head * h.head_dim) % 32 || h.n_ff % 32)) {
+    set_err("Q8_0 weights need n_embd, n_head*head_dim and n_ff to be multiples of 32");
+    return nullptr;
+  }
   const int G = h.n_head / h.n_head_kv;
   if (!(G == 1 || G == 2 || G == 4 || G == 8)) { set_err("n_head / n_head_kv must be 1, 2, 4 or 8"); return nullptr; }
   if (!(h.head_dim == 16 || h.head_dim == 32 || h.head_dim == 64 || h.head_dim == 128)) {
@@ -497,7 +504,7 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
 
   const bool first_gemv = !use_mfma(T, d);
   int ps = prof_begin(c, TDF_OP_EMBED, !first_gemv);
-  TDF_HIP(launch_embed(m->token_embd, wbf16, u.tokens, T, d, c->x, first_gemv ? attn_gain(0) : nullptr,
+  TDF_HIP(launch_embed(m->token_embd, h.weight_dtype, V, u.tokens, T, d, c->x, first_gemv ? attn_gain(0) : nullptr,
                        c->u, c->ssp, c->ssp_stride, s));
   TDF_HIP(launch_scatter(c->cell_list, u.list_writes, u.n_list_writes, s));
   TDF_HIP(launch_rope_table(u.pos, c->inv_freq, T, hd / 2, c->rope_cs, s));
@@ -518,7 +525,7 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     LinearArgs qa;
     qa.w0 = W.wq; qa.w1 = W.wk; qa.w2 = W.wv;
     qa.n0 = H * hd; qa.n1 = Hkv * hd; qa.n2 = Hkv * hd;
-    qa.K = d; qa.T = T; qa.weight_bf16 = wbf16;
+    qa.K = d; qa.T = T; qa.weight_dtype = h.weight_dtype;
     qa.act_f32 = c->u; qa.act_hi = c->h_hi; qa.act_lo = c->h_lo;
     qa.norm_ssp = c->ssp; qa.norm_nparts = u_parts; qa.norm_stride = c->ssp_stride; qa.norm_eps = h.rms_eps;
     qa.epi = EPI_QKV;
@@ -585,7 +592,7 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     const int T_mlp = last ? u.R : T;
     const bool bigm = use_mfma(T_mlp, d) && use_mfma(T_mlp, F);
     LinearArgs oa;
-    oa.w0 = W.wo; oa.n0 = d; oa.K = H * hd; oa.T = T; oa.weight_bf16 = wbf16;
+    oa.w0 = W.wo; oa.n0 = d; oa.K = H * hd; oa.T = T; oa.weight_dtype = h.weight_dtype;
     oa.act_f32 = c->o; oa.act_hi = c->o_hi; oa.act_lo = c->o_lo;
     oa.epi = EPI_RESIDUAL; oa.out = cur; oa.ldo = d;
     const bool wo_mfma = big && use_mfma(T, H * hd);
@@ -616,14 +623,14 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
       if (int rc = prep_norm((const float*)W.ffn_norm, T)) return rc;
     }
     LinearArgs ga;
-    ga.w0 = W.w_gate; ga.w1 = W.w_up; ga.n0 = F; ga.K = d; ga.T = T; ga.weight_bf16 = wbf16;
+    ga.w0 = W.w_gate; ga.w1 = W.w_up; ga.n0 = F; ga.K = d; ga.T = T; ga.weight_dtype = h.weight_dtype;
     ga.act_f32 = c->u; ga.act_hi = c->h_hi; ga.act_lo = c->h_lo;
     ga.norm_ssp = c->ssp; ga.norm_nparts = u_parts; ga.norm_stride = c->ssp_stride; ga.norm_eps = h.rms_eps;
     ga.epi = EPI_SWIGLU; ga.out = c->mb; ga.out_hi = c->m_hi; ga.out_lo = c->m_lo; ga.ldo = F;
     if (int rc = run_linear(c, ga, bigm, TDF_OP_GATE_UP)) return rc;
     u_parts = 0;
     LinearArgs da;
-    da.w0 = W.w_down; da.n0 = d; da.K = F; da.T = T; da.weight_bf16 = wbf16;
+    da.w0 = W.w_down; da.n0 = d; da.K = F; da.T = T; da.weight_dtype = h.weight_dtype;
     da.act_f32 = c->mb; da.act_hi = c->m_hi; da.act_lo = c->m_lo;
     da.epi = EPI_RESIDUAL; da.out = cur; da.ldo = d;
     const bool next_gemv = last ? !use_mfma(T, d) : !use_mfma(T, d);
@@ -652,7 +659,7 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     if (int rc = prep_norm(m->output_norm, T)) return rc;
   }
   LinearArgs la;
-  la.w0 = m->output; la.n0 = V; la.K = d; la.T = T; la.weight_bf16 = wbf16;
+  la.w0 = m->output; la.n0 = V; la.K = d; la.T = T; la.weight_dtype = h.weight_dtype;
   la.act_f32 = c->u; la.act_hi = c->h_hi; la.act_lo = c->h_lo;
   la.norm_ssp = c->ssp; la.norm_nparts = u_parts; la.norm_stride = c->ssp_stride; la.norm_eps = h.rms_eps;
   la.epi = EPI_STORE; la.out = c->logits + (size_t)u.out_row0 * V; la.ldo = V;
@@ -1243,7 +1250,7 @@ extern "C" int32_t tdf_time_op(tdf_context* c, int32_t op, int32_t n_tokens, int
   const bool mfma = wbf16 && T > kGemvMaxT && K % 64 == 0;
   auto args = [&](int l) {
     LinearArgs a;
-    a.T = T; a.weight_bf16 = wbf16;
+    a.T = T; a.weight_dtype = h.weight_dtype;
     if (op == TDF_OP_GATE_UP) {
       const tdf_layer_weights& W = m->layers[l];
       a.w0 = W.w_gate; a.w1 = W.w_up; a.n0 = F; a.K = d;
