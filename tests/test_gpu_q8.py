@@ -2,11 +2,14 @@
 scale times 32 int8 values) against the float64 oracle, which dequantizes
 the same buffers exactly.
 
-Every product d * q is exact in float32, so with a float32 cache the only
-differences are float32 rounding of the sums: the float32 tolerance
-(max-abs 1e-4, rel-L2 1e-5) applies.  With a bf16 cache the cache
-rounding is shared with the oracle but the attention runs on the matrix
-cores with bf16 hi/lo operands: the bf16 tolerance applies.
+Every product d * q is exact in float32.  Where every step runs on the
+vector units (the GEMV for ubatches of up to 8 tokens, or inner sizes that
+are not multiples of 64) with a float32 cache, the only differences are
+float32 rounding of the sums: the float32 tolerance (max-abs 1e-4, rel-L2
+1e-5) applies.  Larger ubatches run the matrix cores (int8 values widened
+exactly to bf16, activations as a bf16 hi/lo pair, one block scale per 32
+products), and a bf16 cache feeds the matrix-core attention: there the bf16
+tolerance applies.
 
 Sizes: the GEMV reads a row in chunks of 1024 int8 (16 per lane), so the
 inner sizes 1056 and 2080 take full chunks plus a ragged 32-element tail;
@@ -33,15 +36,35 @@ Q8_MID = dict(n_vocab=8200, n_embd=1056, n_layer=2, n_head=8, n_head_kv=2, head_
 
 @pytest.mark.parametrize("kv_dtype,tied", [("f32", False), ("bf16", False), ("f32", True)])
 def test_q8_small_prefill_and_steps(kv_dtype, tied):
-    """150 tokens in ubatches of 64, 64, 22, logits for every row, then three
-    single-token steps; tied: the LM head reads the Q8_0 embedding table."""
+    """150 tokens in ubatches of 64, 64, 22 (matrix cores: a 22-row tile
+    included), logits for every row, then three single-token steps (GEMV);
+    tied: the LM head reads the Q8_0 embedding table."""
     cfg, w = make_weights(dict(Q8_SMALL, tied=tied))
     prompt = tdf_synth.prompt(cfg, 0, 150)
     nxt = tdf_synth.prompt(cfg, 1, 3)
     calls = [dict(tokens=prompt)] + [dict(tokens=[int(t)]) for t in nxt]
-    tol = TOL_F32 if kv_dtype == "f32" else TOL_BF16
     log(f"q8 small kv={kv_dtype} tied={tied}")
-    run_pair(cfg, w, dict(n_ctx=256, n_ubatch=64, output_all=True), calls, tol, kv_dtype, "q8-small")
+    run_pair(cfg, w, dict(n_ctx=256, n_ubatch=64, output_all=True), calls, TOL_BF16, kv_dtype, "q8-small")
+
+
+def test_q8_small_vector_units_f32_tolerance():
+    """Ubatches of at most 8 tokens stay on the vector units: with a float32
+    cache the float32 tolerance holds."""
+    cfg, w = make_weights(Q8_SMALL)
+    prompt = tdf_synth.prompt(cfg, 0, 24)
+    calls = [dict(tokens=prompt[i:i + 8], logits=np.ones(8, dtype=np.int8)) for i in range(0, 24, 8)]
+    calls += [dict(tokens=[int(t)]) for t in tdf_synth.prompt(cfg, 1, 2)]
+    run_pair(cfg, w, dict(n_ctx=64, n_ubatch=8), calls, TOL_F32, "f32", "q8-small-gemv")
+
+
+def test_q8_llama1b_width_two_layers():
+    """1B-class widths with Q8_0 weights, two layers: 300-token prompt in
+    ubatches of 128, 128, 44 on the matrix cores (several 64x128 tiles, the
+    residual projections split over K, a ragged last tile), then 4 steps."""
+    cfg = dict(tdf_synth.CONFIGS["llama1b"], weight_dtype="q8_0")
+    cfg, w = make_weights(cfg, layers=2)
+    prompt = tdf_synth.prompt(cfg, 0, 300)
+    teacher_forced(cfg, w, 512, prompt, 4, TOL_BF16, "f16", n_ubatch=128, label="q8-1b-2L")
 
 
 @pytest.mark.parametrize("kv_dtype", ["f32", "bf16"])

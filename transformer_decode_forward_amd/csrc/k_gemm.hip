@@ -17,6 +17,13 @@
 // and down projections (split over K with atomic adds when the tiles alone
 // would leave CUs idle).
 //
+// Q8_0 weights (blocks of 32 int8 of a row with one fp16 scale): the int8
+// values are exact in bf16, so they are widened to bf16 while being staged
+// into LDS and enter the same MFMAs unscaled; each 32-deep block's products
+// are collected in a temporary accumulator and added to the tile scaled by
+// the block scale of their column (exact weights, one FMA per output per
+// block).
+//
 // Tiling: 256 threads = 4 waves in a 2 x 2 grid; wave tile (32 MT) x (32 NT)
 // = MT x NT MFMA tiles of 32 x 32, block tile (64 MT) x (64 NT) x 64.  Tiles
 // go through LDS (row pitch 72 bf16 to spread banks) with the next K tile
@@ -41,15 +48,32 @@ __device__ __forceinline__ void split_store(uint16_t* hi, uint16_t* lo, int64_t 
   split_bf16(v, hi[i], lo[i]);
 }
 
-template <int EPI, typename KvT, int MT, int NT>
+// 8 int8 -> 8 bf16 (exact: at most 8 significant bits)
+__device__ __forceinline__ bf16x8 widen_i8x8(uint2 q) {
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = j < 2 ? q.x : q.y;
+    const int b = (j & 1) * 2;
+    const uint32_t f0 = __builtin_bit_cast(uint32_t, (float)((int32_t)(w << (24 - 8 * b)) >> 24));
+    const uint32_t f1 = __builtin_bit_cast(uint32_t, (float)((int32_t)(w << (16 - 8 * b)) >> 24));
+    o[j] = (f0 >> 16) | (f1 & 0xFFFF0000u);
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+template <int EPI, typename KvT, int MT, int NT, bool Q8>
 __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int tiles_m, int tiles_n,
                                                    int ksplit) {
   constexpr int BM = 64 * MT, BN = 64 * NT;
   constexpr int A_PER = BM * 8 / 256;   // 16-byte A pieces per thread (each of hi, lo)
-  constexpr int B_PER = BN * 8 / 256;   // 16-byte B pieces per thread
+  constexpr int B_PER = BN * 8 / 256;   // B pieces of 8 weights per thread
+  static_assert(BN <= 256, "one scale pair per thread");
   __shared__ __attribute__((aligned(16))) uint16_t Ah[BM * GPITCH];
   __shared__ __attribute__((aligned(16))) uint16_t Al[BM * GPITCH];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * GPITCH];
+  // Q8_0: the two block scales (fp16) of each B row for the current K tile
+  __shared__ uint32_t Ss[Q8 ? BN : 1];
 
   const int total = tiles_m * tiles_n * ksplit;
   int b = blockIdx.x;
@@ -82,24 +106,48 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
     ap_hi[i] = a.act_hi + (int64_t)gm * K + kc;
     ap_lo[i] = a.act_lo + (int64_t)gm * K + kc;
   }
-  const uint16_t* bp[B_PER];
-#pragma unroll
-  for (int i = 0; i < B_PER; ++i) {
-    const int r = (tid >> 3) + 32 * i;
+  // B row r of the block tile: its matrix, row in that matrix and the
+  // matrix's row count (rows past the end clamped to a valid row)
+  auto b_row = [&](int r, const void*& w, int64_t& row, int& rows) {
     if (EPI == EPI_SWIGLU) {
       constexpr int WN = BN / 2, HALF = WN / 2;
       const int part = r / WN, rr = r % WN;
-      const int f = min(n0 + part * HALF + (rr % HALF), a.n0 - 1);
-      bp[i] = (const uint16_t*)(rr >= HALF ? a.w1 : a.w0) + (int64_t)f * K + kc;
+      row = min(n0 + part * HALF + (rr % HALF), a.n0 - 1);
+      w = rr >= HALF ? a.w1 : a.w0;
+      rows = a.n0;
     } else {
       const int gr = min(n0 + r, Ntot - 1);
-      if (gr < a.n0) bp[i] = (const uint16_t*)a.w0 + (int64_t)gr * K + kc;
-      else if (gr < a.n0 + a.n1) bp[i] = (const uint16_t*)a.w1 + (int64_t)(gr - a.n0) * K + kc;
-      else bp[i] = (const uint16_t*)a.w2 + (int64_t)(gr - a.n0 - a.n1) * K + kc;
+      if (gr < a.n0) { w = a.w0; row = gr; rows = a.n0; }
+      else if (gr < a.n0 + a.n1) { w = a.w1; row = gr - a.n0; rows = a.n1; }
+      else { w = a.w2; row = gr - a.n0 - a.n1; rows = a.n2; }
     }
+  };
+  // bf16: element pointers; Q8_0: byte pointers to the int8 values
+  const char* bp[B_PER];
+#pragma unroll
+  for (int i = 0; i < B_PER; ++i) {
+    const void* w;
+    int64_t row;
+    int rows;
+    b_row((tid >> 3) + 32 * i, w, row, rows);
+    bp[i] = (const char*)w + (row * K + kc) * (Q8 ? 1 : 2);
   }
+  // Q8_0: thread r < BN fetches the scale pair of B row r for each K tile
+  const uint32_t* sp = nullptr;
+  if (Q8 && tid < BN) {
+    const void* w;
+    int64_t row;
+    int rows;
+    b_row(tid, w, row, rows);
+    sp = (const uint32_t*)((const int8_t*)w + (int64_t)rows * K) + row * (K / 64);
+  }
+  auto load_b = [&](int i, int k) -> bf16x8 {
+    if (Q8) return widen_i8x8(*(const uint2*)(bp[i] + k));
+    return *(const bf16x8*)(bp[i] + 2 * (int64_t)k);
+  };
 
   bf16x8 rah[A_PER], ral[A_PER], rb[B_PER];
+  uint32_t rs = 0;
 
   f32x16 acc[MT][NT];
 #pragma unroll
@@ -116,7 +164,8 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
     ral[i] = *(const bf16x8*)(ap_lo[i] + k_begin);
   }
 #pragma unroll
-  for (int i = 0; i < B_PER; ++i) rb[i] = *(const bf16x8*)(bp[i] + k_begin);
+  for (int i = 0; i < B_PER; ++i) rb[i] = load_b(i, k_begin);
+  if (Q8 && sp) rs = sp[k_begin / GBK];
 #pragma unroll
   for (int i = 0; i < A_PER; ++i) {
     const int r = (tid >> 3) + 32 * i;
@@ -125,6 +174,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
   }
 #pragma unroll
   for (int i = 0; i < B_PER; ++i) *(bf16x8*)&Bs[((tid >> 3) + 32 * i) * GPITCH + kc] = rb[i];
+  if (Q8 && tid < BN) Ss[tid] = rs;
   __syncthreads();
 
   const int frow = lane & 31;
@@ -140,8 +190,48 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
         ral[i] = *(const bf16x8*)(ap_lo[i] + kn);
       }
 #pragma unroll
-      for (int i = 0; i < B_PER; ++i) rb[i] = *(const bf16x8*)(bp[i] + kn);
+      for (int i = 0; i < B_PER; ++i) rb[i] = load_b(i, kn);
+      if (Q8 && sp) rs = sp[kn / GBK];
     }
+    if (Q8) {
+      // per 32-deep block: unscaled products into tmp, then
+      // acc += scale(column, block) * tmp
+#pragma unroll
+      for (int blk = 0; blk < GBK / 32; ++blk) {
+        bf16x8 ah[2][MT], al[2][MT], bfr[2][NT];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kk = blk * 32 + h * 16;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const int r = (wm * 32 * MT + mt * 32 + frow) * GPITCH + kk + fk;
+            ah[h][mt] = *(const bf16x8*)&Ah[r];
+            al[h][mt] = *(const bf16x8*)&Al[r];
+          }
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            bfr[h][nt] = *(const bf16x8*)&Bs[(wn * 32 * NT + nt * 32 + frow) * GPITCH + kk + fk];
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const uint32_t sc2 = Ss[wn * 32 * NT + nt * 32 + frow];
+          const float sc = f16_to_f32((uint16_t)(blk ? sc2 >> 16 : sc2 & 0xFFFFu));
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            f32x16 tmp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tmp[r] = 0.f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              tmp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[h][mt], bfr[h][nt], tmp, 0, 0, 0);
+              tmp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[h][mt], bfr[h][nt], tmp, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mt][nt][r] = fmaf(sc, tmp[r], acc[mt][nt][r]);
+          }
+        }
+      }
+    } else
 #pragma unroll
     for (int kk = 0; kk < GBK; kk += 16) {
       bf16x8 ah[MT], al[MT], bfr[NT];
@@ -172,6 +262,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
       }
 #pragma unroll
       for (int i = 0; i < B_PER; ++i) *(bf16x8*)&Bs[((tid >> 3) + 32 * i) * GPITCH + kc] = rb[i];
+      if (Q8 && tid < BN) Ss[tid] = rs;
       __syncthreads();
     }
   }
@@ -231,7 +322,8 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
 }
 
 bool gemm_supported(const LinearArgs& a) {
-  return a.weight_dtype == TDF_BF16 && a.act_hi && a.act_lo && a.K % GBK == 0 && a.K >= GBK;
+  return (a.weight_dtype == TDF_BF16 || a.weight_dtype == TDF_Q8_0) && a.act_hi && a.act_lo &&
+         a.K % GBK == 0 && a.K >= GBK;
 }
 
 template <int EPI, typename KvT, int MT, int NT>
@@ -240,7 +332,14 @@ static hipError_t gemm_launch_tile(const LinearArgs& a, int ksplit, hipStream_t 
   const int tiles_m = (M + 64 * MT - 1) / (64 * MT);
   const int Ntot = a.n0 + a.n1 + a.n2;
   const int tiles_n = EPI == EPI_SWIGLU ? (a.n0 + 32 * NT - 1) / (32 * NT) : (Ntot + 64 * NT - 1) / (64 * NT);
-  gemm_kernel<EPI, KvT, MT, NT><<<tiles_m * tiles_n * ksplit, 256, 0, s>>>(a, M, tiles_m, tiles_n, ksplit);
+  if (a.weight_dtype == TDF_Q8_0) {
+    if constexpr (MT == 1 && NT == 2)
+      gemm_kernel<EPI, KvT, MT, NT, true><<<tiles_m * tiles_n * ksplit, 256, 0, s>>>(a, M, tiles_m, tiles_n, ksplit);
+    else
+      return hipErrorInvalidValue;
+  } else {
+    gemm_kernel<EPI, KvT, MT, NT, false><<<tiles_m * tiles_n * ksplit, 256, 0, s>>>(a, M, tiles_m, tiles_n, ksplit);
+  }
   return hipGetLastError();
 }
 
@@ -255,8 +354,11 @@ static hipError_t gemm_launch_t(const LinearArgs& a, hipStream_t s) {
   const int M = a.T;
   const int Ntot = EPI == EPI_SWIGLU ? 2 * a.n0 : a.n0 + a.n1 + a.n2;
   const int nkt = a.K / GBK;
-  const int b24 = ((M + 127) / 128) * ((Ntot + 255) / 256);
-  const int b22 = ((M + 127) / 128) * ((Ntot + 127) / 128);
+  // Q8_0 weights take the 64x128 tile only (the block-scale accumulators of
+  // the larger tiles do not fit in the registers)
+  const bool q8 = a.weight_dtype == TDF_Q8_0;
+  const int b24 = q8 ? 0 : ((M + 127) / 128) * ((Ntot + 255) / 256);
+  const int b22 = q8 ? 0 : ((M + 127) / 128) * ((Ntot + 127) / 128);
   const int b12 = ((M + 63) / 64) * ((Ntot + 127) / 128);
   if (EPI == EPI_RESIDUAL) {
     for (int ks = 1; ks <= 8; ks *= 2) {

@@ -482,10 +482,11 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
   const tdf_hparams& h = m->hp;
   const int d = h.n_embd, H = h.n_head, Hkv = h.n_head_kv, hd = h.head_dim, F = h.n_ff, V = h.n_vocab;
   const int L = h.n_layer;
-  const bool wbf16 = h.weight_dtype == TDF_BF16;
+  // bf16 and Q8_0 weights have matrix-core paths
+  const bool wmfma = h.weight_dtype == TDF_BF16 || h.weight_dtype == TDF_Q8_0;
   hipStream_t s = c->stream;
   int T = u.T;
-  auto use_mfma = [&](int rows, int K) { return wbf16 && rows > kGemvMaxT && K % 64 == 0; };
+  auto use_mfma = [&](int rows, int K) { return wmfma && rows > kGemvMaxT && K % 64 == 0; };
   auto attn_gain = [&](int l) { return (const float*)(l < L ? m->layers[l].attn_norm : m->output_norm); };
 
   // RMSNorm hand-off to the decode GEMV: c->u holds g * x of the rows in
@@ -1238,7 +1239,7 @@ extern "C" int32_t tdf_time_op(tdf_context* c, int32_t op, int32_t n_tokens, int
   const tdf_model* m = c->m;
   const tdf_hparams& h = m->hp;
   const int d = h.n_embd, F = h.n_ff, V = h.n_vocab, L = h.n_layer, T = n_tokens;
-  const bool wbf16 = h.weight_dtype == TDF_BF16;
+  const bool wmfma = h.weight_dtype == TDF_BF16 || h.weight_dtype == TDF_Q8_0;
   if (op == TDF_OP_LM_HEAD && c->logits_cap < T) {
     if (int rc = ensure_logits(c, T)) return rc;
   }
@@ -1247,7 +1248,7 @@ extern "C" int32_t tdf_time_op(tdf_context* c, int32_t op, int32_t n_tokens, int
     return TDF_E_INVALID;
   }
   const int K = op == TDF_OP_DOWN ? F : d;
-  const bool mfma = wbf16 && T > kGemvMaxT && K % 64 == 0;
+  const bool mfma = wmfma && T > kGemvMaxT && K % 64 == 0;
   auto args = [&](int l) {
     LinearArgs a;
     a.T = T; a.weight_dtype = h.weight_dtype;
