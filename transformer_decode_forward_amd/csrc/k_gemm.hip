@@ -31,6 +31,8 @@
 // m tiles and K splits of one n tile run back to back on one XCD (dispatch is
 // round-robin over the 8 XCDs), keeping a weight tile's re-reads in that
 // XCD's L2.
+#include <type_traits>
+
 #include "k_common.hpp"
 #include "kernels.hpp"
 #include "tdf.h"
@@ -122,15 +124,16 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
       else { w = a.w2; row = gr - a.n0 - a.n1; rows = a.n2; }
     }
   };
-  // bf16: element pointers; Q8_0: byte pointers to the int8 values
-  const char* bp[B_PER];
+  // B pieces: bf16 element pointers, or Q8_0 pointers to the int8 values
+  typedef typename std::conditional<Q8, const int8_t*, const uint16_t*>::type BPtr;
+  BPtr bp[B_PER];
 #pragma unroll
   for (int i = 0; i < B_PER; ++i) {
     const void* w;
     int64_t row;
     int rows;
     b_row((tid >> 3) + 32 * i, w, row, rows);
-    bp[i] = (const char*)w + (row * K + kc) * (Q8 ? 1 : 2);
+    bp[i] = (BPtr)w + row * K + kc;
   }
   // Q8_0: thread r < BN fetches the scale pair of B row r for each K tile
   const uint32_t* sp = nullptr;
@@ -141,12 +144,19 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
     b_row(tid, w, row, rows);
     sp = (const uint32_t*)((const int8_t*)w + (int64_t)rows * K) + row * (K / 64);
   }
-  auto load_b = [&](int i, int k) -> bf16x8 {
-    if (Q8) return widen_i8x8(*(const uint2*)(bp[i] + k));
-    return *(const bf16x8*)(bp[i] + 2 * (int64_t)k);
+  // B prefetch registers: 8 bf16, or 8 int8 widened when stored to LDS
+  typedef typename std::conditional<Q8, uint2, bf16x8>::type BRaw;
+  auto load_b = [&](int i, int k) -> BRaw {
+    if constexpr (Q8) return *(const uint2*)(bp[i] + k);
+    else return *(const bf16x8*)(bp[i] + k);
+  };
+  auto b_lds = [&](BRaw v) -> bf16x8 {
+    if constexpr (Q8) return widen_i8x8(v);
+    else return v;
   };
 
-  bf16x8 rah[A_PER], ral[A_PER], rb[B_PER];
+  bf16x8 rah[A_PER], ral[A_PER];
+  BRaw rb[B_PER];
   uint32_t rs = 0;
 
   f32x16 acc[MT][NT];
@@ -173,7 +183,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
     *(bf16x8*)&Al[r * GPITCH + kc] = ral[i];
   }
 #pragma unroll
-  for (int i = 0; i < B_PER; ++i) *(bf16x8*)&Bs[((tid >> 3) + 32 * i) * GPITCH + kc] = rb[i];
+  for (int i = 0; i < B_PER; ++i) *(bf16x8*)&Bs[((tid >> 3) + 32 * i) * GPITCH + kc] = b_lds(rb[i]);
   if (Q8 && tid < BN) Ss[tid] = rs;
   __syncthreads();
 
@@ -194,41 +204,44 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
       if (Q8 && sp) rs = sp[kn / GBK];
     }
     if (Q8) {
-      // per 32-deep block: unscaled products into tmp, then
-      // acc += scale(column, block) * tmp
+      // per 32-deep block and column tile: unscaled products into tmp, then
+      // acc += scale(column, block) * tmp (the block's A fragments stay in
+      // registers across the column tiles)
 #pragma unroll
       for (int blk = 0; blk < GBK / 32; ++blk) {
-        bf16x8 ah[2][MT], al[2][MT], bfr[2][NT];
+        bf16x8 ah[2][MT], al[2][MT];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int kk = blk * 32 + h * 16;
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            const int r = (wm * 32 * MT + mt * 32 + frow) * GPITCH + kk + fk;
+            const int r = (wm * 32 * MT + mt * 32 + frow) * GPITCH + blk * 32 + h * 16 + fk;
             ah[h][mt] = *(const bf16x8*)&Ah[r];
             al[h][mt] = *(const bf16x8*)&Al[r];
           }
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            bfr[h][nt] = *(const bf16x8*)&Bs[(wn * 32 * NT + nt * 32 + frow) * GPITCH + kk + fk];
-        }
-#pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
+          bf16x8 bfr[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            bfr[h] = *(const bf16x8*)&Bs[(wn * 32 * NT + nt * 32 + frow) * GPITCH + blk * 32 + h * 16 + fk];
+          f32x16 tmp[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tmp[mt][r] = 0.f;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              tmp[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[h][mt], bfr[h], tmp[mt], 0, 0, 0);
+              tmp[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[h][mt], bfr[h], tmp[mt], 0, 0, 0);
+            }
           const uint32_t sc2 = Ss[wn * 32 * NT + nt * 32 + frow];
           const float sc = f16_to_f32((uint16_t)(blk ? sc2 >> 16 : sc2 & 0xFFFFu));
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            f32x16 tmp;
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) tmp[r] = 0.f;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              tmp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[h][mt], bfr[h][nt], tmp, 0, 0, 0);
-              tmp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[h][mt], bfr[h][nt], tmp, 0, 0, 0);
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[mt][nt][r] = fmaf(sc, tmp[r], acc[mt][nt][r]);
-          }
+            for (int r = 0; r < 16; ++r) acc[mt][nt][r] = fmaf(sc, tmp[mt][r], acc[mt][nt][r]);
         }
       }
     } else
@@ -261,7 +274,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
         *(bf16x8*)&Al[r * GPITCH + kc] = ral[i];
       }
 #pragma unroll
-      for (int i = 0; i < B_PER; ++i) *(bf16x8*)&Bs[((tid >> 3) + 32 * i) * GPITCH + kc] = rb[i];
+      for (int i = 0; i < B_PER; ++i) *(bf16x8*)&Bs[((tid >> 3) + 32 * i) * GPITCH + kc] = b_lds(rb[i]);
       if (Q8 && tid < BN) Ss[tid] = rs;
       __syncthreads();
     }
