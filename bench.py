@@ -39,9 +39,13 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16
 COPY_BYTES = 1 << 30         # calibration copy: 1 GiB read + 1 GiB written
 TRAFFIC_FILES = {"decode": "profiles/gemv_gate_up_decode_llama8b_traffic.json",
-                 "prefill": "profiles/gemm_gate_up_prefill512_llama8b_traffic.json"}
+                 "prefill": "profiles/gemm_gate_up_prefill512_llama8b_traffic.json",
+                 "decode_q8_0": "profiles/gemv_gate_up_decode_llama8b_q8_0_traffic.json",
+                 "prefill_q8_0": "profiles/gemm_gate_up_prefill512_llama8b_q8_0_traffic.json"}
 KERNEL_SOURCES = {"decode": "transformer_decode_forward_amd/csrc/k_decode.hip",
-                  "prefill": "transformer_decode_forward_amd/csrc/k_gemm.hip"}
+                  "prefill": "transformer_decode_forward_amd/csrc/k_gemm.hip",
+                  "decode_q8_0": "transformer_decode_forward_amd/csrc/k_decode.hip",
+                  "prefill_q8_0": "transformer_decode_forward_amd/csrc/k_gemm.hip"}
 
 
 def log(msg):
@@ -504,11 +508,11 @@ def main():
                     "frac_mfma_peak": round(pre_flops / t_pre / 1e12 / MFMA_BF16_PEAK_TFS, 4)},
         "roofline": {"bound": "hbm", "kernel": "gate/up GEMV + SwiGLU (decode)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None if q8 else traffic("decode"),
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic("decode_q8_0" if q8 else "decode"),
                      "avg_launch_us": round(gu_us, 2), "bytes_per_launch": gu_bytes},
         "roofline_prefill": {"bound": "mfma", "kernel": "gate/up GEMM + SwiGLU (prefill ubatch 512)",
                              "achieved": round(gg_tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                             "frac": round(gg_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None if q8 else traffic("prefill"),
+                             "frac": round(gg_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic("prefill_q8_0" if q8 else "prefill"),
                              "avg_launch_us": round(gg_us, 2), "flops_per_launch": gg_flops,
                              "executed_flops_per_launch": 2 * gg_flops},
         "measured_peaks": peaks,
