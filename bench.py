@@ -200,7 +200,8 @@ def decode_bytes_multi(cfg, ctxs):
                                              "n_vocab", "n_layer"))
     p_layer = d * H * hd + 2 * d * Hkv * hd + H * hd * d + 3 * d * F
     kv_cell = L * 2 * Hkv * hd * 2
-    return 2 * (L * p_layer + V * d) + kv_cell * (sum(ctxs) + len(ctxs)) + 4 * V * len(ctxs)
+    return (weight_bytes_per_element(cfg) * (L * p_layer + V * d) + kv_cell * (sum(ctxs) + len(ctxs))
+            + 4 * V * len(ctxs))
 
 
 def run_multiseq(args, cfg):
@@ -242,10 +243,12 @@ def run_multiseq(args, cfg):
     tps = S * args.steps / t_dec
     log(f"prefill {lens.sum() / t_pre:.0f} tok/s, decode {tps:.1f} tok/s ({ms:.3f} ms per 32-token step)")
     return {
-        "metric": "decode tok/s (% HBM peak), 8B-shape bf16, 32 sequences",
+        "metric": "decode tok/s (% HBM peak), 8B-shape bf16, 32 sequences" if cfg["weight_dtype"] == "bf16" else
+                  f"decode tok/s (% HBM peak), 8B-shape {cfg['weight_dtype'].upper()} weights, 32 sequences",
         "value": round(tps, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "dtype": "bf16" if cfg["weight_dtype"] == "bf16" else f"f32 ({cfg['weight_dtype']} weights)",
+        "data": "synthetic",
         "config": {"workload": f"llama8b_multiseq: {S} sequences, prompts {int(lens.min())}..{int(lens.max())} "
                                f"tokens prefilled per sequence, then lock-step steps of {S} tokens, all rows' logits; "
                                f"KV bf16 {cfg['n_ctx']} cells"},

@@ -29,6 +29,10 @@ from test_gpu_parity import SMALL, run_pair, teacher_forced
 pytestmark = pytest.mark.gpu
 
 Q8_SMALL = dict(SMALL, weight_dtype="q8_0", seed=21)
+# inner sizes 512 and 1024: four and eight 128-wide chunks for the 9..32-token path
+Q8_SK = dict(n_vocab=1000, n_embd=512, n_layer=2, n_head=8, n_head_kv=2, head_dim=64, n_ff=1024,
+             rms_eps=1e-5, rope_theta=10000.0, tied=False, weight_dtype="q8_0", seed=25,
+             weight_std=0.04, gain_std=0.1)
 Q8_MID = dict(n_vocab=8200, n_embd=1056, n_layer=2, n_head=8, n_head_kv=2, head_dim=64, n_ff=2080,
               rms_eps=1e-5, rope_theta=10000.0, tied=False, weight_dtype="q8_0", seed=23,
               weight_std=0.03, gain_std=0.1)
@@ -65,6 +69,23 @@ def test_q8_llama1b_width_two_layers():
     cfg, w = make_weights(cfg, layers=2)
     prompt = tdf_synth.prompt(cfg, 0, 300)
     teacher_forced(cfg, w, 512, prompt, 4, TOL_BF16, "f16", n_ubatch=128, label="q8-1b-2L")
+
+
+def test_q8_nine_to_32_token_ubatches():
+    """Ubatches of 9..32 tokens (the K-sliced matrix-core path: int8 chunks
+    widened into LDS, block scales per row): 48 tokens of 16 interleaved
+    sequences in ubatches of 24, then two lock-step steps of one token per
+    sequence (16 tokens), every row's logits."""
+    cfg, w = make_weights(Q8_SK)
+    rng = np.random.default_rng(7)
+    S = 16
+    seqs = [int(x) for x in rng.integers(0, S, size=48)]
+    calls = [dict(tokens=tdf_synth.prompt(cfg, 0, 48), seq_ids=[[q] for q in seqs], logits=np.ones(48, dtype=np.int8))]
+    for step in range(2):
+        calls.append(dict(tokens=tdf_synth.prompt(cfg, 20 + step, S), seq_ids=[[q] for q in range(S)],
+                          logits=np.ones(S, dtype=np.int8)))
+    log("q8 9..32-token ubatches")
+    run_pair(cfg, w, dict(n_ctx=128, n_ubatch=24, n_seq_max=S), calls, TOL_BF16, "bf16", "q8-skinny")
 
 
 @pytest.mark.parametrize("kv_dtype", ["f32", "bf16"])

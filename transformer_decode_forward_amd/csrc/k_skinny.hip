@@ -11,9 +11,15 @@
 // layout (lane = row, 16 contiguous bytes of it).  Every lane requests the
 // next chunk before the current chunk's MFMAs.  Partial sums of each K slice go to a float32
 // workspace [slice][32][N].
+// Q8_0 weights: a row's 128-wide chunk is 128 int8 (8 lanes of 16 bytes),
+// widened exactly to bf16 on its way into the LDS tile; each 32-deep block's
+// products collect in a temporary tile that is added to the accumulator
+// times the row's block scale (the lane's row: one scale per lane and block).
 // Pass 2 (skinny_epilogue_kernel): sums the slices and applies the epilogue
 // of the layer (store, residual add, SwiGLU as a hi/lo pair, or RoPE with
 // the K/V cache write), as the other linear kernels do.
+#include <type_traits>
+
 #include "k_common.hpp"
 #include "kernels.hpp"
 #include "tdf.h"
@@ -31,14 +37,61 @@ struct SkinnyArgs {
   float* part = nullptr;  // [ksplit][32][N]
 };
 
-__device__ __forceinline__ const uint16_t* sk_row(const LinearArgs& a, bool swiglu, int r) {
-  if (swiglu) return (const uint16_t*)(r < a.n0 ? a.w0 : a.w1) + (int64_t)(r < a.n0 ? r : r - a.n0) * a.K;
-  if (r < a.n0) return (const uint16_t*)a.w0 + (int64_t)r * a.K;
-  if (r < a.n0 + a.n1) return (const uint16_t*)a.w1 + (int64_t)(r - a.n0) * a.K;
-  return (const uint16_t*)a.w2 + (int64_t)(r - a.n0 - a.n1) * a.K;
+// stacked row r: its matrix, row index in it and the matrix's row count
+__device__ __forceinline__ void sk_locate(const LinearArgs& a, bool swiglu, int r, const void*& w, int64_t& row,
+                                          int& rows) {
+  if (swiglu) {
+    w = r < a.n0 ? a.w0 : a.w1; row = r < a.n0 ? r : r - a.n0; rows = a.n0;
+  } else if (r < a.n0) {
+    w = a.w0; row = r; rows = a.n0;
+  } else if (r < a.n0 + a.n1) {
+    w = a.w1; row = r - a.n0; rows = a.n1;
+  } else {
+    w = a.w2; row = r - a.n0 - a.n1; rows = a.n2;
+  }
 }
 
-template <bool SWIGLU>
+__device__ __forceinline__ const uint16_t* sk_row(const LinearArgs& a, bool swiglu, int r) {
+  const void* w;
+  int64_t row;
+  int rows;
+  sk_locate(a, swiglu, r, w, row, rows);
+  return (const uint16_t*)w + row * a.K;
+}
+
+// Q8_0: the int8 values of row r, and its fp16 block scales
+__device__ __forceinline__ const int8_t* sk_row_q8(const LinearArgs& a, bool swiglu, int r) {
+  const void* w;
+  int64_t row;
+  int rows;
+  sk_locate(a, swiglu, r, w, row, rows);
+  return (const int8_t*)w + row * a.K;
+}
+__device__ __forceinline__ const uint16_t* sk_scales_q8(const LinearArgs& a, bool swiglu, int r) {
+  const void* w;
+  int64_t row;
+  int rows;
+  sk_locate(a, swiglu, r, w, row, rows);
+  return (const uint16_t*)((const int8_t*)w + (int64_t)rows * a.K) + row * (a.K / 32);
+}
+
+// 16 int8 -> 16 bf16 (exact) as two 8-element vectors
+__device__ __forceinline__ void widen_i8x16(uint4 q, bf16x8& lo8, bf16x8& hi8) {
+  const uint32_t p[4] = {q.x, q.y, q.z, q.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t v = p[j >> 1];
+    const int b = (j & 1) * 2;
+    const uint32_t f0 = __builtin_bit_cast(uint32_t, (float)((int32_t)(v << (24 - 8 * b)) >> 24));
+    const uint32_t f1 = __builtin_bit_cast(uint32_t, (float)((int32_t)(v << (16 - 8 * b)) >> 24));
+    o[j] = (f0 >> 16) | (f1 & 0xFFFF0000u);
+  }
+  lo8 = __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+  hi8 = __builtin_bit_cast(bf16x8, make_uint4(o[4], o[5], o[6], o[7]));
+}
+
+template <bool SWIGLU, bool Q8>
 __global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs s) {
   const LinearArgs& a = s.a;
   __shared__ __attribute__((aligned(16))) uint16_t Ah[32 * kSkPitch];
@@ -54,10 +107,19 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs s) {
   // whole 256-byte row segments) and pass through the wave's LDS tile into
   // the MFMA operand layout (lane = row, 16 contiguous bytes of it).  Rows
   // past N are clamped: computed and dropped.
-  const uint16_t* wr[kSkU];
+  // Q8_0: QU loads of 16 int8, rows 8u + lane/8, piece lane%8 of the chunk;
+  // the lane's own row (lane%32) fetches that row's 4 block scales per chunk
+  constexpr int QU = kSkChunk * 32 / (64 * 16);  // 4
+  constexpr int NW = Q8 ? QU : kSkU;
+  const void* wr[NW];
 #pragma unroll
-  for (int u = 0; u < kSkU; ++u)
-    wr[u] = sk_row(a, SWIGLU, min(rt * 128 + w * 32 + 4 * u + (lane >> 4), s.N - 1)) + (lane & 15) * 8;
+  for (int u = 0; u < NW; ++u) {
+    if (Q8)
+      wr[u] = sk_row_q8(a, SWIGLU, min(rt * 128 + w * 32 + 8 * u + (lane >> 3), s.N - 1)) + (lane & 7) * 16;
+    else
+      wr[u] = sk_row(a, SWIGLU, min(rt * 128 + w * 32 + 4 * u + (lane >> 4), s.N - 1)) + (lane & 15) * 8;
+  }
+  const uint16_t* wsc = Q8 ? sk_scales_q8(a, SWIGLU, min(rt * 128 + w * 32 + (lane & 31), s.N - 1)) : nullptr;
   uint16_t* wsw = Ws[w];
   f32x16 acc;
 #pragma unroll
@@ -65,7 +127,10 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs s) {
   // activation pieces: 32 tokens x 16 pieces of 8 = 512 per array, 2 per
   // thread: token min(e/16, T-1), k offset (e%16)*8, e = tid + 256 i
   constexpr int AP = 32 * (kSkChunk / 8) / 256;
-  bf16x8 bw[kSkU], ah[AP], al[AP];
+  typedef typename std::conditional<Q8, uint4, bf16x8>::type WRaw;
+  WRaw bw[NW];
+  bf16x8 ah[AP], al[AP];
+  uint2 sc4 = make_uint2(0u, 0u);  // Q8_0: the 4 block scales of the lane's row for the chunk
   const uint16_t* ahp[AP];
   const uint16_t* alp[AP];
 #pragma unroll
@@ -79,7 +144,17 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs s) {
 // the gate/up and down projections at 9..32 tokens)
 #define SK_LOAD(kc_)                                                              \
   do {                                                                            \
-    _Pragma("unroll") for (int u = 0; u < kSkU; ++u) bw[u] = __builtin_nontemporal_load((const bf16x8*)(wr[u] + (kc_))); \
+    if constexpr (Q8) {                                                           \
+      typedef unsigned int u32x4_ __attribute__((ext_vector_type(4)));           \
+      _Pragma("unroll") for (int u = 0; u < NW; ++u) {                            \
+        const u32x4_ v_ = __builtin_nontemporal_load((const u32x4_*)((const int8_t*)wr[u] + (kc_))); \
+        bw[u] = make_uint4(v_[0], v_[1], v_[2], v_[3]);                           \
+      }                                                                           \
+      sc4 = *(const uint2*)(wsc + (kc_) / 32);                                    \
+    } else {                                                                      \
+      _Pragma("unroll") for (int u = 0; u < NW; ++u)                              \
+        bw[u] = __builtin_nontemporal_load((const bf16x8*)((const uint16_t*)wr[u] + (kc_))); \
+    }                                                                             \
     _Pragma("unroll") for (int i = 0; i < AP; ++i) {                              \
       ah[i] = *(const bf16x8*)(ahp[i] + (kc_));                                   \
       al[i] = *(const bf16x8*)(alp[i] + (kc_));                                   \
@@ -95,18 +170,54 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs s) {
       *(bf16x8*)&Ah[off] = ah[i];
       *(bf16x8*)&Al[off] = al[i];
     }
+    uint32_t scw[2] = {0u, 0u};  // Q8_0: this chunk's scales, kept across the next chunk's loads
+    if constexpr (Q8) {
 #pragma unroll
-    for (int u = 0; u < kSkU; ++u) *(bf16x8*)&wsw[(4 * u + (lane >> 4)) * kSkPitch + (lane & 15) * 8] = bw[u];
+      for (int u = 0; u < NW; ++u) {
+        bf16x8 lo8, hi8;
+        widen_i8x16(bw[u], lo8, hi8);
+        uint16_t* dst = &wsw[(8 * u + (lane >> 3)) * kSkPitch + (lane & 7) * 16];
+        *(bf16x8*)dst = lo8;
+        *(bf16x8*)(dst + 8) = hi8;
+      }
+      scw[0] = sc4.x;
+      scw[1] = sc4.y;
+    } else {
+#pragma unroll
+      for (int u = 0; u < NW; ++u) *(bf16x8*)&wsw[(4 * u + (lane >> 4)) * kSkPitch + (lane & 15) * 8] = bw[u];
+    }
     __syncthreads();
     if (kc + kSkChunk < k1) SK_LOAD(kc + kSkChunk);
+    if constexpr (Q8) {
 #pragma unroll
-    for (int u = 0; u < kSkU; ++u) {
-      const int off = (lane & 31) * kSkPitch + u * 16 + (lane >> 5) * 8;
-      const bf16x8 xh = *(const bf16x8*)&Ah[off];
-      const bf16x8 xl = *(const bf16x8*)&Al[off];
-      const bf16x8 b = *(const bf16x8*)&wsw[off];
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, b, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl, b, acc, 0, 0, 0);
+      for (int blk = 0; blk < kSkChunk / 32; ++blk) {
+        f32x16 tmp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmp[r] = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int off = (lane & 31) * kSkPitch + (2 * blk + h) * 16 + (lane >> 5) * 8;
+          const bf16x8 xh = *(const bf16x8*)&Ah[off];
+          const bf16x8 xl = *(const bf16x8*)&Al[off];
+          const bf16x8 b = *(const bf16x8*)&wsw[off];
+          tmp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, b, tmp, 0, 0, 0);
+          tmp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl, b, tmp, 0, 0, 0);
+        }
+        const uint32_t pair = scw[blk >> 1];
+        const float sc = f16_to_f32((uint16_t)((blk & 1) ? pair >> 16 : pair & 0xFFFFu));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = fmaf(sc, tmp[r], acc[r]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kSkU; ++u) {
+        const int off = (lane & 31) * kSkPitch + u * 16 + (lane >> 5) * 8;
+        const bf16x8 xh = *(const bf16x8*)&Ah[off];
+        const bf16x8 xl = *(const bf16x8*)&Al[off];
+        const bf16x8 b = *(const bf16x8*)&wsw[off];
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl, b, acc, 0, 0, 0);
+      }
     }
   }
 #undef SK_LOAD
@@ -188,7 +299,8 @@ __global__ void __launch_bounds__(256) skinny_epilogue_kernel(SkinnyArgs s) {
 
 bool skinny_supported(const LinearArgs& a) {
   const int N = a.epi == EPI_SWIGLU ? 2 * a.n0 : a.n0 + a.n1 + a.n2;
-  return a.weight_dtype == TDF_BF16 && a.act_hi && a.act_lo && a.T > 0 && a.T <= 32 && a.K % kSkChunk == 0 &&
+  return (a.weight_dtype == TDF_BF16 || a.weight_dtype == TDF_Q8_0) && a.act_hi && a.act_lo && a.T > 0 &&
+         a.T <= 32 && a.K % kSkChunk == 0 &&
          (int64_t)N * 32 <= kSkinnyPartFloats && (a.epi != EPI_QKV || (a.n0 % 2 == 0 && a.n1 % 2 == 0));
 }
 
@@ -206,10 +318,14 @@ hipError_t launch_linear_skinny(const LinearArgs& a, float* part, hipStream_t st
   while (nrt * ks < 512 && ks * 2 <= chunks && (int64_t)s.N * 32 * ks * 2 <= kSkinnyPartFloats) ks *= 2;
   s.kslice = ((chunks + ks - 1) / ks) * kSkChunk;
   s.ksplit = (a.K + s.kslice - 1) / s.kslice;
-  if (a.epi == EPI_SWIGLU)
-    skinny_kernel<true><<<nrt * s.ksplit, 256, 0, st>>>(s);
-  else
-    skinny_kernel<false><<<nrt * s.ksplit, 256, 0, st>>>(s);
+  const bool q8 = a.weight_dtype == TDF_Q8_0;
+  if (a.epi == EPI_SWIGLU) {
+    if (q8) skinny_kernel<true, true><<<nrt * s.ksplit, 256, 0, st>>>(s);
+    else skinny_kernel<true, false><<<nrt * s.ksplit, 256, 0, st>>>(s);
+  } else {
+    if (q8) skinny_kernel<false, true><<<nrt * s.ksplit, 256, 0, st>>>(s);
+    else skinny_kernel<false, false><<<nrt * s.ksplit, 256, 0, st>>>(s);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n_thr = a.epi == EPI_SWIGLU ? (int64_t)a.T * a.n0 : (int64_t)a.T * ((s.N + 1) / 2);
