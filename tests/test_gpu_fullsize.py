@@ -72,12 +72,14 @@ def test_llama1b_full_workload_shape():
     log(f"1b full: worst max-abs {max(e[0] for e in errs):.2e}, rel-L2 {max(e[1] for e in errs):.2e}")
 
 
-def test_llama8b_full_depth():
-    """8B-class model, all 32 layers: context 2048 restored, then a 64-token
-    ubatch (matrix-core path; logits for 3 rows) and 2 decode steps."""
-    cfg = tdf_synth.CONFIGS["llama8b"]
+@pytest.mark.parametrize("weight_dtype", ["bf16", "q8_0"])
+def test_llama8b_full_depth(weight_dtype):
+    """8B-class model, all 32 layers (bf16 or Q8_0 weights): context 2048
+    restored, then a 64-token ubatch (matrix-core path; logits for 3 rows) and
+    2 decode steps."""
+    cfg = dict(tdf_synth.CONFIGS["llama8b"], weight_dtype=weight_dtype)
     cfg, w = make_weights(cfg)
-    log("8b weights generated")
+    log(f"8b {weight_dtype} weights generated")
     gm, gc, oc = _restored_pair(cfg, w, 2048, 4096, cache=False)
     toks = tdf_synth.prompt(cfg, 3, 64)
     flags = np.zeros(64, dtype=np.int8)
@@ -99,7 +101,8 @@ def test_llama8b_full_depth():
         check_token(gc.argmax_ith(0), ro.logits[0], f"8b step {step}")
         nxt = int(ro.tokens[0])
         log(f"8b step {step} done")
-    log(f"8b full depth: worst max-abs {max(e[0] for e in errs):.2e}, rel-L2 {max(e[1] for e in errs):.2e}")
+    log(f"8b {weight_dtype} full depth: worst max-abs {max(e[0] for e in errs):.2e}, "
+        f"rel-L2 {max(e[1] for e in errs):.2e}")
 
 
 def test_multisequence_bookkeeping_full():
