@@ -88,6 +88,22 @@ def test_q8_nine_to_32_token_ubatches():
     run_pair(cfg, w, dict(n_ctx=128, n_ubatch=24, n_seq_max=S), calls, TOL_BF16, "bf16", "q8-skinny")
 
 
+def test_q8_four_row_waves_ragged():
+    """Single-token GEMVs with four rows per wave: a vocabulary of 16390 rows
+    (the LM head's last wave holds two rows) and a stacked Q/K/V of 20480 rows
+    (128 query heads of 128, 16 KV heads), then decode steps; f32 cache, so
+    the float32 tolerance applies to the steps after a vector-unit prompt."""
+    cfg = dict(n_vocab=16390, n_embd=256, n_layer=1, n_head=128, n_head_kv=16, head_dim=128, n_ff=512,
+               rms_eps=1e-5, rope_theta=10000.0, tied=False, weight_dtype="q8_0", seed=27,
+               weight_std=0.05, gain_std=0.1)
+    cfg, w = make_weights(cfg)
+    prompt = tdf_synth.prompt(cfg, 0, 8)
+    calls = [dict(tokens=prompt[:4]), dict(tokens=prompt[4:])] + \
+        [dict(tokens=[int(t)]) for t in tdf_synth.prompt(cfg, 1, 4)]
+    log("q8 four-row waves")
+    run_pair(cfg, w, dict(n_ctx=32, n_ubatch=8), calls, TOL_F32, "f32", "q8-r4")
+
+
 @pytest.mark.parametrize("kv_dtype", ["f32", "bf16"])
 def test_q8_ragged_chunks_teacher_forced(kv_dtype):
     """40-token prompt in ubatches of 16, 16, 8, then 6 teacher-forced steps."""
