@@ -481,9 +481,12 @@ def main():
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(cfg, host, P)
 
+    # the counter records cover the 8B shape's kernels
+    is8b = args.config == "llama8b" and not args.swa
+    shape = {"llama8b": "8B", "llama1b": "1B", "tiny": "tiny"}.get(args.config, args.config)
     out = {
-        "metric": ("decode tok/s (% HBM peak) + prefill tok/s (% MFMA peak), 8B-shape bf16" if not q8 else
-                   "decode tok/s (% HBM peak) + prefill tok/s, 8B-shape Q8_0 weights"),
+        "metric": (f"decode tok/s (% HBM peak) + prefill tok/s (% MFMA peak), {shape}-shape bf16" if not q8 else
+                   f"decode tok/s (% HBM peak) + prefill tok/s, {shape}-shape Q8_0 weights"),
         "value": round(decode_tps, 3),
         "unit": "tok/s",
         "n_gpus": 1,
@@ -496,7 +499,7 @@ def main():
         "dtype": "f32 (q8_0 weights)" if q8 else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{args.config}: batch 1, {P}-token prompt in ubatches of {U} "
-                               f"(last-position logits), then greedy decode steps; KV bf16 {n_ctx} cells"
+                               f"(last-position logits), then greedy decode steps; KV {cfg['kv_dtype']} {n_ctx} cells"
                                + ("; Q8_0 weights" if q8 else ""),
                    "d_model": d, "n_layer": cfg["n_layer"], "n_ff": F, "n_vocab": cfg["n_vocab"],
                    "attention_window": args.swa or None},
@@ -511,11 +514,11 @@ def main():
                     "frac_mfma_peak": round(pre_flops / t_pre / 1e12 / MFMA_BF16_PEAK_TFS, 4)},
         "roofline": {"bound": "hbm", "kernel": "gate/up GEMV + SwiGLU (decode)",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic("decode_q8_0" if q8 else "decode"),
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic("decode_q8_0" if q8 else "decode") if is8b else None,
                      "avg_launch_us": round(gu_us, 2), "bytes_per_launch": gu_bytes},
         "roofline_prefill": {"bound": "mfma", "kernel": "gate/up GEMM + SwiGLU (prefill ubatch 512)",
                              "achieved": round(gg_tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                             "frac": round(gg_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic("prefill_q8_0" if q8 else "prefill"),
+                             "frac": round(gg_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic("prefill_q8_0" if q8 else "prefill") if is8b else None,
                              "avg_launch_us": round(gg_us, 2), "flops_per_launch": gg_flops,
                              "executed_flops_per_launch": 2 * gg_flops},
         "measured_peaks": peaks,
