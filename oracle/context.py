@@ -53,7 +53,14 @@ Readings where the pages are silent or inconsistent:
   DType; the llama.cpp walkthrough's KV-cache section names the cache type
   as a storage setting): with ``kv_dtype`` set, each stored value is the
   float64 result rounded to nearest-even in that type (f32, f16 or bf16);
-  without it the cache keeps float64.
+  without it the cache keeps float64.  ``q8_0`` (a quantized cache: the
+  backend chapter and the walkthrough's KV-cache section name quantized
+  cache types without defining them) stores each row of head_dim values as
+  blocks of 32: the value is first rounded to float32 (the precision in
+  which a float32 forward pass takes the decision), then
+  d = fp16(max|x| / 127), q = round-half-even(x / d) clamped to [-127, 127]
+  (q = 0 when d = 0), all in float32; the stored value is d * q.  Imported
+  rows for such a cache are float32 values, quantized the same way.
 * Logits: one row per flagged token, in batch order, accumulated over the
   ubatches of the call.  Greedy ties go to the lowest index.
 """
@@ -103,7 +110,25 @@ def _round_storage(a: np.ndarray, dtype: Optional[str]) -> np.ndarray:
         u = f.view(np.uint32)
         u = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
         return u.view(np.float32).astype(np.float64)
+    if dtype == "q8_0":
+        return quantize_q8_0_rows(a)
     raise ValueError(dtype)
+
+
+def quantize_q8_0_rows(a: np.ndarray) -> np.ndarray:
+    """Stored value of a Q8_0 cache row (last axis, a multiple of 32): per
+    block of 32, d = fp16(max|x| / 127) and q = round-half-even(x / d)
+    clamped to [-127, 127], with x rounded to float32 first and every step in
+    float32; returns d * q (exact) in float64."""
+    shape = a.shape
+    f = np.asarray(a, dtype=np.float64).astype(np.float32).reshape(*shape[:-1], shape[-1] // 32, 32)
+    amax = np.max(np.abs(f), axis=-1)
+    d = (amax / np.float32(127)).astype(np.float16)
+    d32 = d.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(d32 > 0, np.rint(f / np.where(d32 > 0, d32, np.float32(1))), np.float32(0))
+    q = np.clip(q, -127, 127)
+    return (q.astype(np.float64) * d.astype(np.float64)[..., None]).reshape(shape)
 
 
 class OracleContext:
@@ -304,8 +329,8 @@ class OracleContext:
             for l in range(self.hp["n_layer"]):
                 kl = k_layers(l) if callable(k_layers) else k_layers[l]
                 vl = v_layers(l) if callable(v_layers) else v_layers[l]
-                self._layer_cache(l)[0][cells] = widen(kl)
-                self._layer_cache(l)[1][cells] = widen(vl)
+                self._layer_cache(l)[0][cells] = _round_storage(widen(kl), self.kv_dtype)
+                self._layer_cache(l)[1][cells] = _round_storage(widen(vl), self.kv_dtype)
         self.last_import_cells = cells
         return OK
 
