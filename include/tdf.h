@@ -34,12 +34,15 @@
 extern "C" {
 #endif
 
-/* TDF_Q8_0 is a weight format only (llama.cpp walkthrough and the Ollama
- * backends chapter name the "Q8_0" type without defining it; the common
- * reading is taken): every block of 32 consecutive elements of a row is one
- * fp16 scale d times 32 int8 values q, w = d * q.  A Q8_0 matrix [rows][K]
- * (K a multiple of 32) is one buffer: rows*K int8 values q, row-major, then
- * rows*K/32 fp16 scales, row-major [rows][K/32], starting at byte rows*K. */
+/* TDF_Q8_0 (llama.cpp walkthrough and the Ollama backends chapter name the
+ * "Q8_0" type without defining it; the common reading is taken): every block
+ * of 32 consecutive elements of a row is one fp16 scale d times 32 int8
+ * values q, w = d * q.  A Q8_0 matrix [rows][K] (K a multiple of 32) is one
+ * buffer: rows*K int8 values q, row-major, then rows*K/32 fp16 scales,
+ * row-major [rows][K/32], starting at byte rows*K.  As a cache type each
+ * cached K or V row of head_dim values is quantized the same way when it is
+ * stored: d = fp16(max|x| / 127), q = round-half-even(x / d) clamped to
+ * [-127, 127] (0 when d is 0), decided in float32. */
 typedef enum { TDF_F32 = 0, TDF_F16 = 1, TDF_BF16 = 2, TDF_Q8_0 = 3 } tdf_dtype;
 
 /* Return codes of tdf_decode / tdf_kv_import (llama.cpp walkthrough,
@@ -115,7 +118,8 @@ typedef struct {
 
 /* n_ctx = KV cells; n_batch = largest batch per decode (clamped to n_ctx);
  * n_ubatch = tokens per forward chunk (clamped to n_batch); n_seq_max <= 64;
- * kv_dtype = TDF_F32, TDF_F16 or TDF_BF16; output_all = default output flag
+ * kv_dtype = TDF_F32, TDF_F16, TDF_BF16 or TDF_Q8_0 (head_dim a multiple of
+ * 32; attention then runs on the vector units); output_all = default output flag
  * of every token instead of the last; stream = hipStream_t to run on (NULL:
  * the context creates its own). */
 typedef struct {
@@ -198,7 +202,8 @@ int32_t tdf_last_slots(const tdf_context *c, int32_t *slots);
 /* Place positions [pos0, pos0+n) of sequence s in cells (one chunk, the
  * ubatch placement rule) and fill them with given post-RoPE keys and values:
  * k_layers[l] / v_layers[l] are DEVICE pointers to [n][n_head_kv][head_dim]
- * arrays in the context's kv dtype (HOST array of n_layer pointers).  Used
+ * arrays in the context's kv dtype, float32 for a TDF_Q8_0 cache (quantized
+ * on import) (HOST array of n_layer pointers).  Used
  * to restore a cache state.  Returns TDF_OK, TDF_NO_SLOT, TDF_E_INVALID (pos0
  * must exceed seq_pos_max(s)) or TDF_E_DEVICE. */
 int32_t tdf_kv_import(tdf_context *c, int32_t s, int32_t pos0, int32_t n,

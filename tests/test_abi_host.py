@@ -151,6 +151,14 @@ def test_q8_0_weights_accepted_and_sizes_checked():
             tdf.Model(dict(HP, weight_dtype="q8_0", **bad), dry_run=True)
 
 
+def test_q8_0_cache_needs_head_dim_multiple_of_32():
+    m16 = tdf.Model(HP, dry_run=True)  # head_dim 16
+    with pytest.raises(RuntimeError):
+        tdf.Context(m16, n_ctx=16, kv_dtype="q8_0", dry_run=True)
+    m32 = tdf.Model(dict(HP, head_dim=32), dry_run=True)
+    tdf.Context(m32, n_ctx=16, kv_dtype="q8_0", dry_run=True)
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_random_scripts_with_removal_and_shift_match_oracle(seed):
     """Decode calls interleaved with range removals and shifts (valid and

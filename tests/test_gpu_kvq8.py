@@ -1,0 +1,86 @@
+"""GPU parity of the Q8_0 KV cache (each cached K/V row stored as blocks of
+32: fp16 scale, int8 codes decided in float32) against the float64 oracle,
+whose cache stores the same rule's values.
+
+Both sides quantize their own float32 K/V rows.  The GPU's rows come from
+float32 (vector units) or hi/lo bf16 (matrix cores) projections and differ
+from the oracle's in the last bits, so a code can differ by one where x / d
+falls next to a rounding boundary; the bf16 tolerance (max-abs 3e-2, rel-L2
+1e-2) covers that.  Imported rows are the same float32 values on both sides,
+so their codes agree exactly.  Cells, positions and output rows: bit-exact.
+"""
+import numpy as np
+import pytest
+
+import tdf_synth
+from oracle import OracleContext
+
+from gpu_common import TOL_BF16, check_logits, check_token, device_model, log, make_weights, oracle_model
+from test_gpu_parity import SMALL, run_pair
+from test_gpu_swa import SMALL64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("cfg0", [SMALL, SMALL64], ids=["hd32", "hd64"])
+def test_prefill_and_steps(cfg0):
+    """150 tokens in ubatches of 64, 64, 22 (attention over the quantized
+    rows on the vector units), logits for every row, then three steps."""
+    cfg, w = make_weights(cfg0)
+    prompt = tdf_synth.prompt(cfg, 0, 150)
+    calls = [dict(tokens=prompt)] + [dict(tokens=[int(t)]) for t in tdf_synth.prompt(cfg, 1, 3)]
+    log(f"q8 cache hd={cfg['head_dim']}")
+    run_pair(cfg, w, dict(n_ctx=256, n_ubatch=64, output_all=True), calls, TOL_BF16, "q8_0", "kvq8")
+
+
+def test_multi_sequence_steps():
+    cfg, w = make_weights(SMALL64)
+    rng = np.random.default_rng(4)
+    seqs = [int(s) for s in rng.integers(0, 3, size=90)]
+    calls = [dict(tokens=tdf_synth.prompt(cfg, 0, 90), seq_ids=[[s] for s in seqs],
+                  logits=np.ones(90, dtype=np.int8))]
+    for step in range(3):
+        calls.append(dict(tokens=tdf_synth.prompt(cfg, 10 + step, 3), seq_ids=[[0], [1], [2]],
+                          logits=np.ones(3, dtype=np.int8)))
+    run_pair(cfg, w, dict(n_ctx=200, n_ubatch=40, n_seq_max=4), calls, TOL_BF16, "q8_0", "kvq8-multiseq")
+
+
+def test_import_then_decode():
+    """300 positions of float32 N(0,1) rows imported (quantized on both sides
+    by the same rule from the same values), then decode steps."""
+    import transformer_decode_forward_amd as tdf
+    from transformer_decode_forward_amd.device import to_device
+    cfg, w = make_weights(SMALL64)
+    L, P = cfg["n_layer"], 300
+    ks = [tdf_synth.kv_fill(cfg, l, "k", 0, P, "f32") for l in range(L)]
+    vs = [tdf_synth.kv_fill(cfg, l, "v", 0, P, "f32") for l in range(L)]
+    gc = tdf.Context(device_model(cfg, w), n_ctx=512, kv_dtype="q8_0")
+    kd = [to_device(k) for k in ks]
+    vd = [to_device(v) for v in vs]
+    assert gc.kv_import(0, 0, P, [t.data_ptr() for t in kd], [t.data_ptr() for t in vd]) == 0
+    oc = OracleContext(oracle_model(cfg, w), n_ctx=512, kv_dtype="q8_0")
+    assert oc.kv_import(0, 0, P, ks, vs) == 0
+    for t in tdf_synth.prompt(cfg, 2, 3):
+        assert gc.decode([int(t)]) == 0
+        ro = oc.decode([int(t)])
+        assert gc.last_slots() == ro.slots
+        check_logits(gc.logits_ith(0), ro.logits[0], TOL_BF16, "kvq8 import")
+        check_token(gc.argmax_ith(0), ro.logits[0], "kvq8 import")
+
+
+def test_drop_and_shift_then_decode():
+    """Drop positions [0, 30) of a 100-token prompt, shift the rest down by 30
+    (the stored keys rotated and re-quantized), then 5 steps."""
+    import transformer_decode_forward_amd as tdf
+    cfg, w = make_weights(SMALL64)
+    gc = tdf.Context(device_model(cfg, w), n_ctx=256, n_ubatch=64, kv_dtype="q8_0")
+    oc = OracleContext(oracle_model(cfg, w), n_ctx=256, n_ubatch=64, kv_dtype="q8_0")
+    prompt = tdf_synth.prompt(cfg, 0, 100)
+    assert gc.decode(prompt) == 0 and oc.decode(prompt).status == 0
+    assert gc.kv_seq_rm(0, 0, 30) == oc.kv_seq_rm(0, 0, 30) == 0
+    assert gc.kv_seq_shift(0, 30, -1, -30) == oc.kv_seq_shift(0, 30, -1, -30) == 0
+    for k, t in enumerate(tdf_synth.prompt(cfg, 1, 5)):
+        assert gc.decode([int(t)]) == 0
+        ro = oc.decode([int(t)])
+        assert gc.last_slots() == ro.slots
+        check_logits(gc.logits_ith(0), ro.logits[0], TOL_BF16, f"kvq8 shift step {k}")

@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libtdf.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-DEVICE_SOURCES = ["k_decode.hip", "k_attn_decode.hip", "k_gemm.hip", "k_attn_prefill.hip", "k_sample.hip", "k_skinny.hip", "tdf_api.hip"]
+DEVICE_SOURCES = ["k_decode.hip", "k_attn_decode.hip", "k_gemm.hip", "k_attn_prefill.hip", "k_sample.hip", "k_skinny.hip", "k_kvq8.hip", "tdf_api.hip"]
 HOST_SOURCES = ["host_plan.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops

@@ -44,6 +44,14 @@ template <> __device__ __forceinline__ void unpack16<kv_bf16>(uint4 u, float* ou
     out[2 * j + 1] = __builtin_bit_cast(float, p[j] & 0xFFFF0000u);
   }
 }
+// Q8_0: 16 int8 codes (the block scale is applied by the caller)
+template <> __device__ __forceinline__ void unpack16<kv_q8>(uint4 u, float* out) {
+  const uint32_t p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) out[4 * j + b] = (float)((int32_t)(p[j] << (24 - 8 * b)) >> 24);
+}
 template <> __device__ __forceinline__ void unpack16<kv_f16>(uint4 u, float* out) {
   const uint32_t p[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -69,7 +77,11 @@ __device__ __forceinline__ float group_sum(float v) {
 template <typename KvT, int HD, int G>
 __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
   typedef typename KvStore<KvT>::T ST;
-  constexpr int E = sizeof(ST) == 2 ? 8 : 4;          // elements per 16-byte piece
+  // Q8_0 rows: 16 codes per 16-byte piece, inside one 32-element block whose
+  // fp16 scale (from the scale array after the codes) multiplies the piece's
+  // score part and its probability for V
+  constexpr bool Q8 = std::is_same<KvT, kv_q8>::value;
+  constexpr int E = Q8 ? 16 : sizeof(ST) == 2 ? 8 : 4;  // elements per 16-byte piece
   constexpr int PR = HD / E;                           // pieces per row: 2..32
   constexpr int ROWS = 256 / PR;                       // rows per pass of the block
   constexpr int TILE = ROWS > kTile ? ROWS : kTile;    // rows per tile
@@ -88,6 +100,13 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
   const ST* vc = (const ST*)a.v_cache + (int64_t)g * a.n_ctx * HD;
   const int r0 = tid / PR;        // row of this lane in each pass
   const int dq = (tid % PR) * E;  // first element of this lane's piece
+  constexpr int NB = HD / 32;     // Q8_0 blocks per row
+  const uint16_t* ksc = nullptr;
+  const uint16_t* vsc = nullptr;
+  if (Q8) {
+    ksc = (const uint16_t*)((const int8_t*)a.k_cache + (int64_t)a.Hkv * a.n_ctx * HD) + (int64_t)g * a.n_ctx * NB + dq / 32;
+    vsc = (const uint16_t*)((const int8_t*)a.v_cache + (int64_t)a.Hkv * a.n_ctx * HD) + (int64_t)g * a.n_ctx * NB + dq / 32;
+  }
 
   // Loads come from clamped addresses, unconditionally: a load under a
   // divergent branch makes the compiler wait for every load in flight.  The
@@ -107,6 +126,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
   }
   int row[PPER];
   uint4 kr[PPER], vr[PPER];
+  uint16_t ksr[PPER], vsr[PPER];  // Q8_0 scales of the pieces
   if (!staged) {
 #pragma unroll
     for (int pi = 0; pi < PPER; ++pi) row[pi] = cells[min(c_lo + r0 + pi * ROWS, c_hi - 1)];
@@ -134,6 +154,10 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
     const int64_t off = (int64_t)row[pi] * HD + dq;
     kr[pi] = *(const uint4*)(kc + off);
     vr[pi] = *(const uint4*)(vc + off);
+    if (Q8) {
+      ksr[pi] = ksc[(int64_t)row[pi] * NB];
+      vsr[pi] = vsc[(int64_t)row[pi] * NB];
+    }
   }
 
   float m_w[G], l_w[G], acc[G][E];
@@ -148,10 +172,13 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
   for (int c0 = c_lo; c0 < c_hi; c0 += TILE) {
     const int nc = min(TILE, c_hi - c0);
     uint4 kt[PPER], vt[PPER];
+    float kst[PPER], vst[PPER];
 #pragma unroll
     for (int pi = 0; pi < PPER; ++pi) {
       kt[pi] = kr[pi];
       vt[pi] = vr[pi];
+      kst[pi] = Q8 ? f16_to_f32(ksr[pi]) : 1.f;
+      vst[pi] = Q8 ? f16_to_f32(vsr[pi]) : 1.f;
     }
     if (c0 + TILE < c_hi) {  // block-uniform: request the next tile
 #pragma unroll
@@ -164,6 +191,10 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
         const int64_t off = (int64_t)row[pi] * HD + dq;
         kr[pi] = *(const uint4*)(kc + off);
         vr[pi] = *(const uint4*)(vc + off);
+        if (Q8) {
+          ksr[pi] = ksc[(int64_t)row[pi] * NB];
+          vsr[pi] = vsc[(int64_t)row[pi] * NB];
+        }
       }
     }
     // scores of this lane's rows, summed over the PR lanes of each row
@@ -181,7 +212,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
           x0 = fmaf(qr[h][e], kf[e], x0);
           x1 = fmaf(qr[h][e + 1], kf[e + 1], x1);
         }
-        const float x = group_sum<PR>(x0 + x1);
+        const float x = group_sum<PR>(Q8 ? (x0 + x1) * kst[pi] : x0 + x1);
         sc[pi][h] = live ? x : -INFINITY;
       }
     }
@@ -214,9 +245,11 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
       float vf[E];
       unpack16<KvT>(vt[pi], vf);
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+      for (int h = 0; h < G; ++h) {
+        const float pv = Q8 ? sc[pi][h] * vst[pi] : sc[pi][h];
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[h][e] = fmaf(sc[pi][h], vf[e], acc[h][e]);
+        for (int e = 0; e < E; ++e) acc[h][e] = fmaf(pv, vf[e], acc[h][e]);
+      }
     }
   }
 
@@ -679,7 +712,7 @@ static hipError_t attn_launch_hd(const AttnArgs& a, hipStream_t s) {
   // 16-bit caches with head_dim 64 or 128: scores and value products on the
   // matrix cores (chunks of at most kCellStage cells)
   bool done = false;
-  if constexpr (!std::is_same<KvT, float>::value && (HD == 64 || HD == 128)) {
+  if constexpr (!std::is_same<KvT, float>::value && !std::is_same<KvT, kv_q8>::value && (HD == 64 || HD == 128)) {
     if (a.chunk <= kCellStage) {
       switch (G) {
         case 1: attn_decode_mfma_kernel<KvT, HD, 1><<<grid, 256, 0, s>>>(a); break;
@@ -735,7 +768,9 @@ hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s) {
 template <typename KvT>
 static hipError_t attn_launch_kv(const AttnArgs& a, hipStream_t s) {
   switch (a.hd) {
-    case 16: return attn_launch_hd<KvT, 16>(a, s);
+    case 16:
+      if constexpr (std::is_same<KvT, kv_q8>::value) return hipErrorInvalidValue;  // blocks of 32
+      else return attn_launch_hd<KvT, 16>(a, s);
     case 32: return attn_launch_hd<KvT, 32>(a, s);
     case 64: return attn_launch_hd<KvT, 64>(a, s);
     case 128: return attn_launch_hd<KvT, 128>(a, s);
@@ -747,6 +782,10 @@ hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   if (a.kv_dtype == TDF_BF16) return attn_launch_kv<kv_bf16>(a, s);
   if (a.kv_dtype == TDF_F16) return attn_launch_kv<kv_f16>(a, s);
+  if (a.kv_dtype == TDF_Q8_0) {
+    if (a.hd % 32 != 0) return hipErrorInvalidValue;
+    return attn_launch_kv<kv_q8>(a, s);
+  }
   return attn_launch_kv<float>(a, s);
 }
 

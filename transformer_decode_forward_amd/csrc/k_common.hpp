@@ -38,6 +38,7 @@ __device__ __forceinline__ uint16_t f32_to_f16(float f) {
 // Cache element types: KvT = float, or a tag for 16-bit formats.
 struct kv_bf16 {};
 struct kv_f16 {};
+struct kv_q8 {};  // Q8_0 blocks of 32 (int8 codes + fp16 scales, read by the vector attention)
 
 template <typename KvT> struct KvStore;
 template <> struct KvStore<float> {
@@ -49,6 +50,9 @@ template <> struct KvStore<kv_bf16> {
   typedef uint16_t T;
   __device__ __forceinline__ static float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
   __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+template <> struct KvStore<kv_q8> {
+  typedef int8_t T;  // codes; blocks are written whole by kv_quantize
 };
 template <> struct KvStore<kv_f16> {
   typedef uint16_t T;

@@ -101,6 +101,20 @@ hipError_t launch_gather_rows(const float* src, const int32_t* rows, int R, int 
 hipError_t launch_kv_rotate(void* kv, int kv_dtype, size_t layer_stride_bytes, int L, int Hkv, int n_ctx, int hd,
                             const int32_t* cells, int n_cells, const double2* cs, hipStream_t s);
 
+// Q8_0 KV cache (layout per layer array: int8 codes [Hkv][n_ctx][hd], then
+// fp16 scales [Hkv][n_ctx][hd/32]).  kv_quantize stores float32 rows (row
+// (t, h) at src + t * t_stride + h * h_stride) in cells[t]; kv_rotate_q8
+// rotates the stored keys of n_cells cells (every layer) and re-quantizes.
+inline size_t kv_q8_array_bytes(int Hkv, int n_ctx, int hd) {
+  const size_t b = (size_t)Hkv * n_ctx * hd + (size_t)Hkv * n_ctx * (hd / 32) * 2;
+  return (b + 255) / 256 * 256;
+}
+hipError_t launch_kv_quantize(const float* src_k, const float* src_v, int64_t t_stride, int64_t h_stride, int T,
+                              int Hkv, int hd, const int32_t* cells, void* k_dst, void* v_dst, int n_ctx,
+                              hipStream_t s);
+hipError_t launch_kv_rotate_q8(void* kv, size_t layer_stride_bytes, int L, int Hkv, int n_ctx, int hd,
+                               const int32_t* cells, int n_cells, const double2* cs, hipStream_t s);
+
 // Sampling chain of one token per logits row (temperature > 0): Top-K
 // (1 <= top_k <= kMaxTopK), temperature, softmax, Top-P, Min-P, draw with
 // u[r] in [0, 1) (device array); tok[r] receives the token.

@@ -109,6 +109,8 @@ struct tdf_context {
   // bf16 hi/lo pairs of the matrix-core inputs: normed rows, attention output, MLP product
   uint16_t *h_hi = nullptr, *h_lo = nullptr, *o_hi = nullptr, *o_lo = nullptr, *m_hi = nullptr, *m_lo = nullptr;
   float *part_acc = nullptr, *part_ml = nullptr;
+  float* kv_stage = nullptr;        // Q8_0 cache: float32 K/V rows of the ubatch [2][Hkv][n_ubatch][hd]
+  int32_t* iota = nullptr;          // Q8_0 cache: 0 .. n_ubatch-1 (staging rows)
   size_t part_rows = 0;             // capacity in (token, head, chunk) triples
   void* ints = nullptr;             // per-call packed integers
   size_t ints_bytes = 0;
@@ -347,7 +349,14 @@ extern "C" tdf_context* tdf_context_create(const tdf_model* m, const tdf_context
     set_err("invalid context parameters");
     return nullptr;
   }
-  if (p->kv_dtype != TDF_F32 && p->kv_dtype != TDF_F16 && p->kv_dtype != TDF_BF16) { set_err("invalid kv_dtype"); return nullptr; }
+  if (p->kv_dtype != TDF_F32 && p->kv_dtype != TDF_F16 && p->kv_dtype != TDF_BF16 && p->kv_dtype != TDF_Q8_0) {
+    set_err("invalid kv_dtype");
+    return nullptr;
+  }
+  if (p->kv_dtype == TDF_Q8_0 && m->hp.head_dim % 32 != 0) {
+    set_err("a Q8_0 cache needs head_dim to be a multiple of 32");
+    return nullptr;
+  }
   tdf_context* c = new tdf_context();
   c->m = m;
   c->n_ctx = p->n_ctx;
@@ -382,7 +391,8 @@ extern "C" tdf_context* tdf_context_create(const tdf_model* m, const tdf_context
     }
     c->own_stream = true;
   }
-  c->kv_layer_bytes = (size_t)Hkv * c->n_ctx * hd * dtype_size(c->kv_dtype);
+  c->kv_layer_bytes = c->kv_dtype == TDF_Q8_0 ? kv_q8_array_bytes(Hkv, c->n_ctx, hd)
+                                              : (size_t)Hkv * c->n_ctx * hd * dtype_size(c->kv_dtype);
   A(&c->kv, c->kv_layer_bytes * 2 * std::max(1, h.n_layer));
   A((void**)&c->cell_list, (size_t)c->n_seq_max * c->n_ctx * sizeof(int32_t));
   A((void**)&c->inv_freq, (size_t)(hd / 2) * sizeof(double));
@@ -406,6 +416,18 @@ extern "C" tdf_context* tdf_context_create(const tdf_model* m, const tdf_context
   A((void**)&c->part_acc, c->part_rows * hd * 4);
   A((void**)&c->part_ml, c->part_rows * 2 * 4);
   if (U > kGemvMaxT) A((void**)&c->skinny_part, (size_t)kSkinnyPartFloats * 4);
+  if (c->kv_dtype == TDF_Q8_0) {
+    A((void**)&c->kv_stage, (size_t)2 * Hkv * U * hd * 4);
+    A((void**)&c->iota, (size_t)U * 4);
+    if (rc == TDF_OK) {
+      std::vector<int32_t> io(U);
+      for (int i = 0; i < U; ++i) io[i] = i;
+      if (hipMemcpy(c->iota, io.data(), (size_t)U * 4, hipMemcpyHostToDevice) != hipSuccess) {
+        set_err("upload of the staging rows failed");
+        rc = TDF_E_DEVICE;
+      }
+    }
+  }
   // per-call integers: 5 int32 per token + selected rows, then int64 list writes
   c->ints_bytes = staging_i64_base(c->n_batch, c->n_ubatch, c->n_seq_max) +
                   (size_t)2 * c->n_batch * c->n_seq_max * 8;
@@ -534,7 +556,20 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     qa.k_cache = kv_k(c, l); qa.v_cache = kv_v(c, l);
     qa.kv_dtype = c->kv_dtype; qa.n_ctx = c->n_ctx; qa.head_dim = hd;
     qa.slots = u.slots; qa.pos = u.pos; qa.rope_cs = c->rope_cs;
+    const bool kvq8 = c->kv_dtype == TDF_Q8_0;
+    if (kvq8) {
+      // float32 rows into the staging area (row t of head h at [h][t]), then
+      // quantized into their cells
+      qa.k_cache = c->kv_stage; qa.v_cache = c->kv_stage + (size_t)Hkv * c->n_ubatch * hd;
+      qa.kv_dtype = TDF_F32; qa.n_ctx = c->n_ubatch; qa.slots = c->iota;
+    }
     if (int rc = run_linear(c, qa, big, TDF_OP_QKV)) return rc;
+    if (kvq8) {
+      ps = prof_begin(c, TDF_OP_QKV, big);
+      TDF_HIP(launch_kv_quantize(c->kv_stage, c->kv_stage + (size_t)Hkv * c->n_ubatch * hd, hd,
+                                 (int64_t)c->n_ubatch * hd, T, Hkv, hd, u.slots, kv_k(c, l), kv_v(c, l), c->n_ctx, s));
+      prof_end(c, ps);
+    }
     u_parts = 0;
 
     const bool win = m->windowed[l] != 0;
@@ -1036,7 +1071,11 @@ extern "C" int32_t tdf_kv_import(tdf_context* c, int32_t s, int32_t pos0, int32_
   const int64_t total = (int64_t)n * Hkv * hd;
   const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
   for (int l = 0; l < L; ++l) {
-    if (c->kv_dtype == TDF_F32) {
+    if (c->kv_dtype == TDF_Q8_0) {
+      // float32 rows [n][Hkv][hd], quantized into their cells
+      TDF_HIP(launch_kv_quantize((const float*)k_layers[l], (const float*)v_layers[l], (int64_t)Hkv * hd, hd, n, Hkv,
+                                 hd, (const int32_t*)dcells, kv_k(c, l), kv_v(c, l), c->n_ctx, c->stream));
+    } else if (c->kv_dtype == TDF_F32) {
       kv_import_kernel<float><<<blocks, 256, 0, c->stream>>>((float*)kv_k(c, l), (const float*)k_layers[l],
                                                             (const int32_t*)dcells, n, Hkv, hd, c->n_ctx);
       kv_import_kernel<float><<<blocks, 256, 0, c->stream>>>((float*)kv_v(c, l), (const float*)v_layers[l],
@@ -1195,8 +1234,12 @@ extern "C" int32_t tdf_kv_seq_shift(tdf_context* c, int32_t seq, int32_t p0, int
   TDF_HIP(hipMallocAsync(&dcs, cs.size() * 8, c->stream));
   TDF_HIP(hipMemcpyAsync(dcells, cells.data(), cells.size() * 4, hipMemcpyHostToDevice, c->stream));
   TDF_HIP(hipMemcpyAsync(dcs, cs.data(), cs.size() * 8, hipMemcpyHostToDevice, c->stream));
-  TDF_HIP(launch_kv_rotate(c->kv, c->kv_dtype, 2 * c->kv_layer_bytes, h.n_layer, h.n_head_kv, c->n_ctx, hd,
-                           (const int32_t*)dcells, (int)cells.size(), (const double2*)dcs, c->stream));
+  if (c->kv_dtype == TDF_Q8_0)
+    TDF_HIP(launch_kv_rotate_q8(c->kv, 2 * c->kv_layer_bytes, h.n_layer, h.n_head_kv, c->n_ctx, hd,
+                                (const int32_t*)dcells, (int)cells.size(), (const double2*)dcs, c->stream));
+  else
+    TDF_HIP(launch_kv_rotate(c->kv, c->kv_dtype, 2 * c->kv_layer_bytes, h.n_layer, h.n_head_kv, c->n_ctx, hd,
+                             (const int32_t*)dcells, (int)cells.size(), (const double2*)dcs, c->stream));
   TDF_HIP(hipFreeAsync(dcells, c->stream));
   TDF_HIP(hipFreeAsync(dcs, c->stream));
   TDF_HIP(hipStreamSynchronize(c->stream));
