@@ -76,6 +76,12 @@ def weight_bytes_per_element(cfg):
     return {"bf16": 2.0, "f32": 4.0, "q8_0": 34.0 / 32.0}[cfg["weight_dtype"]]
 
 
+def kv_cell_bytes(cfg):
+    """Bytes of one cached cell (K and V of every layer) in the cache type."""
+    per = {"bf16": 2.0, "f16": 2.0, "f32": 4.0, "q8_0": 34.0 / 32.0}[cfg["kv_dtype"]]
+    return cfg["n_layer"] * 2 * cfg["n_head_kv"] * cfg["head_dim"] * per
+
+
 def decode_bytes(cfg, ctx_len):
     """Algorithmic HBM bytes of one single-token decode step at context ctx_len:
     every weight once, K/V of the visible cells, the new K/V, the logits."""
@@ -83,7 +89,7 @@ def decode_bytes(cfg, ctx_len):
                                              "n_vocab", "n_layer"))
     p_layer = d * H * hd + 2 * d * Hkv * hd + H * hd * d + 3 * d * F
     weights = weight_bytes_per_element(cfg) * (L * p_layer + V * d)
-    kv_cell = L * 2 * Hkv * hd * 2
+    kv_cell = kv_cell_bytes(cfg)
     return weights + kv_cell * ctx_len + kv_cell + 4 * V
 
 
@@ -199,7 +205,7 @@ def decode_bytes_multi(cfg, ctxs):
     d, H, Hkv, hd, F, V, L = (cfg[k] for k in ("n_embd", "n_head", "n_head_kv", "head_dim", "n_ff",
                                              "n_vocab", "n_layer"))
     p_layer = d * H * hd + 2 * d * Hkv * hd + H * hd * d + 3 * d * F
-    kv_cell = L * 2 * Hkv * hd * 2
+    kv_cell = kv_cell_bytes(cfg)
     return (weight_bytes_per_element(cfg) * (L * p_layer + V * d) + kv_cell * (sum(ctxs) + len(ctxs))
             + 4 * V * len(ctxs))
 
@@ -243,15 +249,16 @@ def run_multiseq(args, cfg):
     tps = S * args.steps / t_dec
     log(f"prefill {lens.sum() / t_pre:.0f} tok/s, decode {tps:.1f} tok/s ({ms:.3f} ms per 32-token step)")
     return {
-        "metric": "decode tok/s (% HBM peak), 8B-shape bf16, 32 sequences" if cfg["weight_dtype"] == "bf16" else
-                  f"decode tok/s (% HBM peak), 8B-shape {cfg['weight_dtype'].upper()} weights, 32 sequences",
+        "metric": ("decode tok/s (% HBM peak), 8B-shape bf16, 32 sequences" if cfg["weight_dtype"] == "bf16" else
+                   f"decode tok/s (% HBM peak), 8B-shape {cfg['weight_dtype'].upper()} weights, 32 sequences")
+                  + ("" if cfg["kv_dtype"] == "bf16" else f", {cfg['kv_dtype'].upper()} cache"),
         "value": round(tps, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg["weight_dtype"] == "bf16" else f"f32 ({cfg['weight_dtype']} weights)",
         "data": "synthetic",
         "config": {"workload": f"llama8b_multiseq: {S} sequences, prompts {int(lens.min())}..{int(lens.max())} "
                                f"tokens prefilled per sequence, then lock-step steps of {S} tokens, all rows' logits; "
-                               f"KV bf16 {cfg['n_ctx']} cells"},
+                               f"KV {cfg['kv_dtype']} {cfg['n_ctx']} cells"},
         "decode": {"tok_s": round(tps, 2), "sum_ctx_mean": round(sum(mean), 1),
                    "algorithmic_bytes_per_step": int(step_bytes),
                    "achieved_GBs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
@@ -339,6 +346,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--weights", choices=["bf16", "q8_0"], default=None,
                     help="weight storage of the single-sequence workload (default: the config's, bf16)")
+    ap.add_argument("--kv", choices=["bf16", "f16", "q8_0"], default=None,
+                    help="KV cache element type (default: the config's)")
     ap.add_argument("--swa", type=int, default=0,
                     help="sliding-window attention of this many positions on every layer (0: none)")
     args = ap.parse_args()
@@ -359,6 +368,8 @@ def main():
         cfg["n_swa"] = args.swa
     if args.weights:
         cfg["weight_dtype"] = args.weights
+    if args.kv:
+        cfg["kv_dtype"] = args.kv
     q8 = cfg["weight_dtype"] == "q8_0"
     if args.config == "llama8b_multiseq":
         print(json.dumps(run_multiseq(args, cfg)), flush=True)
