@@ -16,7 +16,7 @@ import tdf_synth
 from oracle import OracleContext
 
 from gpu_common import TOL_BF16, check_logits, check_token, device_model, log, make_weights, oracle_model
-from test_gpu_parity import SMALL, run_pair
+from test_gpu_parity import SMALL, run_pair, teacher_forced
 from test_gpu_swa import SMALL64
 
 pytestmark = pytest.mark.gpu
@@ -24,8 +24,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("cfg0", [SMALL, SMALL64], ids=["hd32", "hd64"])
 def test_prefill_and_steps(cfg0):
-    """150 tokens in ubatches of 64, 64, 22 (attention over the quantized
-    rows on the vector units), logits for every row, then three steps."""
+    """150 tokens in ubatches of 64, 64, 22, logits for every row, then three
+    steps (head_dim 32: vector-unit attention; 64: matrix cores)."""
     cfg, w = make_weights(cfg0)
     prompt = tdf_synth.prompt(cfg, 0, 150)
     calls = [dict(tokens=prompt)] + [dict(tokens=[int(t)]) for t in tdf_synth.prompt(cfg, 1, 3)]
@@ -84,3 +84,17 @@ def test_drop_and_shift_then_decode():
         ro = oc.decode([int(t)])
         assert gc.last_slots() == ro.slots
         check_logits(gc.logits_ith(0), ro.logits[0], TOL_BF16, f"kvq8 shift step {k}")
+
+
+@pytest.mark.parametrize("hd,n_head,n_head_kv", [(128, 8, 2), (128, 2, 2), (64, 8, 1)], ids=["hd128g4", "hd128g1", "hd64g8"])
+def test_matrix_core_long_context(hd, n_head, n_head_kv):
+    """Matrix-core attention over Q8_0 rows (codes widened to bf16, key block
+    scales on the 32-deep score products, value block scales folded into the
+    probabilities): a 1100-token prompt in ubatches of 512, 512, 76, then
+    four steps whose 1100+ cells split into chunks of 128 that are merged
+    (a ragged last tile in each)."""
+    cfg0 = dict(SMALL, n_embd=256, n_head=n_head, n_head_kv=n_head_kv, head_dim=hd, n_ff=256, seed=31 + hd + n_head)
+    cfg, w = make_weights(cfg0)
+    prompt = tdf_synth.prompt(cfg, 0, 1100)
+    log(f"q8 cache matrix cores hd={hd} G={n_head // n_head_kv}")
+    teacher_forced(cfg, w, 1200, prompt, 4, TOL_BF16, "q8_0", n_ubatch=512, label=f"kvq8-mfma-hd{hd}")

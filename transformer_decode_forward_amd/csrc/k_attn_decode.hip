@@ -380,6 +380,29 @@ __device__ __forceinline__ float dpp_max(float v) {
   return fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, -INFINITY),
                                                                       __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false)));
 }
+// Q8_0 rows use the bf16 products: the int8 codes are exact in bf16
+template <> struct Mfma16<kv_q8> : Mfma16<kv_bf16> {};
+
+// 8 int8 codes -> 8 bf16 (exact: at most 8 significant bits)
+__device__ __forceinline__ bf16x8 q8_widen8(uint2 q) {
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w = j < 2 ? q.x : q.y;
+    const int b = (j & 1) * 2;
+    const uint32_t f0 = __builtin_bit_cast(uint32_t, (float)((int32_t)(w << (24 - 8 * b)) >> 24));
+    const uint32_t f1 = __builtin_bit_cast(uint32_t, (float)((int32_t)(w << (16 - 8 * b)) >> 24));
+    o[j] = (f0 >> 16) | (f1 & 0xFFFF0000u);
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+// fp16 scale b of a row's scale word(s)
+__device__ __forceinline__ float q8_scale(uint2 r, int b) {
+  const uint32_t w = b < 2 ? r.x : r.y;
+  return f16_to_f32((uint16_t)(w >> (16 * (b & 1))));
+}
+__device__ __forceinline__ float q8_scale(uint32_t r, int b) { return f16_to_f32((uint16_t)(r >> (16 * b))); }
+
 // max / sum over each row of 16 lanes, every lane of the row receiving it
 __device__ __forceinline__ float row16_max(float v) {
   v = dpp_max<0xB1>(v);
@@ -398,6 +421,15 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
   typedef typename KvStore<KvT>::T ST;
   static_assert(HD == 64 || HD == 128, "head_dim 64 or 128");
   static_assert(G >= 1 && G <= 8, "at most 8 query heads per kv head");
+  // Q8_0 rows: the codes (8 per lane and load) are widened to bf16 for the
+  // products; each 32-deep score product is scaled by its cell's key block
+  // scale, and the probabilities are multiplied by the value block scales
+  // before the value product (one left operand per 32 output dimensions)
+  constexpr bool Q8 = std::is_same<KvT, kv_q8>::value;
+  constexpr int NB = HD / 32;  // Q8_0 blocks per row
+  typedef typename std::conditional<Q8, uint2, vec>::type KRaw;
+  typedef typename std::conditional<Q8, uint2, uint4>::type VRaw;
+  typedef typename std::conditional<(HD == 128), uint2, uint32_t>::type SRaw;
   constexpr int NKC = HD / 32;   // 32-deep slices of the head dimension (scores)
   constexpr int NN = HD / 16;    // 16-wide output column blocks (P V)
   constexpr int PR = HD / 8;     // V loads: lanes per row (8 dimensions each)
@@ -409,6 +441,7 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
   __shared__ float pt_s[4][G][16];
   __shared__ float acc_s[4][G][HD];
   __shared__ float m_s[4][G], l_s[4][G];
+  __shared__ float vs_s[4][16][Q8 ? NB : 1];  // Q8_0: value block scales of the wave's tile
 
   const int j = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -421,6 +454,13 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
   const int32_t* cells = a.cell_list + a.list_off[t];
   const ST* kc = (const ST*)a.k_cache + (int64_t)g * a.n_ctx * HD;
   const ST* vc = (const ST*)a.v_cache + (int64_t)g * a.n_ctx * HD;
+  // Q8_0 scale rows of this kv head (NB fp16 per cell)
+  const SRaw* ksc = nullptr;
+  const SRaw* vsc = nullptr;
+  if constexpr (Q8) {
+    ksc = (const SRaw*)((const int8_t*)a.k_cache + (int64_t)a.Hkv * a.n_ctx * HD) + (int64_t)g * a.n_ctx;
+    vsc = (const SRaw*)((const int8_t*)a.v_cache + (int64_t)a.Hkv * a.n_ctx * HD) + (int64_t)g * a.n_ctx;
+  }
   for (int e = tid; e < kCellStage; e += 256) {
     const int32_t v = cells[c_lo + min(e, span - 1)];
     cell_s[e] = v;  // entries past the span repeat its last cell
@@ -470,15 +510,20 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
   }
   short* vw = v_s[wv];
   auto cell_of = [&](int tl, int r) { return cell_s[min(tl * 16 + r, span - 1)]; };
-  vec kn[NKC];
-  uint4 vn[CPL];
+  KRaw kn[NKC];
+  VRaw vn[CPL];
+  SRaw ksr, vsr;  // Q8_0: key scales of the lane's cell, value scales of cell lane % 16
   int tl = wv;
   {
     const int ck = cell_of(tl, lane & 15);
 #pragma unroll
-    for (int kk = 0; kk < NKC; ++kk) kn[kk] = *(const vec*)(kc + (int64_t)ck * HD + kk * 32 + (lane >> 4) * 8);
+    for (int kk = 0; kk < NKC; ++kk) kn[kk] = *(const KRaw*)(kc + (int64_t)ck * HD + kk * 32 + (lane >> 4) * 8);
 #pragma unroll
-    for (int pi = 0; pi < CPL; ++pi) vn[pi] = *(const uint4*)(vc + (int64_t)cell_of(tl, rg * CPL + pi) * HD + pc * 8);
+    for (int pi = 0; pi < CPL; ++pi) vn[pi] = *(const VRaw*)(vc + (int64_t)cell_of(tl, rg * CPL + pi) * HD + pc * 8);
+    if constexpr (Q8) {
+      ksr = ksc[ck];
+      vsr = vsc[ck];
+    }
   }
   for (; tl < ntiles; tl += 4) {
     const int nt = min(tl + 4, ntiles - 1);  // next tile of this wave (clamped)
@@ -486,24 +531,45 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
     // the next tile's V requested into the same registers
 #pragma unroll
     for (int pi = 0; pi < CPL; ++pi) {
+      uint4 v4;
+      if constexpr (Q8) v4 = __builtin_bit_cast(uint4, q8_widen8(vn[pi]));
+      else v4 = vn[pi];
       uint2* dst = (uint2*)(vw + (rg * CPL + pi) * VP + pc * 8);
-      dst[0] = make_uint2(vn[pi].x, vn[pi].y);
-      dst[1] = make_uint2(vn[pi].z, vn[pi].w);
+      dst[0] = make_uint2(v4.x, v4.y);
+      dst[1] = make_uint2(v4.z, v4.w);
+    }
+    if constexpr (Q8) {
+      if (lane < 16) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) vs_s[wv][lane][b] = q8_scale(vsr, b);
+      }
     }
 #pragma unroll
-    for (int pi = 0; pi < CPL; ++pi) vn[pi] = *(const uint4*)(vc + (int64_t)cell_of(nt, rg * CPL + pi) * HD + pc * 8);
+    for (int pi = 0; pi < CPL; ++pi) vn[pi] = *(const VRaw*)(vc + (int64_t)cell_of(nt, rg * CPL + pi) * HD + pc * 8);
+    if constexpr (Q8) vsr = vsc[cell_of(nt, lane & 15)];
     // scores: component i of lane l is head 4 (l / 16) + i of cell l % 16;
     // then the next tile's K requested into the same registers
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NKC; ++kk) {
-      s = M::mma(qh[kk], kn[kk], s);
-      s = M::mma(ql[kk], kn[kk], s);
+      if constexpr (Q8) {
+        const vec kv = q8_widen8(kn[kk]);
+        f32x4 tk = {0.f, 0.f, 0.f, 0.f};
+        tk = M::mma(qh[kk], kv, tk);
+        tk = M::mma(ql[kk], kv, tk);
+        const float dk = q8_scale(ksr, kk);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = fmaf(dk, tk[i], s[i]);
+      } else {
+        s = M::mma(qh[kk], kn[kk], s);
+        s = M::mma(ql[kk], kn[kk], s);
+      }
     }
     {
       const int ck = cell_of(nt, lane & 15);
 #pragma unroll
-      for (int kk = 0; kk < NKC; ++kk) kn[kk] = *(const vec*)(kc + (int64_t)ck * HD + kk * 32 + (lane >> 4) * 8);
+      for (int kk = 0; kk < NKC; ++kk) kn[kk] = *(const KRaw*)(kc + (int64_t)ck * HD + kk * 32 + (lane >> 4) * 8);
+      if constexpr (Q8) ksr = ksc[ck];
     }
     const bool live = tl * 16 + (lane & 15) < span;
     float mr[4];  // reference max of this lane's heads
@@ -559,6 +625,7 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
       if (hrow + i < G) pt_s[wv][hrow + i][lane & 15] = ps[i];
     __builtin_amdgcn_wave_barrier();
     vec4 ph, pl;
+    vec4 phb[Q8 ? NB : 1], plb[Q8 ? NB : 1];  // Q8_0: probabilities times the value block scales
     {
       const int hp = lane & 15;
       const float4 p4 = *(const float4*)&pt_s[wv][min(hp, G - 1)][hrow];
@@ -569,6 +636,14 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
         M::split(hp < G ? pv[q] : 0.f, hi, lo);
         ph[q] = __builtin_bit_cast(typename std::remove_reference<decltype(ph[0])>::type, hi);
         pl[q] = __builtin_bit_cast(typename std::remove_reference<decltype(pl[0])>::type, lo);
+        if constexpr (Q8) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            M::split(hp < G ? pv[q] * vs_s[wv][hrow + q][b] : 0.f, hi, lo);
+            phb[b][q] = __builtin_bit_cast(typename std::remove_reference<decltype(ph[0])>::type, hi);
+            plb[b][q] = __builtin_bit_cast(typename std::remove_reference<decltype(pl[0])>::type, lo);
+          }
+        }
       }
     }
     // value product: right operand lane l = cells 4 (l / 16) .. + 4 of
@@ -582,8 +657,13 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
         const short x = vw[(hrow + q) * VP + n * 16 + (lane & 15)];
         b[q] = __builtin_bit_cast(typename std::remove_reference<decltype(b[0])>::type, x);
       }
-      acc[n] = M::mma4(ph, b, acc[n]);
-      acc[n] = M::mma4(pl, b, acc[n]);
+      if constexpr (Q8) {
+        acc[n] = M::mma4(phb[n / 2], b, acc[n]);
+        acc[n] = M::mma4(plb[n / 2], b, acc[n]);
+      } else {
+        acc[n] = M::mma4(ph, b, acc[n]);
+        acc[n] = M::mma4(pl, b, acc[n]);
+      }
     }
     acc_l = M::mma4(ph, ones, acc_l);
     acc_l = M::mma4(pl, ones, acc_l);
@@ -709,10 +789,10 @@ template <typename KvT, int HD>
 static hipError_t attn_launch_hd(const AttnArgs& a, hipStream_t s) {
   const int G = a.H / a.Hkv;
   dim3 grid(a.n_chunks, a.Hkv, a.T);
-  // 16-bit caches with head_dim 64 or 128: scores and value products on the
-  // matrix cores (chunks of at most kCellStage cells)
+  // 16-bit and Q8_0 caches with head_dim 64 or 128: scores and value
+  // products on the matrix cores (chunks of at most kCellStage cells)
   bool done = false;
-  if constexpr (!std::is_same<KvT, float>::value && !std::is_same<KvT, kv_q8>::value && (HD == 64 || HD == 128)) {
+  if constexpr (!std::is_same<KvT, float>::value && (HD == 64 || HD == 128)) {
     if (a.chunk <= kCellStage) {
       switch (G) {
         case 1: attn_decode_mfma_kernel<KvT, HD, 1><<<grid, 256, 0, s>>>(a); break;

@@ -164,12 +164,12 @@ struct AttnArgs {
   uint16_t* out_lo = nullptr;
 };
 hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t s);
-// Decode attention stages a block's cell indices in LDS; with 16-bit caches
-// and head_dim 64 or 128 it runs on the matrix cores when a.chunk is at most
+// Decode attention stages a block's cell indices in LDS; with 16-bit or Q8_0
+// caches and head_dim 64 or 128 it runs on the matrix cores when a.chunk is at most
 // this many cells.
 constexpr int kDecodeCellStage = 1024;
 inline bool attn_decode_on_mfma(int kv_dtype, int hd) {
-  return (kv_dtype == TDF_F16 || kv_dtype == TDF_BF16) && (hd == 64 || hd == 128);
+  return (kv_dtype == TDF_F16 || kv_dtype == TDF_BF16 || kv_dtype == TDF_Q8_0) && (hd == 64 || hd == 128);
 }
 // merge of split partials only (part_* -> out / out_bf16)
 hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s);
