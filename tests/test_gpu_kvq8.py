@@ -88,11 +88,12 @@ def test_drop_and_shift_then_decode():
 
 @pytest.mark.parametrize("hd,n_head,n_head_kv", [(128, 8, 2), (128, 2, 2), (64, 8, 1)], ids=["hd128g4", "hd128g1", "hd64g8"])
 def test_matrix_core_long_context(hd, n_head, n_head_kv):
-    """Matrix-core attention over Q8_0 rows (codes widened to bf16, key block
-    scales on the 32-deep score products, value block scales folded into the
-    probabilities): a 1100-token prompt in ubatches of 512, 512, 76, then
-    four steps whose 1100+ cells split into chunks of 128 that are merged
-    (a ragged last tile in each)."""
+    """Matrix-core attention over Q8_0 rows: a 1100-token prompt in ubatches
+    of 512, 512, 76 (prefill attention: blocks dequantized into LDS as bf16
+    hi/lo pairs), then four steps (decode attention: codes widened to bf16,
+    key block scales on the 32-deep score products, value block scales folded
+    into the probabilities) whose 1100+ cells split into chunks of 128 that
+    are merged, a ragged last tile in each."""
     cfg0 = dict(SMALL, n_embd=256, n_head=n_head, n_head_kv=n_head_kv, head_dim=hd, n_ff=256, seed=31 + hd + n_head)
     cfg, w = make_weights(cfg0)
     prompt = tdf_synth.prompt(cfg, 0, 1100)

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 SMALL64 = dict(SMALL, n_embd=256, n_head=4, n_head_kv=2, head_dim=64, n_ff=256, seed=12)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f16", "q8_0"])
 def test_window_prefill_tiles_and_decode(kv_dtype):
     """150 tokens in ubatches of 64, 64, 22 with a 37-position window on layer
     0 (query tiles of 32 whose first visible entries differ), every row's

@@ -25,6 +25,12 @@
 // each product taking two MFMAs, so that the scores and the weighted sums keep
 // about 16 significant bits, as the projections do.
 //
+// Q8_0 caches (blocks of 32 along the head dimension: fp16 scale d, int8
+// codes q): the block's staging threads form d * q (exact in float32) and
+// store it in LDS as a bf16 pair hi + lo, shared by the G waves; each product
+// adds a third MFMA for the low part (Klo Qhi, Vlo Phi), so K and V enter
+// with about 16 significant bits.
+//
 // With n_splits > 1 each block covers one range of `chunk` list entries and
 // writes (max, sum, unnormalised accumulator) partials, merged afterwards by
 // the decode merge kernel.
@@ -44,6 +50,7 @@ template <> struct MfmaOf<kv_bf16> {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
 };
+template <> struct MfmaOf<kv_q8> : MfmaOf<kv_bf16> {};
 template <> struct MfmaOf<kv_f16> {
   typedef f16x8 vec;
   typedef _Float16 elem;
@@ -62,8 +69,15 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))
   typedef typename M::vec vec;
   constexpr int KP = HD + 8;     // K row pitch (elements)
   constexpr int VP = kCT + 8;    // V^T row pitch (elements)
+  constexpr bool Q8 = std::is_same<KvT, kv_q8>::value;
+  constexpr int NB = HD / 32;    // Q8_0 blocks per row
+  typedef typename std::conditional<Q8, int8_t, uint16_t>::type ST;
+  typedef typename std::conditional<Q8, uint2, uint4>::type Raw;  // 8 stored elements
   __shared__ __attribute__((aligned(16))) uint16_t k_s[kCT * KP];
   __shared__ __attribute__((aligned(16))) uint16_t vt_s[HD * VP];
+  // Q8_0: low parts of the dequantized tiles
+  __shared__ __attribute__((aligned(16))) uint16_t kl_s[Q8 ? kCT * KP : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t vtl_s[Q8 ? HD * VP : 8];
 
   const int tile = blockIdx.x, g = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -77,8 +91,15 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))
   if (c_lo >= tile_nvis) return;
   const int c_hi = min(tile_nvis, c_lo + a.chunk);
   const int32_t* cells = a.cell_list + a.tile_list_off[tile];
-  const uint16_t* kc = (const uint16_t*)a.k_cache + (int64_t)g * a.n_ctx * HD;
-  const uint16_t* vc = (const uint16_t*)a.v_cache + (int64_t)g * a.n_ctx * HD;
+  const ST* kc = (const ST*)a.k_cache + (int64_t)g * a.n_ctx * HD;
+  const ST* vc = (const ST*)a.v_cache + (int64_t)g * a.n_ctx * HD;
+  // Q8_0 scales: [Hkv][n_ctx][NB] fp16 after the codes
+  const uint16_t* ksc = nullptr;
+  const uint16_t* vsc = nullptr;
+  if constexpr (Q8) {
+    ksc = (const uint16_t*)((const int8_t*)a.k_cache + (int64_t)a.Hkv * a.n_ctx * HD) + (int64_t)g * a.n_ctx * NB;
+    vsc = (const uint16_t*)((const int8_t*)a.v_cache + (int64_t)a.Hkv * a.n_ctx * HD) + (int64_t)g * a.n_ctx * NB;
+  }
   const float scale = rsqrtf((float)HD);
 
   typedef typename M::elem E;
@@ -118,15 +139,21 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))
   // the current one would need 32 more registers than the kernel has left:
   // measured slower with the spills).
   constexpr int SUB = PPT < 4 ? PPT : 4;
-  uint4 kreg[SUB], vreg[SUB];
+  Raw kreg[SUB], vreg[SUB];
+  uint16_t ksreg[SUB], vsreg[SUB];  // Q8_0: scales of the pieces' blocks
 #define TILE_LOAD(c0_, i0_)                                                            \
   do {                                                                                 \
     _Pragma("unroll") for (int i = 0; i < SUB; ++i) {                                  \
       const int ii = tid + ((i0_) + i) * 64 * G;                                       \
       const int cc = min((c0_) + ii % kCT, c_hi - 1);                                  \
-      const int64_t row = (int64_t)(staged ? cell_s[cc - c_lo] : cells[cc]) * HD + (ii / kCT) * 8; \
-      kreg[i] = *(const uint4*)(kc + row);                                             \
-      vreg[i] = *(const uint4*)(vc + row);                                             \
+      const int64_t cell = staged ? cell_s[cc - c_lo] : cells[cc];                     \
+      const int64_t row = cell * HD + (ii / kCT) * 8;                                  \
+      kreg[i] = *(const Raw*)(kc + row);                                               \
+      vreg[i] = *(const Raw*)(vc + row);                                               \
+      if constexpr (Q8) {                                                              \
+        ksreg[i] = ksc[cell * NB + (ii / kCT) / 4];                                    \
+        vsreg[i] = vsc[cell * NB + (ii / kCT) / 4];                                    \
+      }                                                                                \
     }                                                                                  \
   } while (0)
   for (int c0 = c_lo; c0 < c_hi; c0 += kCT) {
@@ -138,10 +165,31 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))
       for (int i = 0; i < SUB; ++i) {
         const int ii = tid + (i0 + i) * 64 * G;
         const int c = ii % kCT, dchunk = (ii / kCT) * 8;
-        *(uint4*)&k_s[c * KP + dchunk] = kreg[i];
-        const uint16_t* vh = (const uint16_t*)&vreg[i];
+        if constexpr (Q8) {
+          const float dk = f16_to_f32(ksreg[i]), dv = f16_to_f32(vsreg[i]);
+          const int8_t* kq = (const int8_t*)&kreg[i];
+          const int8_t* vq = (const int8_t*)&vreg[i];
+          uint16_t kh[8], kl[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vt_s[(dchunk + e) * VP + c] = vh[e];
+          for (int e = 0; e < 8; ++e) {
+            split_bf16(dk * (float)kq[e], kh[e], kl[e]);
+            uint16_t vh, vl;
+            split_bf16(dv * (float)vq[e], vh, vl);
+            vt_s[(dchunk + e) * VP + c] = vh;
+            vtl_s[(dchunk + e) * VP + c] = vl;
+          }
+          auto pack = [](const uint16_t* x) {
+            return make_uint4(x[0] | ((uint32_t)x[1] << 16), x[2] | ((uint32_t)x[3] << 16),
+                              x[4] | ((uint32_t)x[5] << 16), x[6] | ((uint32_t)x[7] << 16));
+          };
+          *(uint4*)&k_s[c * KP + dchunk] = pack(kh);
+          *(uint4*)&kl_s[c * KP + dchunk] = pack(kl);
+        } else {
+          *(uint4*)&k_s[c * KP + dchunk] = kreg[i];
+          const uint16_t* vh = (const uint16_t*)&vreg[i];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vt_s[(dchunk + e) * VP + c] = vh[e];
+        }
       }
     }
     __syncthreads();
@@ -157,6 +205,10 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))
         const vec kf = *(const vec*)&k_s[(sub * 32 + ql) * KP + ks * 16 + qg * 8];
         s[sub] = M::mma(kf, qh[ks], s[sub]);
         s[sub] = M::mma(kf, qlo[ks], s[sub]);
+        if constexpr (Q8) {
+          const vec kfl = *(const vec*)&kl_s[(sub * 32 + ql) * KP + ks * 16 + qg * 8];
+          s[sub] = M::mma(kfl, qh[ks], s[sub]);
+        }
       }
     }
     // causal / range mask and online softmax for this lane's query
@@ -206,6 +258,12 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))
           const vec vf = __builtin_bit_cast(vec, make_uint4(lo.x, lo.y, hi.x, hi.y));
           o[dt] = M::mma(vf, ph[sub][s2], o[dt]);
           o[dt] = M::mma(vf, plo[sub][s2], o[dt]);
+          if constexpr (Q8) {
+            const uint16_t* vrl = &vtl_s[(dt * 32 + ql) * VP];
+            const uint2 l2 = *(const uint2*)(vrl + cb);
+            const uint2 h2 = *(const uint2*)(vrl + cb + 8);
+            o[dt] = M::mma(__builtin_bit_cast(vec, make_uint4(l2.x, l2.y, h2.x, h2.y)), ph[sub][s2], o[dt]);
+          }
         }
     }
   }
@@ -266,7 +324,7 @@ static hipError_t prefill_attn_hd(const PrefillAttnArgs& a, hipStream_t s) {
 }
 
 bool prefill_attention_supported(int kv_dtype, int head_dim) {
-  return (kv_dtype == TDF_BF16 || kv_dtype == TDF_F16) && (head_dim == 64 || head_dim == 128);
+  return (kv_dtype == TDF_BF16 || kv_dtype == TDF_F16 || kv_dtype == TDF_Q8_0) && (head_dim == 64 || head_dim == 128);
 }
 
 hipError_t launch_attention_prefill(const PrefillAttnArgs& a, hipStream_t s) {
@@ -276,6 +334,8 @@ hipError_t launch_attention_prefill(const PrefillAttnArgs& a, hipStream_t s) {
     e = a.hd == 128 ? prefill_attn_hd<kv_bf16, 128>(a, s) : prefill_attn_hd<kv_bf16, 64>(a, s);
   else if (a.kv_dtype == TDF_F16)
     e = a.hd == 128 ? prefill_attn_hd<kv_f16, 128>(a, s) : prefill_attn_hd<kv_f16, 64>(a, s);
+  else if (a.kv_dtype == TDF_Q8_0)
+    e = a.hd == 128 ? prefill_attn_hd<kv_q8, 128>(a, s) : prefill_attn_hd<kv_q8, 64>(a, s);
   else
     return hipErrorInvalidValue;
   if (e != hipSuccess || a.n_splits == 1) return e;
