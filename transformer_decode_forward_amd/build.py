@@ -26,13 +26,18 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-x", "hip"
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
+# Decode attention: matrix-core accumulators in ordinary VGPRs.  With the
+# default (AGPR accumulators) the compiler copies the 36 accumulator registers
+# out and back around every tile, because the online-softmax rescale works on
+# them with vector instructions.
+EXTRA_FLAGS = {"k_attn_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src + ".o")
     if src.endswith(".hip"):
-        cmd = [HIPCC] + HIP_FLAGS + ["-c", path, "-o", obj]
+        cmd = [HIPCC] + HIP_FLAGS + EXTRA_FLAGS.get(src, []) + ["-c", path, "-o", obj]
     else:
         cmd = ["g++"] + HOST_FLAGS + ["-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
