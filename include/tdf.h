@@ -119,7 +119,7 @@ typedef struct {
 /* n_ctx = KV cells; n_batch = largest batch per decode (clamped to n_ctx);
  * n_ubatch = tokens per forward chunk (clamped to n_batch); n_seq_max <= 64;
  * kv_dtype = TDF_F32, TDF_F16, TDF_BF16 or TDF_Q8_0 (head_dim a multiple of
- * 32; attention then runs on the vector units); output_all = default output flag
+ * 32; blocks of 32 along head_dim); output_all = default output flag
  * of every token instead of the last; stream = hipStream_t to run on (NULL:
  * the context creates its own). */
 typedef struct {
