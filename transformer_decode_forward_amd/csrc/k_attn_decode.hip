@@ -324,7 +324,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 // ---------------------------------------------------------------------------
-// Decode attention with the scores on the matrix cores (16-bit caches, head
+// Decode attention with the scores on the matrix cores (16-bit and Q8_0 caches, head
 // dimension 64 or 128).  Block (chunk j, kv head g, token t) as above; each
 // wave takes every fourth 16-cell tile of the chunk.  Scores: the G query
 // heads (rows of a 16-row operand, the rest zero) times the tile's keys as
