@@ -84,3 +84,44 @@ def test_margin_flags_boundaries():
     z = np.log(p)
     assert sample_margin(z, 1.0, 3, 1.0, 0.0, 0.5) < 1e-9        # u * total on a cumulative boundary
     assert sample_margin(z, 1.0, 3, 1.0, 0.0, 0.25) > 0.1
+
+
+def test_margin_values_on_hand_cases():
+    """The margin of each decision, written out from its definition on a
+    distribution with known probabilities (0.5, 0.3, 0.2)."""
+    p = np.array([0.5, 0.3, 0.2])
+    z = np.log(p)
+    # greedy: the top-2 logit gap
+    assert sample_margin(np.array([1.0, 3.0, 2.5]), 0.0, 3, 1.0, 0.0, 0.3) == 0.5
+    # Top-P 0.75: cumulative 0.5 | 0.8, 1.0 -> nearest cut distance 0.05; the
+    # draw over the single survivor is 0.5 (1 - u) = 0.45 away
+    np.testing.assert_allclose(sample_margin(z, 1.0, 3, 0.75, 0.0, 0.1), 0.05, rtol=1e-12)
+    # Min-P 0.5: threshold 0.25, relative distances |0.3 - 0.25| / 0.25 = |0.2 - 0.25| / 0.25 = 0.2;
+    # the draw over the two survivors at u = 0.3 is min(|0.5 - 0.24|, |0.8 - 0.24|) = 0.26
+    np.testing.assert_allclose(sample_margin(z, 1.0, 3, 1.0, 0.5, 0.3), 0.2, rtol=1e-12)
+    # the draw alone: |cumulative - u| = 0.01 at u = 0.49
+    np.testing.assert_allclose(sample_margin(z, 1.0, 3, 1.0, 0.0, 0.49), 0.01, rtol=1e-9)
+    # temperature enters before the softmax: T = 2 on log p gives p^(1/2) renormalised
+    q = np.sqrt(p) / np.sqrt(p).sum()
+    np.testing.assert_allclose(sample_margin(z, 2.0, 3, 1.0, 0.0, 0.2), abs(q[0] - 0.2), rtol=1e-9)
+
+
+def test_margin_locates_real_boundaries():
+    """Brute force: wherever the margin is small the token changes under a
+    tiny move of u, and a move of u below the margin never changes it."""
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        z = rng.normal(size=12) * 2
+        t, k, tp, mp = 0.9, 8, 0.9, 0.05
+        u = float(rng.uniform())
+        m = sample_margin(z, t, k, tp, mp, u)
+        tok = sample(z, t, k, tp, mp, u)
+        # the draw's cumulative moves by at most |du| * total <= |du| when u moves by du
+        for du in (-0.5 * m, 0.5 * m):
+            if 0.0 <= u + du < 1.0:
+                assert sample(z, t, k, tp, mp, u + du) == tok
+    # u set exactly on a cumulative boundary: the two sides differ
+    p = np.array([0.5, 0.3, 0.2])
+    z = np.log(p)
+    assert sample_margin(z, 1.0, 3, 1.0, 0.0, 0.8) < 1e-9
+    assert sample(z, 1.0, 3, 1.0, 0.0, 0.8 - 1e-6) != sample(z, 1.0, 3, 1.0, 0.0, 0.8 + 1e-6)
