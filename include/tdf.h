@@ -166,19 +166,32 @@ void tdf_context_free(tdf_context *c);
  * before returning. */
 int32_t tdf_decode(tdf_context *c, const tdf_batch *b);
 
-/* Rows with logits after the last successful tdf_decode. */
+/* Rows with logits after the last successful tdf_decode: the tokens whose
+ * logits flag was set (llama.cpp walkthrough, "Steps 14-15": the context keeps
+ * logits only for positions flagged in the batch).  TDF_E_INVALID for a NULL
+ * context. */
 int32_t tdf_n_outputs(const tdf_context *c);
 
-/* Batch indices (batch order) of those rows into out[n_outputs]; returns
- * n_outputs. */
+/* Batch indices (batch order) of those rows ("Steps 14-15": one row per
+ * flagged position, over every ubatch of the call) into the HOST array
+ * out[n_outputs] (may be NULL to query the count); returns n_outputs, or
+ * TDF_E_INVALID for a NULL context. */
 int32_t tdf_output_ids(const tdf_context *c, int32_t *out);
 
 /* HOST pointer to the n_vocab float32 logits of batch index i of the last
- * decode, or NULL if i was not flagged.  Valid until the next tdf_decode,
- * tdf_kv_clear or tdf_context_free (copied from the device on first use). */
+ * decode (llama.cpp walkthrough, "Steps 14-15": llama_get_logits_ith gives
+ * n_vocab floats for a position of the batch), or NULL if i was not flagged,
+ * is out of range, the context is a dry run, or the copy failed (message in
+ * tdf_last_error).  The memory belongs to the context: valid until the next
+ * tdf_decode, tdf_kv_clear or tdf_context_free (copied from the device on
+ * first use). */
 const float *tdf_get_logits_ith(tdf_context *c, int32_t i);
 
-/* DEVICE pointer to the [n_outputs][n_vocab] float32 logits. */
+/* DEVICE pointer to the [n_outputs][n_vocab] float32 logits of the last
+ * decode (the same rows as tdf_get_logits_ith, "Steps 14-15"), row r for
+ * batch index tdf_output_ids[r]; owned by the context, valid as above, NULL
+ * for a NULL or dry-run context.  Read it on the context's stream or after
+ * tdf_decode returned (it synchronises). */
 const float *tdf_get_logits_device(tdf_context *c);
 
 /* Greedy token (argmax, lowest index on ties) of batch index i, or
@@ -189,23 +202,40 @@ int32_t tdf_argmax_ith(const tdf_context *c, int32_t i);
  * "KV-cache and the Prefill / Decode stages"); TDF_E_INVALID for a bad s. */
 int32_t tdf_seq_pos_max(const tdf_context *c, int32_t s);
 
-/* Free every cell (the cache contents become unreachable). */
+/* Free every cell: every sequence becomes empty (seq_pos_max -1) and the
+ * next decode places its tokens from cell 0 again (llama.cpp walkthrough,
+ * "KV-cache and the Prefill / Decode stages": the cache is sized for n_ctx
+ * at creation and filled position by position; clearing makes the stored
+ * K/V unreachable without touching the device memory).  Also drops the
+ * logits of the last decode.  TDF_OK, or TDF_E_INVALID for a NULL context. */
 int32_t tdf_kv_clear(tdf_context *c);
 
-/* Inspection: position (-1 if free) and sequence bit mask of a cell. */
+/* Inspection of one cell's bookkeeping (Ollama engine page, "KV Cache: memory
+ * for causal attention": each cached slot records its position and the
+ * sequences it belongs to, from which the mask is built): *pos = position
+ * (-1 if free), *seq_mask = bit s set if sequence s holds the cell.  Either
+ * output pointer (HOST) may be NULL.  TDF_OK, or TDF_E_INVALID for a NULL
+ * context or a cell outside [0, n_ctx). */
 int32_t tdf_kv_cell(const tdf_context *c, int32_t cell, int32_t *pos, uint64_t *seq_mask);
 
-/* Cells given to the tokens of the last successful decode (batch order) into
- * slots[n_tokens]; returns n_tokens. */
+/* Cells given to the tokens of the last successful decode or import (batch
+ * order; Ollama engine page, "KV Cache": the slots found for the batch's K/V)
+ * into the HOST array slots[n_tokens] (may be NULL to query the count);
+ * returns n_tokens, or TDF_E_INVALID for a NULL context. */
 int32_t tdf_last_slots(const tdf_context *c, int32_t *slots);
 
-/* Place positions [pos0, pos0+n) of sequence s in cells (one chunk, the
- * ubatch placement rule) and fill them with given post-RoPE keys and values:
+/* Restore cached K/V (llama.cpp walkthrough, "KV-cache and the Prefill /
+ * Decode stages": the cache holds, per layer and position, the keys and
+ * values already computed, so later steps only read them).  Places positions
+ * [pos0, pos0+n) of sequence s in cells (one chunk, the ubatch placement
+ * rule) and fills them with the given post-RoPE keys and values:
  * k_layers[l] / v_layers[l] are DEVICE pointers to [n][n_head_kv][head_dim]
  * arrays in the context's kv dtype, float32 for a TDF_Q8_0 cache (quantized
- * on import) (HOST array of n_layer pointers).  Used
- * to restore a cache state.  Returns TDF_OK, TDF_NO_SLOT, TDF_E_INVALID (pos0
- * must exceed seq_pos_max(s)) or TDF_E_DEVICE. */
+ * on import); k_layers / v_layers are HOST arrays of n_layer pointers, read
+ * only during the call.  The cells are committed only after the device
+ * holds the rows; on any error nothing changes in the bookkeeping.  Returns
+ * TDF_OK, TDF_NO_SLOT, TDF_E_INVALID (pos0 must exceed seq_pos_max(s)) or
+ * TDF_E_DEVICE. */
 int32_t tdf_kv_import(tdf_context *c, int32_t s, int32_t pos0, int32_t n,
                       const void *const *k_layers, const void *const *v_layers);
 
@@ -287,6 +317,14 @@ int32_t tdf_time_op(tdf_context *c, int32_t op, int32_t n_tokens, int32_t reps, 
  * shape, replayed on later calls.  Counts of captures and replays so far.
  * Disabled in TDF_CTX_PROFILE contexts and when TDF_NO_GRAPH=1 is set. */
 int32_t tdf_graph_counts(const tdf_context *c, int64_t *captures, int64_t *replays);
+
+/* Failure injection for tests of the error paths (not part of the forward
+ * pass): the n-th device allocation the library makes from now on fails as
+ * if the device were out of memory (n <= 0 disarms).  The creators then
+ * return NULL and tdf_decode TDF_E_ALLOC with nothing changed.  Process-wide;
+ * the environment variable TDF_FAULT_ALLOC=n does the same for the n-th
+ * allocation of the process.  Returns TDF_OK. */
+int32_t tdf_fault_alloc(int32_t n);
 
 /* Message of the last failure on the calling thread ("" if none). */
 const char *tdf_last_error(void);

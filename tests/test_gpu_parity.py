@@ -177,6 +177,43 @@ def test_graph_replay_matches_eager_launches(monkeypatch):
     assert eager.graph_counts() == (0, 0)
 
 
+def test_graph_key_tracks_list_writes_of_earlier_ubatches(monkeypatch):
+    """A replayed tail ubatch must scatter its own cell-list writes.  The
+    writes of a call's ubatches are packed one after the other, so the tail's
+    writes start later when the first ubatch's tokens belong to two
+    sequences.  Call A: 64 + 20 tokens of sequence 0.  Call B: 64 tokens of
+    sequences {1, 2}, then 20 tokens of sequence 1: the tail has the same
+    size, rows and attention split as call A's, but its writes sit at another
+    offset.  Both calls' logits must match the oracle and plain launches."""
+    import transformer_decode_forward_amd as tdf
+    cfg, w = make_weights(SMALL)
+    gm = device_model(cfg, w)
+    kw = dict(n_ctx=512, n_ubatch=64, n_seq_max=3)
+    monkeypatch.setenv("TDF_NO_GRAPH", "1")
+    eager = tdf.Context(gm, kv_dtype="bf16", **kw)
+    monkeypatch.delenv("TDF_NO_GRAPH")
+    graphed = tdf.Context(gm, kv_dtype="bf16", **kw)
+    oc = OracleContext(oracle_model(cfg, w), kv_dtype="bf16", **kw)
+    calls = [dict(tokens=tdf_synth.prompt(cfg, 60, 84)),
+             dict(tokens=tdf_synth.prompt(cfg, 61, 84), seq_ids=[[1, 2]] * 64 + [[1]] * 20)]
+    for k, call in enumerate(calls):
+        assert eager.decode(**call) == 0 and graphed.decode(**call) == 0, tdf.tdf_last_error()
+        ro = oc.decode(**call)
+        assert graphed.last_slots() == eager.last_slots() == ro.slots
+        a, b = eager.logits_ith(83), graphed.logits_ith(83)
+        assert np.array_equal(a, b), (k, float(np.max(np.abs(a - b))))
+        check_logits(b, ro.logits[0], TOL_BF16, f"call {k}")
+        check_token(graphed.argmax_ith(83), ro.logits[0], f"call {k}")
+    # the two tails were captured separately
+    assert graphed.graph_counts()[0] == 2
+    # sequence 2 holds only the shared first ubatch: a step on it sees those cells
+    step = dict(tokens=[5], seq_ids=[[2]])
+    assert graphed.decode(**step) == 0
+    ro = oc.decode(**step)
+    assert ro.positions == [64]
+    check_logits(graphed.logits_ith(0), ro.logits[0], TOL_BF16, "seq 2 step")
+
+
 @pytest.mark.parametrize("kv_dtype", ["bf16", "f16"])
 def test_mid_size_ubatches_matrix_cores_streaming(kv_dtype):
     """Ubatches of 9..32 tokens (several sequences' decode steps) run the

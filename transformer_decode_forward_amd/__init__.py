@@ -96,6 +96,7 @@ def lib():
             "tdf_sample_logits": (_i32, [_vp, ctypes.c_void_p, _i32, _i32, ctypes.POINTER(tdf_sampling),
                                          ctypes.POINTER(_f32), ctypes.POINTER(_i32)]),
             "tdf_kv_seq_shift": (_i32, [_vp, _i32, _i32, _i32, _i32]),
+            "tdf_fault_alloc": (_i32, [_i32]),
             "tdf_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -137,6 +138,10 @@ def tdf_decode(c, b: tdf_batch) -> int:
 
 def tdf_last_error() -> str:
     return lib().tdf_last_error().decode()
+
+
+def tdf_fault_alloc(n: int) -> int:
+    return lib().tdf_fault_alloc(n)
 
 
 # ---- convenience objects ---------------------------------------------------

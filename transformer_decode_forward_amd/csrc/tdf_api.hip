@@ -36,21 +36,41 @@ thread_local std::string g_err;
 
 void set_err(const std::string& s) { g_err = s; }
 
-// test hook: TDF_FAULT_ALLOC=n makes the n-th device allocation fail
+// test hooks: TDF_FAULT_ALLOC=n in the environment makes the n-th device
+// allocation of the process fail; tdf_fault_alloc(n) makes the n-th next one
+// fail (host-side failure injection: the allocation is simply not made)
 int g_alloc_count = 0;
+int g_fail_in = 0;
 hipError_t dev_alloc(void** p, size_t bytes) {
   static const int fault_at = [] {
     const char* e = getenv("TDF_FAULT_ALLOC");
     return e ? atoi(e) : 0;
   }();
   ++g_alloc_count;
-  if (fault_at > 0 && g_alloc_count == fault_at) {
+  const bool planted = g_fail_in > 0 && --g_fail_in == 0;
+  if (planted || (fault_at > 0 && g_alloc_count == fault_at)) {
     *p = nullptr;
     return hipErrorOutOfMemory;
   }
   if (bytes == 0) bytes = 256;
   return hipMalloc(p, bytes);
 }
+
+// stream-ordered scratch of one call, released on every return path
+struct CallScratch {
+  hipStream_t s;
+  std::vector<void*> p;
+  explicit CallScratch(hipStream_t st) : s(st) {}
+  hipError_t alloc(void** out, size_t bytes) {
+    *out = nullptr;
+    hipError_t e = hipMallocAsync(out, bytes ? bytes : 256, s);
+    if (e == hipSuccess) p.push_back(*out);
+    return e;
+  }
+  ~CallScratch() {
+    for (void* x : p) (void)hipFreeAsync(x, s);
+  }
+};
 
 size_t dtype_size(int dt) { return dt == TDF_F32 ? 4 : 2; }
 
@@ -141,7 +161,8 @@ struct tdf_context {
 
   // launch replay: one instantiated graph per decode ubatch shape
   bool use_graphs = true;
-  std::map<std::tuple<int, int, int, int, int, const void*, const void*, int, int, int, int>, hipGraphExec_t> graphs;
+  std::map<std::tuple<int, int, int, int, int, const void*, const void*, const void*, int, int, int, int>,
+           hipGraphExec_t> graphs;
   int64_t n_graph_captures = 0, n_graph_replays = 0;
 
   // results of the last decode
@@ -395,6 +416,11 @@ extern "C" tdf_context* tdf_context_create(const tdf_model* m, const tdf_context
                                               : (size_t)Hkv * c->n_ctx * hd * dtype_size(c->kv_dtype);
   A(&c->kv, c->kv_layer_bytes * 2 * std::max(1, h.n_layer));
   A((void**)&c->cell_list, (size_t)c->n_seq_max * c->n_ctx * sizeof(int32_t));
+  // every entry a kernel reads is written first; zeros keep any entry in bounds regardless
+  if (rc == TDF_OK && hipMemset(c->cell_list, 0, (size_t)c->n_seq_max * c->n_ctx * sizeof(int32_t)) != hipSuccess) {
+    set_err("cell list initialisation failed");
+    rc = TDF_E_DEVICE;
+  }
   A((void**)&c->inv_freq, (size_t)(hd / 2) * sizeof(double));
   A((void**)&c->rope_cs, (size_t)U * (hd / 2) * sizeof(float2));
   A((void**)&c->x, (size_t)U * d * 4);
@@ -708,9 +734,12 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
 // (the ubatch's integers, cell lists, caches); the key holds everything that
 // enters a kernel argument.
 static int run_graphed(tdf_context* c, const UbatchDev& u) {
+  // the list writes sit after those of the call's earlier ubatches, whose
+  // count depends on how many sequences their tokens carry: the address is
+  // part of the key as the integers' address is
   const auto key = std::make_tuple(u.T, u.R, u.n_list_writes, u.attn_chunk, u.attn_grid,
-                                   (const void*)c->logits, (const void*)u.tokens, u.out_row0,
-                                   (int)u.sel_identity, u.attn_chunk_w, u.attn_grid_w);
+                                   (const void*)c->logits, (const void*)u.tokens, (const void*)u.list_writes,
+                                   u.out_row0, (int)u.sel_identity, u.attn_chunk_w, u.attn_grid_w);
   auto it = c->graphs.find(key);
   if (it == c->graphs.end()) {
     if (c->graphs.size() >= 64) {
@@ -1057,14 +1086,21 @@ extern "C" int32_t tdf_kv_import(tdf_context* c, int32_t s, int32_t pos0, int32_
       if (!k_layers[l] || !v_layers[l]) { set_err("missing layer array"); return TDF_E_INVALID; }
   std::vector<int32_t> slots;
   if (!c->book.find_slots(n, slots)) { set_err("not enough free KV cells"); return TDF_NO_SLOT; }
+  // the placement is worked out on a copy and committed only once the
+  // device holds the rows and the cell lists
+  KvBook next = c->book;
   std::vector<int64_t> writes;
-  for (int i = 0; i < n; ++i) c->book.place(slots[i], pos0 + i, 1ull << s, s, &writes);
-  c->last_slots = slots;
-  if (c->dry_run) return TDF_OK;
+  for (int i = 0; i < n; ++i) next.place(slots[i], pos0 + i, 1ull << s, s, &writes);
+  if (c->dry_run) {
+    c->book = std::move(next);
+    c->last_slots = slots;
+    return TDF_OK;
+  }
   const int Hkv = c->m->hp.n_head_kv, hd = c->m->hp.head_dim;
+  CallScratch scratch(c->stream);
   void *dcells = nullptr, *dwrites = nullptr;
-  TDF_HIP(hipMallocAsync(&dcells, (size_t)n * 4, c->stream));
-  TDF_HIP(hipMallocAsync(&dwrites, writes.size() * 8, c->stream));
+  TDF_HIP(scratch.alloc(&dcells, (size_t)n * 4));
+  TDF_HIP(scratch.alloc(&dwrites, writes.size() * 8));
   TDF_HIP(hipMemcpyAsync(dcells, slots.data(), (size_t)n * 4, hipMemcpyHostToDevice, c->stream));
   TDF_HIP(hipMemcpyAsync(dwrites, writes.data(), writes.size() * 8, hipMemcpyHostToDevice, c->stream));
   TDF_HIP(launch_scatter(c->cell_list, (const int64_t*)dwrites, (int)writes.size() / 2, c->stream));
@@ -1088,9 +1124,9 @@ extern "C" int32_t tdf_kv_import(tdf_context* c, int32_t s, int32_t pos0, int32_
     }
     TDF_HIP(hipGetLastError());
   }
-  TDF_HIP(hipFreeAsync(dcells, c->stream));
-  TDF_HIP(hipFreeAsync(dwrites, c->stream));
   TDF_HIP(hipStreamSynchronize(c->stream));
+  c->book = std::move(next);
+  c->last_slots = slots;
   return TDF_OK;
 }
 
@@ -1187,22 +1223,24 @@ extern "C" int32_t tdf_kv_seq_rm(tdf_context* c, int32_t seq, int32_t p0, int32_
     set_err("invalid kv_seq_rm arguments");
     return TDF_E_INVALID;
   }
-  c->book.seq_rm(seq, p0, p1);
-  if (c->dry_run) return TDF_OK;
-  // rewrite the device copy of seq's (compacted) cell list
-  const std::vector<int32_t>& lst = c->book.seq_cells(seq);
-  if (lst.empty()) return TDF_OK;
-  std::vector<int64_t> writes(2 * lst.size());
-  for (size_t i = 0; i < lst.size(); ++i) {
-    writes[2 * i] = (int64_t)seq * c->n_ctx + (int64_t)i;
-    writes[2 * i + 1] = lst[i];
+  KvBook next = c->book;
+  next.seq_rm(seq, p0, p1);
+  // rewrite the device copy of seq's (compacted) cell list, then commit
+  const std::vector<int32_t>& lst = next.seq_cells(seq);
+  if (!c->dry_run && !lst.empty()) {
+    std::vector<int64_t> writes(2 * lst.size());
+    for (size_t i = 0; i < lst.size(); ++i) {
+      writes[2 * i] = (int64_t)seq * c->n_ctx + (int64_t)i;
+      writes[2 * i + 1] = lst[i];
+    }
+    CallScratch scratch(c->stream);
+    void* dw = nullptr;
+    TDF_HIP(scratch.alloc(&dw, writes.size() * 8));
+    TDF_HIP(hipMemcpyAsync(dw, writes.data(), writes.size() * 8, hipMemcpyHostToDevice, c->stream));
+    TDF_HIP(launch_scatter(c->cell_list, (const int64_t*)dw, (int)lst.size(), c->stream));
+    TDF_HIP(hipStreamSynchronize(c->stream));
   }
-  void* dw = nullptr;
-  TDF_HIP(hipMallocAsync(&dw, writes.size() * 8, c->stream));
-  TDF_HIP(hipMemcpyAsync(dw, writes.data(), writes.size() * 8, hipMemcpyHostToDevice, c->stream));
-  TDF_HIP(launch_scatter(c->cell_list, (const int64_t*)dw, (int)lst.size(), c->stream));
-  TDF_HIP(hipFreeAsync(dw, c->stream));
-  TDF_HIP(hipStreamSynchronize(c->stream));
+  c->book = std::move(next);
   return TDF_OK;
 }
 
@@ -1218,8 +1256,10 @@ extern "C" int32_t tdf_kv_seq_shift(tdf_context* c, int32_t seq, int32_t p0, int
     return TDF_E_INVALID;
   }
   if (cells.empty()) return TDF_OK;
-  c->book.seq_shift(seq, delta, cells);
-  if (c->dry_run) return TDF_OK;
+  if (c->dry_run) {
+    c->book.seq_shift(seq, delta, cells);
+    return TDF_OK;
+  }
   const tdf_hparams& h = c->m->hp;
   const int hd = h.head_dim, half = hd / 2;
   // angles delta * theta^(-2i/hd), as the RoPE table of a ubatch
@@ -1229,9 +1269,10 @@ extern "C" int32_t tdf_kv_seq_shift(tdf_context* c, int32_t seq, int32_t p0, int
     cs[2 * i] = std::cos(phi);
     cs[2 * i + 1] = std::sin(phi);
   }
+  CallScratch scratch(c->stream);
   void *dcells = nullptr, *dcs = nullptr;
-  TDF_HIP(hipMallocAsync(&dcells, cells.size() * 4, c->stream));
-  TDF_HIP(hipMallocAsync(&dcs, cs.size() * 8, c->stream));
+  TDF_HIP(scratch.alloc(&dcells, cells.size() * 4));
+  TDF_HIP(scratch.alloc(&dcs, cs.size() * 8));
   TDF_HIP(hipMemcpyAsync(dcells, cells.data(), cells.size() * 4, hipMemcpyHostToDevice, c->stream));
   TDF_HIP(hipMemcpyAsync(dcs, cs.data(), cs.size() * 8, hipMemcpyHostToDevice, c->stream));
   if (c->kv_dtype == TDF_Q8_0)
@@ -1240,9 +1281,9 @@ extern "C" int32_t tdf_kv_seq_shift(tdf_context* c, int32_t seq, int32_t p0, int
   else
     TDF_HIP(launch_kv_rotate(c->kv, c->kv_dtype, 2 * c->kv_layer_bytes, h.n_layer, h.n_head_kv, c->n_ctx, hd,
                              (const int32_t*)dcells, (int)cells.size(), (const double2*)dcs, c->stream));
-  TDF_HIP(hipFreeAsync(dcells, c->stream));
-  TDF_HIP(hipFreeAsync(dcs, c->stream));
   TDF_HIP(hipStreamSynchronize(c->stream));
+  // positions move only once the keys are rotated
+  c->book.seq_shift(seq, delta, cells);
   return TDF_OK;
 }
 
@@ -1345,6 +1386,11 @@ extern "C" int32_t tdf_time_op(tdf_context* c, int32_t op, int32_t n_tokens, int
     return TDF_E_DEVICE;
   }
   *avg_us = 1000.0 * ms / reps;
+  return TDF_OK;
+}
+
+extern "C" int32_t tdf_fault_alloc(int32_t n) {
+  g_fail_in = n > 0 ? n : 0;
   return TDF_OK;
 }
 
