@@ -1,13 +1,19 @@
 """GPU parity at the workloads' full sizes.
 
-The float64 oracle cannot replay an 8B/70B prompt of thousands of tokens in
-seconds, so full-depth cases restore the cache from the same synthetic
-post-RoPE K/V on both sides (through tdf_kv_import / OracleContext.kv_import,
-values drawn by tdf_synth) and compare the outputs the oracle can compute one
-by one: a matrix-core ubatch on top of the restored context and single-token
-decode steps.  The multi-sequence workload is checked in full for its
-bookkeeping (cells, positions, rows) and on a two-layer full-width model for
-its math, using the independence of sequences.  Tolerances as in
+The 8B workload's prefill runs as the benchmark runs it: a 2048-token prompt
+in ubatches of 512 through all 32 layers (last-row logits), then
+teacher-forced decode steps, against the float64 oracle over the same
+4 ubatches.  Where the oracle cannot replay a prompt of thousands of tokens
+in seconds (the multi-sequence workload's 32 prompts, contexts beyond the
+prompt), the cache is restored from the same synthetic post-RoPE K/V on both
+sides (tdf_kv_import / OracleContext.kv_import, values drawn by tdf_synth)
+and the outputs the oracle can compute one by one are compared: matrix-core
+ubatches and decode steps on top of the restored contexts.  The
+multi-sequence workload is checked in full for its bookkeeping (cells,
+positions, rows), at full depth for a lock-step step of 32 tokens over 4 of
+its sequences (the shortest, the longest and two others, restored at their
+workload lengths; sequences are independent), and on a two-layer
+full-width model with the prompts themselves.  Tolerances as in
 test_gpu_parity.
 """
 import os
@@ -23,24 +29,122 @@ from gpu_common import TOL_BF16, check_logits, check_token, device_model, log, m
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(scope="module")
+def llama8b():
+    """The 8B-class model of the workload (bf16, all 32 layers): host tensors,
+    the device model and an oracle model holding the float64 weights, shared
+    by the tests of this module."""
+    cfg = dict(tdf_synth.CONFIGS["llama8b"])
+    cfg, w = make_weights(cfg)
+    log("8b weights generated")
+    gm = device_model(cfg, w)
+    om = oracle_model(cfg, w, cache=True)
+    log("8b weights uploaded")
+    yield cfg, w, gm, om
+    gm.close()
+
+
+def test_llama8b_prefill_as_benched_full_depth(llama8b):
+    """The 8B workload's prefill as the benchmark runs it: 2048 uniform-random
+    tokens in 4 ubatches of 512 (matrix-core projections and attention)
+    through all 32 layers, logits for the last position only; then 4
+    teacher-forced decode steps on the prompt's cache."""
+    import transformer_decode_forward_amd as tdf
+    cfg, w, gm, om = llama8b
+    gc = tdf.Context(gm, n_ctx=cfg["n_ctx"], n_ubatch=cfg["n_ubatch"], kv_dtype="bf16")
+    oc = OracleContext(om, n_ctx=cfg["n_ctx"], n_ubatch=cfg["n_ubatch"], kv_dtype="bf16")
+    prompt = tdf_synth.prompt(cfg, 0, cfg["prompt_len"])
+    assert gc.decode(prompt) == 0, tdf.tdf_last_error()
+    ro = oc.decode(prompt)
+    log("8b prefill (4 x 512) done on both sides")
+    assert [len(u) for u in ro.ubatches] == [512] * 4
+    assert gc.last_slots() == ro.slots == list(range(2048))
+    assert gc.output_ids() == ro.out_index == [2047]
+    errs = [check_logits(gc.logits_ith(2047), ro.logits[0], TOL_BF16, "8b prefill")]
+    check_token(gc.argmax_ith(2047), ro.logits[0], "8b prefill")
+    nxt = int(ro.tokens[0])
+    for step in range(4):
+        assert gc.decode([nxt]) == 0
+        ro = oc.decode([nxt])
+        assert gc.last_slots() == ro.slots and gc.seq_pos_max(0) == oc.seq_pos_max(0) == 2048 + step
+        errs.append(check_logits(gc.logits_ith(0), ro.logits[0], TOL_BF16, f"8b step {step}"))
+        check_token(gc.argmax_ith(0), ro.logits[0], f"8b step {step}")
+        nxt = int(ro.tokens[0])
+    log(f"8b prefill as benched: prefill max-abs {errs[0][0]:.2e} rel-L2 {errs[0][1]:.2e}; "
+        f"steps worst max-abs {max(e[0] for e in errs[1:]):.2e} rel-L2 {max(e[1] for e in errs[1:]):.2e}")
+    gc.close()
+
+
+def test_multisequence_lockstep_full_depth(llama8b):
+    """The multi-sequence workload at full depth over 4 of its 32 sequences
+    (the shortest, the longest and two others), each restored at its
+    workload length from its own synthetic K/V; then one lock-step step of
+    32 tokens (8 per sequence at consecutive positions: the 9..32-token
+    matrix-core path) and one of 4 tokens (one per sequence: the GEMV path),
+    every row's logits."""
+    import transformer_decode_forward_amd as tdf
+    from transformer_decode_forward_amd.device import to_device
+    cfg, w, gm, om = llama8b
+    mcfg = tdf_synth.CONFIGS["llama8b_multiseq"]
+    lens = tdf_synth.seq_lengths(mcfg)
+    order = np.argsort(lens)
+    picks = [int(order[0]), int(order[len(order) // 3]), int(order[2 * len(order) // 3]), int(order[-1])]
+    n_ctx = int(sum(lens[p] for p in picks)) + 64
+    L = cfg["n_layer"]
+    gc = tdf.Context(gm, n_ctx=n_ctx, n_batch=512, n_ubatch=512, n_seq_max=4, kv_dtype="bf16")
+    oc = OracleContext(om, n_ctx=n_ctx, n_batch=512, n_ubatch=512, n_seq_max=4, kv_dtype="bf16")
+    base = 0
+    for j, s in enumerate(picks):
+        n = int(lens[s])
+        # sequence j's rows come from its own stretch of the fill streams
+        ks = [tdf_synth.kv_fill(cfg, l, "k", base, base + n, "bf16") for l in range(L)]
+        vs = [tdf_synth.kv_fill(cfg, l, "v", base, base + n, "bf16") for l in range(L)]
+        kd, vd = [to_device(k) for k in ks], [to_device(v) for v in vs]
+        assert gc.kv_import(j, 0, n, [t.data_ptr() for t in kd], [t.data_ptr() for t in vd]) == 0
+        assert oc.kv_import(j, 0, n, ks, vs) == 0
+        assert gc.last_slots() == list(oc.last_import_cells)
+        del kd, vd, ks, vs
+        base += n
+    log(f"4 sequences restored: lengths {[int(lens[p]) for p in picks]}")
+    calls = [dict(tokens=tdf_synth.prompt(mcfg, 400, 32), seq_ids=[[j // 8] for j in range(32)],
+                  logits=np.ones(32, np.int8)),
+             dict(tokens=tdf_synth.prompt(mcfg, 401, 4), seq_ids=[[0], [1], [2], [3]],
+                  logits=np.ones(4, np.int8))]
+    errs = []
+    for k, call in enumerate(calls):
+        assert gc.decode(**call) == 0, tdf.tdf_last_error()
+        r = oc.decode(**call)
+        assert gc.last_slots() == r.slots and gc.output_ids() == r.out_index
+        for row, i in enumerate(r.out_index):
+            errs.append(check_logits(gc.logits_ith(i), r.logits[row], TOL_BF16, f"lock-step call {k} row {i}"))
+            check_token(gc.argmax_ith(i), r.logits[row], f"lock-step call {k} row {i}")
+        log(f"lock-step call {k} ({len(call['tokens'])} tokens) done")
+    for j, s in enumerate(picks):
+        assert gc.seq_pos_max(j) == oc.seq_pos_max(j) == int(lens[s]) + 8
+    log(f"multi-sequence full depth: worst max-abs {max(e[0] for e in errs):.2e}, "
+        f"rel-L2 {max(e[1] for e in errs):.2e}")
+    gc.close()
+
+
 def _fill(cfg, P):
     L = cfg["n_layer"]
     return ([tdf_synth.kv_fill(cfg, l, "k", 0, P, "bf16") for l in range(L)],
             [tdf_synth.kv_fill(cfg, l, "v", 0, P, "bf16") for l in range(L)])
 
 
-def _restored_pair(cfg, w, P, n_ctx, cache):
-    """GPU and oracle contexts with positions [0, P) of sequence 0 restored."""
+def _restored_pair(cfg, w, P, n_ctx, cache, gm=None, om=None):
+    """GPU and oracle contexts with positions [0, P) of sequence 0 restored
+    (the device and oracle models are made here unless given)."""
     import transformer_decode_forward_amd as tdf
     from transformer_decode_forward_amd.device import to_device
     ks, vs = _fill(cfg, P)
-    gm = device_model(cfg, w)
+    gm = gm if gm is not None else device_model(cfg, w)
     gc = tdf.Context(gm, n_ctx=n_ctx, n_ubatch=512, kv_dtype="bf16")
     kd = [to_device(k) for k in ks]
     vd = [to_device(v) for v in vs]
     assert gc.kv_import(0, 0, P, [t.data_ptr() for t in kd], [t.data_ptr() for t in vd]) == 0
     del kd, vd
-    oc = OracleContext(oracle_model(cfg, w, cache=cache), n_ctx=n_ctx, kv_dtype="bf16")
+    oc = OracleContext(om if om is not None else oracle_model(cfg, w, cache=cache), n_ctx=n_ctx, kv_dtype="bf16")
     assert oc.kv_import(0, 0, P, ks, vs) == 0
     assert gc.last_slots() == list(oc.last_import_cells)
     return gm, gc, oc
@@ -77,14 +181,18 @@ def test_llama1b_full_workload_shape(kv_dtype):
 
 
 @pytest.mark.parametrize("weight_dtype", ["bf16", "q8_0"])
-def test_llama8b_full_depth(weight_dtype):
+def test_llama8b_full_depth(weight_dtype, llama8b):
     """8B-class model, all 32 layers (bf16 or Q8_0 weights): context 2048
     restored, then a 64-token ubatch (matrix-core path; logits for 3 rows) and
     2 decode steps."""
-    cfg = dict(tdf_synth.CONFIGS["llama8b"], weight_dtype=weight_dtype)
-    cfg, w = make_weights(cfg)
-    log(f"8b {weight_dtype} weights generated")
-    gm, gc, oc = _restored_pair(cfg, w, 2048, 4096, cache=False)
+    if weight_dtype == "bf16":
+        cfg, w, gm, om = llama8b
+        gm, gc, oc = _restored_pair(cfg, w, 2048, 4096, cache=False, gm=gm, om=om)
+    else:
+        cfg = dict(tdf_synth.CONFIGS["llama8b"], weight_dtype=weight_dtype)
+        cfg, w = make_weights(cfg)
+        log(f"8b {weight_dtype} weights generated")
+        gm, gc, oc = _restored_pair(cfg, w, 2048, 4096, cache=False)
     toks = tdf_synth.prompt(cfg, 3, 64)
     flags = np.zeros(64, dtype=np.int8)
     flags[[0, 31, 63]] = 1
