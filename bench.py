@@ -192,10 +192,24 @@ def cpu_baseline(cfg, host_weights, ctx_len):
     r = oc.decode([tok])
     dt = time.perf_counter() - t0
     assert r.status == 0 and r.logits.shape == (1, cfg["n_vocab"])
+    # prefill: one ubatch of the prompt through the first layers only (the
+    # whole prompt would take minutes), rate scaled to the full depth
+    Lp, U = 2, cfg["n_ubatch"]
+    pm = OracleModel(dict(tdf_synth.hparams(cfg), n_layer=Lp), host_weights, cache=False)
+    pc = OracleContext(pm, n_ctx=U, n_ubatch=U)
+    t0 = time.perf_counter()
+    r = pc.decode(tdf_synth.prompt(cfg, 0, U))
+    dtp = time.perf_counter() - t0
+    assert r.status == 0
+    pre_tps = U / (dtp * L / Lp)
     return {"value": 1.0 / dt, "unit": "decode tok/s", "cores": threads or os.cpu_count(),
             "kind": "oracle",
             "sample": f"1 decode step of the {L}-layer model at context {ctx_len} (cache restored "
-                      f"from synthetic K/V), float64 numpy, {dt:.1f} s"}
+                      f"from synthetic K/V), float64 numpy, {dt:.1f} s",
+            "prefill": {"value": pre_tps, "unit": "prefill tok/s",
+                        "sample": f"one {U}-token ubatch (positions 0..{U - 1}) through the first {Lp} of the "
+                                  f"{L} layers plus the LM head row, {dtp:.1f} s, rate scaled by {L}/{Lp} "
+                                  f"(the LM head is counted {L // Lp} times: an upper bound on the time)"}}
 
 
 def decode_bytes_multi(cfg, ctxs):
@@ -210,16 +224,20 @@ def decode_bytes_multi(cfg, ctxs):
             + 4 * V * len(ctxs))
 
 
-def run_multiseq(args, cfg):
+def run_multiseq(args, cfg, model=None, steps=None, warmup=None):
     """32 sequences sharing one cache: prompts of 1024..8192 tokens prefilled
     one call per sequence, then lock-step decode steps of 32 tokens (one per
-    sequence, its own position and id), logits for all 32 rows."""
+    sequence, its own position and id), logits for all 32 rows.  ``model``:
+    an uploaded model of the same shape to reuse (else one is made)."""
     import torch
     import tdf_synth
     import transformer_decode_forward_amd as tdf
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     S, lens = cfg["n_seqs"], tdf_synth.seq_lengths(cfg)
-    log(f"generating and uploading weights; {S} sequences, {int(lens.sum())} prompt tokens")
-    model, _ = build_model(cfg, keep_host=False)
+    if model is None:
+        log(f"generating and uploading weights; {S} sequences, {int(lens.sum())} prompt tokens")
+        model, _ = build_model(cfg, keep_host=False)
     ctx = tdf.Context(model, n_ctx=cfg["n_ctx"], n_batch=8192, n_ubatch=cfg["n_ubatch"], n_seq_max=S,
                       kv_dtype=cfg["kv_dtype"])
     torch.cuda.synchronize()
@@ -231,28 +249,28 @@ def run_multiseq(args, cfg):
     seq_ids = [[s] for s in range(S)]
     flags = np.ones(S, dtype=np.int8)
     toks = [ctx.argmax_ith(int(lens[S - 1]) - 1)] * S
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         assert ctx.decode(toks, seq_ids=seq_ids, logits=flags) == 0, tdf.tdf_last_error()
         toks = [ctx.argmax_ith(i) for i in range(S)]
-    ctx0 = [int(lens[s]) + args.warmup for s in range(S)]
+    ctx0 = [int(lens[s]) + warmup for s in range(S)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         assert ctx.decode(toks, seq_ids=seq_ids, logits=flags) == 0, tdf.tdf_last_error()
         toks = [ctx.argmax_ith(i) for i in range(S)]
     torch.cuda.synchronize()
     t_dec = time.perf_counter() - t0
     ctx.close()
-    mean = [c + (args.steps - 1) / 2.0 for c in ctx0]
+    mean = [c + (steps - 1) / 2.0 for c in ctx0]
     step_bytes = decode_bytes_multi(cfg, mean)
-    ms = 1000.0 * t_dec / args.steps
-    tps = S * args.steps / t_dec
+    ms = 1000.0 * t_dec / steps
+    tps = S * steps / t_dec
     log(f"prefill {lens.sum() / t_pre:.0f} tok/s, decode {tps:.1f} tok/s ({ms:.3f} ms per 32-token step)")
     return {
         "metric": ("decode tok/s (% HBM peak), 8B-shape bf16, 32 sequences" if cfg["weight_dtype"] == "bf16" else
                    f"decode tok/s (% HBM peak), 8B-shape {cfg['weight_dtype'].upper()} weights, 32 sequences")
                   + ("" if cfg["kv_dtype"] == "bf16" else f", {cfg['kv_dtype'].upper()} cache"),
-        "value": round(tps, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "value": round(tps, 2), "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if cfg["weight_dtype"] == "bf16" else f"f32 ({cfg['weight_dtype']} weights)",
         "data": "synthetic",
@@ -343,6 +361,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--config", default="llama8b")
     ap.add_argument("--no-peaks", action="store_true")
+    ap.add_argument("--no-multiseq", action="store_true",
+                    help="skip the 32-sequence section of the default (8B) run")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--weights", choices=["bf16", "q8_0"], default=None,
                     help="weight storage of the single-sequence workload (default: the config's, bf16)")
@@ -487,6 +507,15 @@ def main():
                          for k, v in sorted(pr.items())}
                  for phase, pr in prof_phase.items()}
 
+    # the multi-sequence workload on the same weights: 32 sequences' prompts,
+    # then a few lock-step steps of 32 tokens
+    multi = None
+    if args.config == "llama8b" and not args.no_multiseq and not args.swa:
+        mcfg = dict(tdf_synth.CONFIGS["llama8b_multiseq"], weight_dtype=cfg["weight_dtype"],
+                    kv_dtype=cfg["kv_dtype"])
+        log("multi-sequence section (32 sequences)")
+        multi = run_multiseq(args, mcfg, model=model, steps=8, warmup=2)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -523,10 +552,13 @@ def main():
                     "algorithmic_tflop": round(pre_flops / 1e12, 4),
                     "achieved_TFLOPs": round(pre_flops / t_pre / 1e12, 2),
                     "frac_mfma_peak": round(pre_flops / t_pre / 1e12 / MFMA_BF16_PEAK_TFS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "gate/up GEMV + SwiGLU (decode)",
+        # the dominant decode kernel; the whole step's fraction (every kernel
+        # of the step, launch gaps included) is step_frac_hbm_peak
+        "roofline": {"bound": "hbm", "kernel": "gate/up GEMV + SwiGLU (decode), dominant kernel only",
                      "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": traffic("decode_q8_0" if q8 else "decode") if is8b else None,
-                     "avg_launch_us": round(gu_us, 2), "bytes_per_launch": gu_bytes},
+                     "avg_launch_us": round(gu_us, 2), "bytes_per_launch": gu_bytes,
+                     "step_frac_hbm_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline_prefill": {"bound": "mfma", "kernel": "gate/up GEMM + SwiGLU (prefill ubatch 512)",
                              "achieved": round(gg_tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                              "frac": round(gg_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic("prefill_q8_0" if q8 else "prefill") if is8b else None,
@@ -538,6 +570,8 @@ def main():
         "kernels": breakdown,
         "cpu_baseline": cpu,
     }
+    if multi is not None:
+        out["multiseq"] = {k: multi[k] for k in ("config", "decode", "prefill", "steps", "warmup", "ms_per_step")}
     print(json.dumps(out), flush=True)
 
 
