@@ -272,6 +272,25 @@ int32_t tdf_sample(tdf_context *c, const tdf_sampling *p, const float *u, int32_
 int32_t tdf_sample_logits(tdf_context *c, const float *logits, int32_t n_rows, int32_t n_vocab,
                           const tdf_sampling *p, const float *u, int32_t *tokens);
 
+/* Allocation-free variant of tdf_sample_logits, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc.  It makes no allocation of any kind.
+ * logits: DEVICE [n_rows][n_vocab] float32 (read only); u: DEVICE array of
+ * n_rows uniform numbers (read only; needed when temperature > 0; values
+ * are not checked on the host: u >= 1 picks the last survivor); tokens:
+ * DEVICE array of n_rows entries, written by the kernels.  The work is
+ * enqueued on stream (a hipStream_t; NULL: the null stream) and the call
+ * returns without waiting for it.  Greedy (temperature <= 0) keeps its
+ * per-row partial maxima in a static device array of 1 MiB per GPU (shared
+ * by every call on that GPU, held until the process ends, fully overwritten
+ * by each call; calls that overlap on one GPU race on it); rows x partials
+ * beyond that size (more than 2080 rows of 128256 logits) are rejected with
+ * TDF_E_INVALID before anything is enqueued.  The sampling chain needs no
+ * scratch.  Returns TDF_OK, TDF_E_INVALID or TDF_E_DEVICE (launch failure,
+ * message in tdf_last_error). */
+int32_t tdf_sample_logits_static(const float *logits, int32_t n_rows, int32_t n_vocab,
+                                 const tdf_sampling *p, const float *u, int32_t *tokens, void *stream);
+
 /* Sliding the context window (Ollama engine page, "KV Cache: memory for
  * causal attention": when the cache is full, the model's shift function
  * re-encodes the RoPE positions of the cached keys and the window moves

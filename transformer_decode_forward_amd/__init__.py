@@ -97,6 +97,8 @@ def lib():
                                          ctypes.POINTER(_f32), ctypes.POINTER(_i32)]),
             "tdf_kv_seq_shift": (_i32, [_vp, _i32, _i32, _i32, _i32]),
             "tdf_fault_alloc": (_i32, [_i32]),
+            "tdf_sample_logits_static": (_i32, [ctypes.c_void_p, _i32, _i32, ctypes.POINTER(tdf_sampling),
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
             "tdf_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -142,6 +144,14 @@ def tdf_last_error() -> str:
 
 def tdf_fault_alloc(n: int) -> int:
     return lib().tdf_fault_alloc(n)
+
+
+def tdf_sample_logits_static(logits_ptr: int, n_rows: int, n_vocab: int, p: tdf_sampling, u_ptr: int,
+                             tokens_ptr: int, stream: int = 0) -> int:
+    """Device addresses in, device tokens out, enqueued on ``stream``."""
+    return lib().tdf_sample_logits_static(ctypes.c_void_p(logits_ptr), n_rows, n_vocab, ctypes.byref(p),
+                                          ctypes.c_void_p(u_ptr or None), ctypes.c_void_p(tokens_ptr),
+                                          ctypes.c_void_p(stream or None))
 
 
 # ---- convenience objects ---------------------------------------------------

@@ -17,6 +17,7 @@
 #include <algorithm>
 #include <cmath>
 #include <map>
+#include <mutex>
 #include <tuple>
 #include <cstdio>
 #include <cstdlib>
@@ -1216,6 +1217,84 @@ extern "C" int32_t tdf_sample_logits(tdf_context* c, const float* logits, int32_
   }
   return sample_rows(c, logits, n_rows, n_vocab, p, u, tokens, c->ext_u, c->ext_tok, c->ext_pv, c->ext_pi,
                      c->ext_htok);
+}
+
+// ---------------------------------------------------------------------------
+// allocation-free sampling: the argmax partials live in a static device array
+// (one copy per GPU, kept until the process ends) instead of memory the
+// library allocates
+
+namespace {
+constexpr size_t kStaticScratchBytes = 1u << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+// Device address of this GPU's `scratch` (looked up once per device with
+// that device current; the array's name is only a host-side stand-in).
+static int static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    set_err(std::string("tdf_sample_logits_static: no usable current device: ") + hipGetErrorString(e));
+    return TDF_E_DEVICE;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      set_err(std::string("tdf_sample_logits_static: scratch lookup failed: ") + hipGetErrorString(e));
+      return TDF_E_DEVICE;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TDF_OK;
+}
+
+extern "C" int32_t tdf_sample_logits_static(const float* logits, int32_t n_rows, int32_t n_vocab,
+                                            const tdf_sampling* p, const float* u, int32_t* tokens,
+                                            void* stream) {
+  g_err.clear();
+  if (!logits || !p || !tokens || n_rows < 0 || n_vocab < 1) {
+    set_err("tdf_sample_logits_static: invalid arguments");
+    return TDF_E_INVALID;
+  }
+  if (n_rows == 0) return TDF_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (p->temperature > 0.f) {
+    // the chain needs no scratch: one block per row, its candidates in LDS
+    if (!u || p->top_k < 1 || p->top_k > kMaxTopK || !(p->min_p >= 0.f && p->min_p <= 1.f) ||
+        !(p->top_p == p->top_p) || !std::isfinite(p->temperature)) {
+      set_err("tdf_sample_logits_static: invalid sampling parameters");
+      return TDF_E_INVALID;
+    }
+    SampleParams sp;
+    sp.temperature = p->temperature;
+    sp.top_k = p->top_k;
+    sp.top_p = p->top_p;
+    sp.min_p = p->min_p;
+    TDF_HIP(launch_sample(logits, n_rows, n_vocab, sp, u, tokens, s));
+    return TDF_OK;
+  }
+  // greedy: per row argmax_splits(n_vocab) partial (value, index) pairs
+  const size_t n_part = (size_t)n_rows * argmax_splits(n_vocab);
+  const size_t v_bytes = (n_part * sizeof(float) + 255) & ~(size_t)255;
+  if (v_bytes + n_part * sizeof(int32_t) > kStaticScratchBytes) {
+    set_err("tdf_sample_logits_static: " + std::to_string(n_rows) + " rows of " + std::to_string(n_vocab) +
+            " logits need more than the " + std::to_string(kStaticScratchBytes) + "-byte static scratch");
+    return TDF_E_INVALID;
+  }
+  void* ptr = nullptr;
+  if (int rc = static_scratch(&ptr)) return rc;
+  float* pv = (float*)ptr;
+  int32_t* pi = (int32_t*)((char*)ptr + v_bytes);
+  TDF_HIP(launch_argmax(logits, n_rows, n_vocab, tokens, pv, pi, s));
+  return TDF_OK;
 }
 
 extern "C" int32_t tdf_kv_seq_rm(tdf_context* c, int32_t seq, int32_t p0, int32_t p1) {
