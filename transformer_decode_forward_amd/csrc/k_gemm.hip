@@ -358,10 +358,17 @@ static hipError_t gemm_launch_tile(const LinearArgs& a, int ksplit, hipStream_t 
 
 // Tile choice.  Plain epilogues: the largest of 128x256, 128x128, 64x128
 // that gives at least 384 blocks (1.5 per CU).  Residual epilogue: the
-// smallest K split (1, 2, 4, 8) for which some tile reaches 512 blocks, with
-// the largest such tile; the atomic adds of deeper splits cost more than the
-// smaller tiles' extra operand traffic (at 512 x 4096 x 4096, 64x128 tiles
-// split in 2 run in about half the time of 128x256 tiles split in 8).
+// largest tile that reaches 512 blocks with a K split (2, 4) that still
+// leaves each split at least 48 K tiles; failing that, the smallest K split
+// (1, 2, 4, 8) for which some tile reaches 512 blocks, with the largest such
+// tile.  The atomic adds of a split cost less than small tiles' extra
+// operand traffic only when the split is deep in K: measured at M = 512,
+// K = 14336 (8B down) 128x128 tiles split in 4 take 137.5 us against 146 us
+// for 64x128 split in 2; K = 28672 (70B down) 128x256 split in 4 take 441 us
+// against 567 us for 64x128 unsplit; K = 8192 (70B output projection)
+// 128x128 split in 2 take 156 us against 175 us; at K = 4096 (8B output
+// projection) 64x128 tiles split in 2 stay best (51 us; 128x256 split in 8:
+// 93 us).
 template <int EPI, typename KvT>
 static hipError_t gemm_launch_t(const LinearArgs& a, hipStream_t s) {
   const int M = a.T;
@@ -374,6 +381,14 @@ static hipError_t gemm_launch_t(const LinearArgs& a, hipStream_t s) {
   const int b22 = q8 ? 0 : ((M + 127) / 128) * ((Ntot + 127) / 128);
   const int b12 = ((M + 63) / 64) * ((Ntot + 127) / 128);
   if (EPI == EPI_RESIDUAL) {
+    for (int ks = 2; ks <= 4; ks *= 2) {
+      if (nkt % ks != 0 || nkt / ks < 48) break;
+      if (b24 * ks >= 512) return gemm_launch_tile<EPI, KvT, 2, 4>(a, ks, s);
+    }
+    for (int ks = 2; ks <= 4; ks *= 2) {
+      if (nkt % ks != 0 || nkt / ks < 48) break;
+      if (b22 * ks >= 512) return gemm_launch_tile<EPI, KvT, 2, 2>(a, ks, s);
+    }
     for (int ks = 1; ks <= 8; ks *= 2) {
       // each split keeps at least 4 K tiles
       if (ks > 1 && (nkt % ks != 0 || nkt / ks < 4)) break;
