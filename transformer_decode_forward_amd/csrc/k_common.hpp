@@ -128,4 +128,12 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// Q8_0 block rule, in float32: the scale is fp16(max|x| / 127); a code is
+// x / d rounded half-even and clamped to [-127, 127], or 0 when d is 0
+__device__ __forceinline__ uint16_t q8_scale_bits(float amax) { return f32_to_f16(amax / 127.f); }
+__device__ __forceinline__ int8_t q8_code(float x, float d) {
+  const float r = d > 0.f ? rintf(x / d) : 0.f;
+  return (int8_t)fminf(fmaxf(r, -127.f), 127.f);
+}
+
 }  // namespace tdf

@@ -12,6 +12,7 @@
 // GEMV streams each weight row once with 16-byte loads per lane and keeps the
 // activations in float32.
 #include <algorithm>
+#include <type_traits>
 
 #include "k_common.hpp"
 #include "kernels.hpp"
@@ -429,13 +430,35 @@ __device__ __forceinline__ void kv_put(void* cache, int64_t idx, float v) {
   KvStore<KvT>::store((typename KvStore<KvT>::T*)cache, idx, v);
 }
 
+// Waves per GEMV block: 4, or 32 / R when the epilogue stores K/V rows in a
+// Q8_0 cache.  Then a block's 32 rows are exactly one 32-value block of one
+// head's K or V row, so the block decides its scale and codes itself.
+template <typename KvT, int R> struct GemvWaves { static constexpr int n = 4; };
+template <int R> struct GemvWaves<kv_q8, R> { static constexpr int n = 32 / R; };
+
+// sum of r[0..BW)[t] as a pairwise tree ((r0 + r1) + (r2 + r3)) ...
+template <int BW, int NT>
+__device__ __forceinline__ float block_tree_sum(const float (&r)[BW][NT], int t) {
+  float v[BW];
+#pragma unroll
+  for (int i = 0; i < BW; ++i) v[i] = r[i][t];
+#pragma unroll
+  for (int w = BW / 2; w >= 1; w /= 2)
+#pragma unroll
+    for (int i = 0; i < w; ++i) v[i] = v[2 * i] + v[2 * i + 1];
+  return v[0];
+}
+
 template <int WT, int NT, int EPI, typename KvT, bool NORM, int U, int R>
-__global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt) {
+__global__ void __launch_bounds__((64 * GemvWaves<KvT, R>::n)) gemv_kernel(LinearArgs a, int t0, int nt) {
   static_assert(R == 2 || R == 4, "rows per wave");
+  constexpr int BW = GemvWaves<KvT, R>::n, BT = 64 * BW;  // waves and threads per block
+  constexpr bool KVQ8 = std::is_same<KvT, kv_q8>::value;
+  static_assert(!KVQ8 || (EPI == EPI_QKV && NT == 1), "Q8_0 cache rows: single-token QKV");
   constexpr int P = R / 2;  // output pairs per wave
-  __shared__ float red[4][NT];
+  __shared__ float red[BW][NT];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wave = blockIdx.x * 4 + wid;
+  const int wave = blockIdx.x * BW + wid;
   const int N = a.n0 + a.n1 + a.n2;
   const int K = a.K;
   // The R rows of this wave.  Rows past the end are clamped to the last row
@@ -482,13 +505,13 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
   const bool active = rv[0];
   const float* act = a.act_f32 + (int64_t)t0 * K;
 
-  // RMSNorm consumer: the block's 256 threads fetch the producer's partial
+  // RMSNorm consumer: the block's threads fetch the producer's partial
   // sums of x^2 together with the first batch of weights (same memory round
   // trip) and add them up once per block after the row loop.  The loads use
   // clamped indices and are masked by a multiply: a load under a divergent
   // branch (or a select of a load, which becomes one) makes the compiler wait
   // for every load in flight.
-  constexpr int kNormPer = 4;  // partials per thread fetched with the weights (1024 per block)
+  constexpr int kNormPer = 4;  // partials per thread fetched with the weights (4 * BT per block)
   float nss[NORM ? NT : 1][kNormPer];
 #pragma unroll
   for (int t = 0; t < (NORM ? NT : 1); ++t)
@@ -499,7 +522,7 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int q = 0; q < kNormPer; ++q) {
-        const int pidx = threadIdx.x + q * 256;
+        const int pidx = threadIdx.x + q * BT;
         const int tc = t < nt ? t : nt - 1;
         const float v = a.norm_ssp[(int64_t)(t0 + tc) * a.norm_stride + min(pidx, a.norm_nparts - 1)];
         nss[t][q] += v * ((t < nt && pidx < a.norm_nparts) ? on : 0.f);
@@ -636,14 +659,14 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
   if (NORM) {
     // RMS scale 1/sqrt(ss/K + eps), ss = sum of the producer's partials
     if (!norm_fetched) norm_fetch(1.f);  // short or ragged rows, inactive waves
-    __shared__ float red_n[4][NT];
+    __shared__ float red_n[BW][NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       float ss = 0.f;
 #pragma unroll
       for (int q = 0; q < kNormPer; ++q) ss += nss[t][q];
       if (t < nt)
-        for (int pi = threadIdx.x + kNormPer * 256; pi < a.norm_nparts; pi += 256)
+        for (int pi = threadIdx.x + kNormPer * BT; pi < a.norm_nparts; pi += BT)
           ss += a.norm_ssp[(int64_t)(t0 + t) * a.norm_stride + pi];
       ss = wave_sum(ss);
       if (lane == 0) red_n[wid][t] = ss;
@@ -651,7 +674,7 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const float ss = (red_n[0][t] + red_n[1][t]) + (red_n[2][t] + red_n[3][t]);
+      const float ss = block_tree_sum<BW, NT>(red_n, t);
       const float r = 1.0f / sqrtf(ss / (float)K + a.norm_eps);
 #pragma unroll
       for (int i = 0; i < R; ++i) acc[i][t] *= r;
@@ -660,6 +683,8 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
   // lane t writes token t; pair j covers rows 2j and 2j+1 of the wave (r1 ==
   // r0: a single row at the end of the matrix stack)
   const bool produce = EPI == EPI_RESIDUAL && a.next_g != nullptr;
+  // Q8_0 cache: the block's 32 K or V values (row r at [r % 32])
+  __shared__ float kvq[KVQ8 ? 32 : 1];
   float sq[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -704,11 +729,17 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
           if (r0 < a.n0) {
             a.q_out[(int64_t)tg * a.n0 + lr] = z0;
             a.q_out[(int64_t)tg * a.n0 + lr + 1] = z1;
+          } else if constexpr (KVQ8) {
+            kvq[r0 & 31] = z0;
+            kvq[(r0 & 31) + 1] = z1;
           } else {
             const int64_t ci = ((int64_t)(lr / hd) * a.n_ctx + a.slots[tg]) * hd + (lr % hd);
             kv_put<KvT>(a.k_cache, ci, z0);
             kv_put<KvT>(a.k_cache, ci + 1, z1);
           }
+        } else if constexpr (KVQ8) {
+          kvq[r0 & 31] = y0;
+          kvq[(r0 & 31) + 1] = y1;
         } else {
           const int lr = r0 - a.n0 - a.n1;
           const int64_t ci = ((int64_t)(lr / hd) * a.n_ctx + a.slots[tg]) * hd + (lr % hd);
@@ -726,9 +757,36 @@ __global__ void __launch_bounds__(256) gemv_kernel(LinearArgs a, int t0, int nt)
       if (lane == 0) red[wid][t] = v;
     }
     __syncthreads();
-    if (threadIdx.x < nt)
-      a.next_ssp[(int64_t)(t0 + threadIdx.x) * a.next_stride + blockIdx.x] =
-          red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] + red[3][threadIdx.x];
+    if (threadIdx.x < nt) {
+      float v = red[0][threadIdx.x];
+#pragma unroll
+      for (int w = 1; w < BW; ++w) v += red[w][threadIdx.x];
+      a.next_ssp[(int64_t)(t0 + threadIdx.x) * a.next_stride + blockIdx.x] = v;
+    }
+  }
+  if constexpr (KVQ8) {
+    // A K or V block (rows n0 .. N; the row counts and head_dim are multiples
+    // of 32, checked by the launcher): wave 0 quantizes the 32 values into
+    // their cell, one code per lane, with the rule of kv_quantize.
+    const int rb = blockIdx.x * 32;
+    if (rb >= a.n0 && rb < N) {
+      __syncthreads();
+      if (wid == 0) {
+        const bool is_v = rb >= a.n0 + a.n1;
+        const int lr = rb - a.n0 - (is_v ? a.n1 : 0);
+        const int hd = a.head_dim, Hkv = a.n1 / hd;
+        const float x = lane < 32 ? kvq[lane] : 0.f;
+        const uint16_t dbits = q8_scale_bits(wave_max(fabsf(x)));
+        const float d = f16_to_f32(dbits);
+        const int64_t crow = (int64_t)(lr / hd) * a.n_ctx + a.slots[t0];
+        int8_t* codes = (int8_t*)(is_v ? a.v_cache : a.k_cache);
+        if (lane < 32) codes[crow * hd + (lr % hd) + lane] = q8_code(x, d);
+        if (lane == 0) {
+          uint16_t* scales = (uint16_t*)(codes + (int64_t)Hkv * a.n_ctx * hd);
+          scales[crow * (hd / 32) + (lr % hd) / 32] = dbits;
+        }
+      }
+    }
   }
 }
 
@@ -740,8 +798,9 @@ template <int WT, int NT, int EPI, typename KvT, int R>
 static hipError_t gemv_launch_r(const LinearArgs& a, hipStream_t s) {
   const int N = a.n0 + a.n1 + a.n2;
   constexpr int P = R / 2;
+  constexpr int BW = GemvWaves<KvT, R>::n;
   const int waves = EPI == EPI_SWIGLU ? (a.n0 + P - 1) / P : (N + R - 1) / R;
-  const int blocks = (waves + 3) / 4;
+  const int blocks = (waves + BW - 1) / BW;
   // chunks per batch at two rows per wave: 8 for a single token on grids of
   // at least 8192 rows (the large matrices), else 4 (2 for float32 weights);
   // a Q8_0 chunk holds twice the elements of a bf16 one, so half as many per
@@ -755,16 +814,27 @@ static hipError_t gemv_launch_r(const LinearArgs& a, hipStream_t s) {
   for (int t0 = 0; t0 < a.T; t0 += NT) {
     const int nt = a.T - t0 < NT ? a.T - t0 : NT;
     if (a.norm_ssp) {
-      if (big) gemv_kernel<WT, NT, EPI, KvT, true, U_BIG, R><<<blocks, 256, 0, s>>>(a, t0, nt);
-      else gemv_kernel<WT, NT, EPI, KvT, true, U_MANY, R><<<blocks, 256, 0, s>>>(a, t0, nt);
+      if (big) gemv_kernel<WT, NT, EPI, KvT, true, U_BIG, R><<<blocks, 64 * BW, 0, s>>>(a, t0, nt);
+      else gemv_kernel<WT, NT, EPI, KvT, true, U_MANY, R><<<blocks, 64 * BW, 0, s>>>(a, t0, nt);
     } else {
-      if (big) gemv_kernel<WT, NT, EPI, KvT, false, U_BIG, R><<<blocks, 256, 0, s>>>(a, t0, nt);
-      else gemv_kernel<WT, NT, EPI, KvT, false, U_MANY, R><<<blocks, 256, 0, s>>>(a, t0, nt);
+      if (big) gemv_kernel<WT, NT, EPI, KvT, false, U_BIG, R><<<blocks, 64 * BW, 0, s>>>(a, t0, nt);
+      else gemv_kernel<WT, NT, EPI, KvT, false, U_MANY, R><<<blocks, 64 * BW, 0, s>>>(a, t0, nt);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// Single-token QKV into a Q8_0 cache: one block per 32 rows (every row count
+// is a multiple of 32), R rows per wave, U chunks per batch.
+template <int WT, int R, int U>
+static hipError_t gemv_launch_kvq8(const LinearArgs& a, hipStream_t s) {
+  constexpr int BT = 64 * GemvWaves<kv_q8, R>::n;
+  const int blocks = (a.n0 + a.n1 + a.n2) / 32;
+  if (a.norm_ssp) gemv_kernel<WT, 1, EPI_QKV, kv_q8, true, U, R><<<blocks, BT, 0, s>>>(a, 0, 1);
+  else gemv_kernel<WT, 1, EPI_QKV, kv_q8, false, U, R><<<blocks, BT, 0, s>>>(a, 0, 1);
+  return hipGetLastError();
 }
 
 // rows per wave: 4 for the single-token Q8_0 GEMV of matrices with at least
@@ -786,6 +856,15 @@ static hipError_t gemv_dispatch_epi(const LinearArgs& a, hipStream_t s) {
     case EPI_RESIDUAL: return gemv_launch_t<WT, NT, EPI_RESIDUAL, float>(a, s);
     case EPI_SWIGLU: return gemv_launch_t<WT, NT, EPI_SWIGLU, float>(a, s);
     case EPI_QKV:
+      if (a.kv_dtype == TDF_Q8_0) {
+        // single token only; whole 32-value blocks of K/V rows per GEMV block
+        if constexpr (NT == 1) {
+          if (a.T != 1 || a.head_dim % 32 || a.n0 % 32 || a.n1 % 32 || a.n2 % 32 || a.n1 != a.n2)
+            return hipErrorInvalidValue;
+          return gemv_launch_kvq8<WT, 2, WT == W_Q8 ? 2 : 4>(a, s);
+        }
+        return hipErrorInvalidValue;
+      }
       if (a.kv_dtype == TDF_BF16) return gemv_launch_t<WT, NT, EPI_QKV, kv_bf16>(a, s);
       if (a.kv_dtype == TDF_F16) return gemv_launch_t<WT, NT, EPI_QKV, kv_f16>(a, s);
       return gemv_launch_t<WT, NT, EPI_QKV, float>(a, s);

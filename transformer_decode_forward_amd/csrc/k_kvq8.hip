@@ -8,8 +8,9 @@
 // Layout of one layer's K (or V) array: the codes [Hkv][n_ctx][hd] int8, then
 // the scales [Hkv][n_ctx][hd / 32] fp16.
 //
-// The projections write float32 K/V rows into a staging area; kv_quantize
-// then stores each 32-element block of a row in its cell.  The cache shift
+// A single-token projection quantizes its K/V blocks in its own epilogue
+// (the decode GEMV); the others write float32 K/V rows into a staging area,
+// and kv_quantize then stores each 32-element block of a row in its cell.  The cache shift
 // rotates the stored keys in double and re-quantizes them.
 #include "k_common.hpp"
 #include "kernels.hpp"
@@ -22,13 +23,10 @@ __device__ __forceinline__ void q8_block(const float* x, int8_t* q, uint16_t& db
   float amax = 0.f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
-  dbits = f32_to_f16(amax / 127.f);
+  dbits = q8_scale_bits(amax);
   const float d = f16_to_f32(dbits);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float r = d > 0.f ? rintf(x[i] / d) : 0.f;
-    q[i] = (int8_t)fminf(fmaxf(r, -127.f), 127.f);
-  }
+  for (int i = 0; i < 32; ++i) q[i] = q8_code(x[i], d);
 }
 
 // src row (t, h) at src + t * ts + h * hs (float32, hd values); destination
