@@ -46,6 +46,9 @@ KERNEL_SOURCES = {"decode": "transformer_decode_forward_amd/csrc/k_decode.hip",
                   "prefill": "transformer_decode_forward_amd/csrc/k_gemm.hip",
                   "decode_q8_0": "transformer_decode_forward_amd/csrc/k_decode.hip",
                   "prefill_q8_0": "transformer_decode_forward_amd/csrc/k_gemm.hip"}
+# rocprofv3 matrix-core counters of the prefill kernels (GEMMs and attention)
+MFMA_FILES = {"prefill": "profiles/llama8b_prefill_mfma.json",
+              "prefill_q8_0": "profiles/llama8b_q8_0_prefill_mfma.json"}
 
 
 def log(msg):
@@ -123,6 +126,20 @@ def traffic(kind):
     if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kind]):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def mfma_busy(kind):
+    """MFMA-busy fraction of each prefill kernel (SQ_VALU_MFMA_BUSY_CYCLES over
+    the SIMDs' active cycles) from the committed counter summary, or None when
+    a kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, MFMA_FILES[kind])
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if any(h != source_hash(src) for src, h in rec.get("sources", {}).items()):
+        return None
+    return {k: v["mfma_busy"] for k, v in rec["kernels"].items()}
 
 
 def calibrate_copy():
@@ -523,6 +540,7 @@ def main():
 
     # the counter records cover the 8B shape's kernels
     is8b = args.config == "llama8b" and not args.swa
+    busy = mfma_busy("prefill_q8_0" if q8 else "prefill") if is8b and cfg["kv_dtype"] == "bf16" else None
     shape = {"llama8b": "8B", "llama1b": "1B", "tiny": "tiny"}.get(args.config, args.config)
     out = {
         "metric": (f"decode tok/s (% HBM peak) + prefill tok/s (% MFMA peak), {shape}-shape bf16" if not q8 else
@@ -563,7 +581,9 @@ def main():
                              "achieved": round(gg_tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                              "frac": round(gg_tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic("prefill_q8_0" if q8 else "prefill") if is8b else None,
                              "avg_launch_us": round(gg_us, 2), "flops_per_launch": gg_flops,
-                             "executed_flops_per_launch": 2 * gg_flops},
+                             "executed_flops_per_launch": 2 * gg_flops,
+                             "mfma_busy": (busy or {}).get("gate_up"),
+                             "mfma_busy_by_kernel": busy},
         "measured_peaks": peaks,
         "kv_slide": slide,
         "sampling": samp,
