@@ -437,7 +437,7 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
   constexpr int CPL = 16 / RG;   // V loads: cells of a tile per lane
   constexpr int VP = HD + 4;     // V tile row pitch in LDS (elements; breaks bank conflicts)
   __shared__ int32_t cell_s[kCellStage];
-  __shared__ short v_s[4][16 * VP];
+  __shared__ __attribute__((aligned(16))) short v_s[4][16 * VP];
   __shared__ float pt_s[4][G][16];
   __shared__ float acc_s[4][G][HD];
   __shared__ float m_s[4][G], l_s[4][G];
@@ -647,16 +647,16 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
       }
     }
     // value product: right operand lane l = cells 4 (l / 16) .. + 4 of
-    // dimension 16 n + l % 16, read down the LDS tile's column; a column of
-    // ones gives the probability sums
+    // dimension 16 n + l % 16, read down the LDS tile's column with one
+    // transposing LDS load; a column of ones gives the probability sums
 #pragma unroll
     for (int n = 0; n < NN; ++n) {
-      vec4 b;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const short x = vw[(hrow + q) * VP + n * 16 + (lane & 15)];
-        b[q] = __builtin_bit_cast(typename std::remove_reference<decltype(b[0])>::type, x);
-      }
+      // transposing LDS read: in each 16-lane group, lane 4e + q points at
+      // cell hrow + e, dimensions 16n + 4q .. + 4; lane i of the group
+      // receives dimension 16n + i of cells hrow .. hrow + 3
+      const s16x4 bt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)&vw[(hrow + ((lane & 15) >> 2)) * VP + n * 16 + 4 * (lane & 3)]);
+      const vec4 b = __builtin_bit_cast(vec4, bt);
       if constexpr (Q8) {
         acc[n] = M::mma4(phb[n / 2], b, acc[n]);
         acc[n] = M::mma4(plb[n / 2], b, acc[n]);
