@@ -99,3 +99,17 @@ def test_matrix_core_long_context(hd, n_head, n_head_kv):
     prompt = tdf_synth.prompt(cfg, 0, 1100)
     log(f"q8 cache matrix cores hd={hd} G={n_head // n_head_kv}")
     teacher_forced(cfg, w, 1200, prompt, 4, TOL_BF16, "q8_0", n_ubatch=512, label=f"kvq8-mfma-hd{hd}")
+
+
+def test_llama8b_width_single_token_quantize():
+    """8B-class widths (32 query heads, 8 KV heads of 128), two layers, Q8_0
+    cache: a 600-token prompt in ubatches of 512 and 88 (the matrix-core
+    projections write float32 rows that a separate pass quantizes), then four
+    single-token steps, whose QKV GEMV quantizes its own K/V rows in its
+    epilogue (192 blocks of 32 rows, each one 32-value block of a head's
+    row)."""
+    cfg = dict(tdf_synth.CONFIGS["llama8b"])
+    cfg, w = make_weights(cfg, layers=2)
+    prompt = tdf_synth.prompt(cfg, 0, 600)
+    log("q8 cache at 8B widths")
+    teacher_forced(cfg, w, 1024, prompt, 4, TOL_BF16, "q8_0", n_ubatch=512, label="kvq8-8b-2L")
