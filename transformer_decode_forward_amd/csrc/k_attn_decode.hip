@@ -721,12 +721,15 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
 }
 
 // One block of NTH threads (NTH >= 64, a multiple of HD) per (query head,
-// token).  Wave 0 turns the per-split maxima and sums into weights
-// exp(m_j - M) and the total L; then NTH/HD thread groups each sum every
-// (NTH/HD)-th split for all HD outputs, 16 independent loads at a time, and
-// the groups are added through LDS.  Decode ubatches (many splits, few
-// tokens) use 256 threads; larger ubatches (few splits, many tokens) the
-// smallest block.
+// token).  Every load goes out before the token's split count is known: the
+// NTH/HD thread groups request their splits' accumulators (every
+// (NTH/HD)-th of the launch's n_chunks, up to kMergeBatch of them at once)
+// while wave 0 requests the per-split maxima and sums; with the count in
+// hand, wave 0 turns them into weights exp(m_j - M) and the total L, the
+// groups sum their weighted splits (splits past the count are selected away,
+// never multiplied: their memory holds stale values) and add up through
+// LDS.  Decode ubatches (many splits, few tokens) use 256 threads; larger
+// ubatches (few splits, many tokens) the smallest block.
 constexpr int kMergeBatch = 16;
 template <int HD, int NTH>
 __global__ void __launch_bounds__(NTH) attn_merge_kernel(AttnArgs a) {
@@ -735,42 +738,52 @@ __global__ void __launch_bounds__(NTH) attn_merge_kernel(AttnArgs a) {
   __shared__ float part_s[NP][HD];
   __shared__ float inv_l;
   const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  const int nc = a.n_chunks;  // splits launched (>= the token's count)
+  const int64_t base = ((int64_t)t * a.H + h) * nc;
+  const int d = tid % HD, part = tid / HD;
+  const float* pa = a.part_acc + base * HD + d;
+  // first batch of accumulators and the maxima / sums, requested together
+  float v[kMergeBatch];
+#pragma unroll
+  for (int b = 0; b < kMergeBatch; ++b) v[b] = pa[(int64_t)min(part + b * NP, nc - 1) * HD];
+  constexpr int R = kMergeMaxSplits / 64;
+  float2 ml[R];
+  if (tid < 64) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) ml[r] = *(const float2*)&a.part_ml[(base + min(tid + r * 64, nc - 1)) * 2];
+  }
   const int nch = (a.n_vis[t] + a.chunk - 1) / a.chunk;
   if (nch == 1 && !a.merge_single) return;  // the split kernel wrote this token already
-  const int64_t base = ((int64_t)t * a.H + h) * a.n_chunks;
   if (tid < 64) {
-    constexpr int R = kMergeMaxSplits / 64;
-    float2 ml[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      ml[r] = *(const float2*)&a.part_ml[(base + min(tid + r * 64, nch - 1)) * 2];
     float M = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < R; ++r) M = fmaxf(M, ml[r].x);
+    for (int r = 0; r < R; ++r)
+      if (tid + r * 64 < nch) M = fmaxf(M, ml[r].x);
     M = wave_max(M);
     float L = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int jj = tid + r * 64;
       const float w = jj < nch ? __expf(ml[r].x - M) : 0.f;
-      if (jj < nch) w_s[jj] = w;
-      L = fmaf(ml[r].y, w, L);
+      if (jj < nch) {
+        w_s[jj] = w;
+        L = fmaf(ml[r].y, w, L);
+      }
     }
     L = wave_sum(L);
     if (tid == 0) inv_l = 1.f / L;
   }
   __syncthreads();
-  const int d = tid % HD, part = tid / HD;
-  const float* pa = a.part_acc + base * HD + d;
   float o = 0.f;
   for (int j0 = part; j0 < nch; j0 += NP * kMergeBatch) {
-    float v[kMergeBatch];
+    if (j0 != part) {
 #pragma unroll
-    for (int b = 0; b < kMergeBatch; ++b) v[b] = pa[(int64_t)min(j0 + b * NP, nch - 1) * HD];
+      for (int b = 0; b < kMergeBatch; ++b) v[b] = pa[(int64_t)min(j0 + b * NP, nc - 1) * HD];
+    }
 #pragma unroll
     for (int b = 0; b < kMergeBatch; ++b) {
       const int jj = j0 + b * NP;
-      o = fmaf(v[b], jj < nch ? w_s[jj] : 0.f, o);
+      if (jj < nch) o = fmaf(v[b], w_s[jj], o);
     }
   }
   part_s[part][d] = o;
