@@ -15,6 +15,8 @@ durations come from tdf_time_op, back-to-back launches of that kernel on the
 library's stream between two HIP events, cycling over the 32 layers' weights.
 ``traffic`` is read from the committed rocprofv3 counter summary of that
 kernel when the kernel source still matches it (else null).
+``multiseq`` (32 sequences in lock-step steps, same weights) and ``llama1b``
+(the 1B shape, its own weights) are compact sections of other workloads.
 ``kernels`` is a per-operation breakdown from an eager repeat with a HIP
 event pair around every launch (it includes the events' own overhead):
 ``prefill`` covers the prompt, ``decode`` the timed single-token steps.
@@ -304,6 +306,47 @@ def run_multiseq(args, cfg, model=None, steps=None, warmup=None):
     }
 
 
+def run_small(cfg, steps=64, warmup=8):
+    """A compact single-sequence run of another shape (its own prompt in
+    ubatches, then graph-replayed greedy decode steps): decode tok/s and
+    fraction of the HBM peak, prefill tok/s and fraction of the MFMA peak."""
+    import torch
+    import tdf_synth
+    import transformer_decode_forward_amd as tdf
+    P, U = cfg["prompt_len"], cfg["n_ubatch"]
+    model, _ = build_model(cfg, keep_host=False)
+    ctx = tdf.Context(model, n_ctx=cfg["n_ctx"], n_ubatch=U, kv_dtype=cfg["kv_dtype"])
+    prompt = tdf_synth.prompt(cfg, 0, P)
+    for _ in range(2):  # the second prefill is timed
+        ctx.kv_clear()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        assert ctx.decode(prompt) == 0, tdf.tdf_last_error()
+        t_pre = time.perf_counter() - t0
+    tok = ctx.argmax_ith(P - 1)
+    for _ in range(warmup):
+        assert ctx.decode([tok]) == 0, tdf.tdf_last_error()
+        tok = ctx.argmax_ith(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        assert ctx.decode([tok]) == 0, tdf.tdf_last_error()
+        tok = ctx.argmax_ith(0)
+    torch.cuda.synchronize()
+    t_dec = time.perf_counter() - t0
+    ctx.close()
+    del model
+    mean_ctx = P + warmup + (steps - 1) / 2.0
+    ms = 1000.0 * t_dec / steps
+    step_bytes = decode_bytes(cfg, mean_ctx)
+    flops = prefill_flops(cfg, P, U)
+    return {"decode": {"tok_s": round(steps / t_dec, 2), "ms_per_step": round(ms, 4), "mean_ctx": mean_ctx,
+                       "algorithmic_bytes_per_step": int(step_bytes),
+                       "frac_hbm_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "prefill": {"tok_s": round(P / t_pre, 1), "ms": round(1000 * t_pre, 3),
+                        "frac_mfma_peak": round(flops / t_pre / 1e12 / MFMA_BF16_PEAK_TFS, 4)}}
+
+
 def run_70b(args, cfg):
     """70B-class model on one GPU: 4096-token prompt in ubatches of 512, then
     decode windows at positions 4096, 16384 and 32752 (the cache filled up to
@@ -379,7 +422,7 @@ def main():
     ap.add_argument("--config", default="llama8b")
     ap.add_argument("--no-peaks", action="store_true")
     ap.add_argument("--no-multiseq", action="store_true",
-                    help="skip the 32-sequence section of the default (8B) run")
+                    help="skip the 32-sequence and 1B-shape sections of the default (8B) run")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--weights", choices=["bf16", "q8_0"], default=None,
                     help="weight storage of the single-sequence workload (default: the config's, bf16)")
@@ -533,6 +576,15 @@ def main():
         log("multi-sequence section (32 sequences)")
         multi = run_multiseq(args, mcfg, model=model, steps=8, warmup=2)
 
+    # the 1B shape, compactly (its own weights; the 8B model's are freed first
+    # only in the sense that both fit: 16 GB and 2.5 GB)
+    small = None
+    if args.config == "llama8b" and not args.no_multiseq and not args.swa:
+        scfg = dict(tdf_synth.CONFIGS["llama1b"])
+        log("1B-shape section (512-token prompt, 64 decode steps)")
+        small = run_small(scfg)
+        log(f"1B: prefill {small['prefill']['tok_s']:.0f} tok/s, decode {small['decode']['tok_s']:.1f} tok/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -592,6 +644,10 @@ def main():
     }
     if multi is not None:
         out["multiseq"] = {k: multi[k] for k in ("config", "decode", "prefill", "steps", "warmup", "ms_per_step")}
+    if small is not None:
+        out["llama1b"] = dict(small, config={"workload": "llama1b: batch 1, 512-token prompt in one ubatch "
+                                                         "(last-position logits), then greedy decode steps; KV f16 4096 cells",
+                                             "d_model": 2048, "n_layer": 16})
     print(json.dumps(out), flush=True)
 
 
