@@ -89,7 +89,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(AttnArgs a) {
   __shared__ float acc_s[4][G][HD];
   __shared__ float m_s[4][G], l_s[4][G];
 
-  const int j = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
+  const int g = blockIdx.x, j = blockIdx.y, t = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nvis = a.n_vis[t];
   const int c_lo = j * a.chunk;
@@ -443,7 +443,7 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
   __shared__ float m_s[4][G], l_s[4][G];
   __shared__ float vs_s[4][16][Q8 ? NB : 1];  // Q8_0: value block scales of the wave's tile
 
-  const int j = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
+  const int g = blockIdx.x, j = blockIdx.y, t = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nvis = a.n_vis[t];
   const int c_lo = j * a.chunk;
@@ -801,7 +801,13 @@ __global__ void __launch_bounds__(NTH) attn_merge_kernel(AttnArgs a) {
 template <typename KvT, int HD>
 static hipError_t attn_launch_hd(const AttnArgs& a, hipStream_t s) {
   const int G = a.H / a.Hkv;
-  dim3 grid(a.n_chunks, a.Hkv, a.T);
+  // kv head fastest: consecutive blocks go to consecutive XCDs (block b to
+  // XCD b % 8), so with 8 kv heads each XCD takes one head of every
+  // (token, chunk) and all XCDs get the same work.  With the chunk index
+  // fastest, XCD k would take chunk k of every token: sequences of unequal
+  // length leave the XCDs of the high chunks idle (32 sequences of
+  // 1.2k..7.9k cells: 145 us against 120 us per layer).
+  dim3 grid(a.Hkv, a.n_chunks, a.T);
   // 16-bit and Q8_0 caches with head_dim 64 or 128: scores and value
   // products on the matrix cores (chunks of at most kCellStage cells)
   bool done = false;
