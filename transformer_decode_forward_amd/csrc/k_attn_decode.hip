@@ -412,6 +412,60 @@ __device__ __forceinline__ float row16_max(float v) {
 }
 __device__ __forceinline__ float row16_sum(float v) { return group_sum<16>(v); }
 
+// Work items of the matrix-core decode attention, one (token, chunk) pair
+// each: items 0 .. F-1 are the whole chunks (a.chunk cells) of every token in
+// token order, items F .. F+P-1 the last, partial chunks of the tokens whose
+// visible count is not a multiple of a.chunk, again in token order.  Blocks
+// are placed on the shader engines of an XCD round-robin and in order, and a
+// block that must wait for a slot on a full engine holds back the ones after
+// it; items of (nearly) equal size in dispatch order keep the engines evenly
+// loaded, and the shorter partial chunks fill the end of the launch.  Every
+// wave of a block computes the same result; false past the last item.
+__device__ __forceinline__ bool decode_item(const int32_t* n_vis, int T, int chunk, int item, int lane,
+                                            int& t_out, int& j_out) {
+  int base = 0;  // whole chunks of the tokens before this group of 64
+#pragma unroll 1
+  for (int t0 = 0; t0 < T; t0 += 64) {
+    const int nv = t0 + lane < T ? n_vis[t0 + lane] : 0;
+    const int full = nv / chunk;
+    int incl = full;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const int tot = __shfl(incl, 63);
+    if (item < base + tot) {
+      const int tl = __builtin_ctzll(__ballot(base + incl > item));
+      t_out = t0 + tl;
+      j_out = item - base - __shfl(incl - full, tl);
+      return true;
+    }
+    base += tot;
+  }
+  int rel = item - base;  // among the partial chunks
+#pragma unroll 1
+  for (int t0 = 0; t0 < T; t0 += 64) {
+    const int nv = t0 + lane < T ? n_vis[t0 + lane] : 0;
+    const int part = nv % chunk != 0 ? 1 : 0;
+    int incl = part;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const int tot = __shfl(incl, 63);
+    if (rel < tot) {
+      const int tl = __builtin_ctzll(__ballot(incl > rel));
+      t_out = t0 + tl;
+      j_out = __shfl(nv / chunk, tl);
+      return true;
+    }
+    rel -= tot;
+  }
+  return false;
+}
+
 template <typename KvT, int HD, int G>
 __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
   typedef Mfma16<KvT> M;
@@ -443,13 +497,20 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
   __shared__ float m_s[4][G], l_s[4][G];
   __shared__ float vs_s[4][16][Q8 ? NB : 1];  // Q8_0: value block scales of the wave's tile
 
-  const int g = blockIdx.x, j = blockIdx.y, t = blockIdx.z;
+  // one-dimensional grid: kv head fastest (consecutive blocks go to
+  // consecutive XCDs, so with 8 kv heads each XCD takes one head), then the
+  // work item
+  const int g = blockIdx.x % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int t, j;
+  if (!decode_item(a.n_vis, a.T, a.chunk, blockIdx.x / a.Hkv, lane, t, j)) return;
+  t = __builtin_amdgcn_readfirstlane(t);
+  j = __builtin_amdgcn_readfirstlane(j);
+  if (j >= a.n_chunks) return;  // cells past the launch's split count are not covered
   const int nvis = a.n_vis[t];
   const int c_lo = j * a.chunk;
-  if (c_lo >= nvis) return;
   const int c_hi = min(nvis, c_lo + a.chunk);
-  const int span = c_hi - c_lo;  // <= kCellStage (checked at launch)
+  const int span = c_hi - c_lo;  // 1 .. kCellStage (checked at launch)
   const int ntiles = (span + 15) >> 4;
   const int32_t* cells = a.cell_list + a.list_off[t];
   const ST* kc = (const ST*)a.k_cache + (int64_t)g * a.n_ctx * HD;
@@ -805,19 +866,21 @@ static hipError_t attn_launch_hd(const AttnArgs& a, hipStream_t s) {
   // XCD b % 8), so with 8 kv heads each XCD takes one head of every
   // (token, chunk) and all XCDs get the same work.  With the chunk index
   // fastest, XCD k would take chunk k of every token: sequences of unequal
-  // length leave the XCDs of the high chunks idle (32 sequences of
-  // 1.2k..7.9k cells: 145 us against 120 us per layer).
+  // length leave the XCDs of the high chunks idle.  The matrix-core kernel
+  // also packs the (token, chunk) pairs that have cells into a dense list
+  // (decode_item), so that no surplus block sits between two working ones.
   dim3 grid(a.Hkv, a.n_chunks, a.T);
+  const unsigned items = (unsigned)a.Hkv * a.n_chunks * a.T;
   // 16-bit and Q8_0 caches with head_dim 64 or 128: scores and value
   // products on the matrix cores (chunks of at most kCellStage cells)
   bool done = false;
   if constexpr (!std::is_same<KvT, float>::value && (HD == 64 || HD == 128)) {
     if (a.chunk <= kCellStage) {
       switch (G) {
-        case 1: attn_decode_mfma_kernel<KvT, HD, 1><<<grid, 256, 0, s>>>(a); break;
-        case 2: attn_decode_mfma_kernel<KvT, HD, 2><<<grid, 256, 0, s>>>(a); break;
-        case 4: attn_decode_mfma_kernel<KvT, HD, 4><<<grid, 256, 0, s>>>(a); break;
-        case 8: attn_decode_mfma_kernel<KvT, HD, 8><<<grid, 256, 0, s>>>(a); break;
+        case 1: attn_decode_mfma_kernel<KvT, HD, 1><<<items, 256, 0, s>>>(a); break;
+        case 2: attn_decode_mfma_kernel<KvT, HD, 2><<<items, 256, 0, s>>>(a); break;
+        case 4: attn_decode_mfma_kernel<KvT, HD, 4><<<items, 256, 0, s>>>(a); break;
+        case 8: attn_decode_mfma_kernel<KvT, HD, 8><<<items, 256, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
       }
       done = true;
