@@ -40,3 +40,27 @@ def test_decode_attention_group_sizes(hd, H, Hkv, kv_dtype):
     calls.append(dict(tokens=tdf_synth.prompt(cfg, 80, 2), seq_ids=[[0], [1]], logits=np.ones(2, np.int8)))
     run_pair(cfg, w, dict(n_ctx=2048, n_ubatch=256, n_seq_max=2), calls, TOL_BF16, kv_dtype,
              f"attn hd{hd} G{H // Hkv}")
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "q8_0"])
+def test_decode_split_list_unequal_sequences(kv_dtype):
+    """Five sequences whose step tokens see 128, 256, 301, 1001 and 65 cells.
+    At this size the host splits every token's cells into chunks of 128, so
+    the matrix-core kernel's dense (token, chunk) list holds in one launch a
+    token with a single whole chunk (written directly), one with whole chunks
+    only, one with whole chunks and a partial last one, a long one, and one
+    with a single partial chunk; a second step moves every count by one."""
+    hd, H, Hkv = 128, 8, 2
+    d = H * hd
+    cfg = dict(SMALL, n_embd=d, n_head=H, n_head_kv=Hkv, head_dim=hd, n_ff=256, n_vocab=300,
+               seed=91, weight_std=0.08 * (128 / d) ** 0.5)
+    cfg, w = make_weights(cfg)
+    lens = (127, 255, 300, 1000, 64)
+    calls = []
+    for s, n in enumerate(lens):
+        calls.append(dict(tokens=tdf_synth.prompt(cfg, 100 + s, n), seq_ids=[[s]] * n))
+    for k in range(2):
+        calls.append(dict(tokens=tdf_synth.prompt(cfg, 120 + k, len(lens)), seq_ids=[[s] for s in range(len(lens))],
+                          logits=np.ones(len(lens), np.int8)))
+    run_pair(cfg, w, dict(n_ctx=2048, n_ubatch=256, n_seq_max=len(lens)), calls, TOL_BF16, kv_dtype,
+             f"split list {kv_dtype}")
