@@ -297,6 +297,71 @@ __global__ void __launch_bounds__(256) skinny_epilogue_kernel(SkinnyArgs s) {
   }
 }
 
+// Residual pass with the next RMSNorm (EPI_RESIDUAL, norm_out_g set): one
+// block of 1024 threads per token holds the token's whole row, so the sum of
+// squares of the new residual needs no second pass over memory.  Thread i
+// takes columns 4 i + 4096 p (float4), requests every K slice's partial at
+// once, adds them to the residual, writes it back, and after the block's
+// reduction writes g * x_new * r as a bf16 pair, r = 1 / sqrt(ss / N + eps)
+// as rmsnorm_kernel computes it.
+constexpr int kSkNormThreads = 1024;
+__global__ void __launch_bounds__(kSkNormThreads) skinny_residual_norm_kernel(SkinnyArgs s) {
+  const LinearArgs& a = s.a;
+  __shared__ float red[kSkNormThreads / 64];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int N = s.N;
+  float* xo = a.out + (int64_t)t * a.ldo;
+  constexpr int P = 2;  // float4 per thread: rows of up to 8192
+  float4 xv[P];
+  float ss = 0.f;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int n = tid * 4 + p * 4 * kSkNormThreads;
+    xv[p] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (n < N) {
+      float4 y = *(const float4*)(xo + n);
+      for (int k0 = 0; k0 < s.ksplit; k0 += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = *(const float4*)&s.part[((int64_t)min(k0 + k, s.ksplit - 1) * 32 + t) * N + n];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float on = k0 + k < s.ksplit ? 1.f : 0.f;
+          y.x = fmaf(v[k].x, on, y.x); y.y = fmaf(v[k].y, on, y.y);
+          y.z = fmaf(v[k].z, on, y.z); y.w = fmaf(v[k].w, on, y.w);
+        }
+      }
+      *(float4*)(xo + n) = y;
+      xv[p] = y;
+      ss += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
+    }
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  ss = 0.f;
+#pragma unroll
+  for (int w = 0; w < kSkNormThreads / 64; ++w) ss += red[w];
+  const float r = 1.0f / sqrtf(ss / (float)N + a.norm_out_eps);
+  const int64_t ro = (int64_t)t * N;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    const int n = tid * 4 + p * 4 * kSkNormThreads;
+    if (n >= N) break;
+    const float4 gv = *(const float4*)(a.norm_out_g + n);
+    const float v[4] = {xv[p].x * r * gv.x, xv[p].y * r * gv.y, xv[p].z * r * gv.z, xv[p].w * r * gv.w};
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split_bf16(v[e], h[e], l[e]);
+    *(uint2*)(a.norm_out_hi + ro + n) = make_uint2(h[0] | (uint32_t)h[1] << 16, h[2] | (uint32_t)h[3] << 16);
+    *(uint2*)(a.norm_out_lo + ro + n) = make_uint2(l[0] | (uint32_t)l[1] << 16, l[2] | (uint32_t)l[3] << 16);
+  }
+}
+
+bool skinny_norm_supported(const LinearArgs& a) {
+  return a.epi == EPI_RESIDUAL && a.n0 % 4 == 0 && a.n0 <= 8 * kSkNormThreads && a.ldo % 4 == 0;
+}
+
 bool skinny_supported(const LinearArgs& a) {
   const int N = a.epi == EPI_SWIGLU ? 2 * a.n0 : a.n0 + a.n1 + a.n2;
   return (a.weight_dtype == TDF_BF16 || a.weight_dtype == TDF_Q8_0) && a.act_hi && a.act_lo && a.T > 0 &&
@@ -311,11 +376,13 @@ hipError_t launch_linear_skinny(const LinearArgs& a, float* part, hipStream_t st
   s.N = a.epi == EPI_SWIGLU ? 2 * a.n0 : a.n0 + a.n1 + a.n2;
   s.part = part;
   // K slices: enough blocks to fill the chip (>= 512), each slice a whole
-  // number of 128-wide chunks, within the workspace
+  // number of 128-wide chunks and at least 4 of them, within the workspace
+  // (8B widths at 32 tokens, output projection: 8 slices of 4 chunks 15.3 us
+  // with the epilogue, 16 slices of 2 chunks 16.7 us)
   const int nrt = (s.N + 127) / 128;
   const int chunks = a.K / kSkChunk;
   int ks = 1;
-  while (nrt * ks < 512 && ks * 2 <= chunks && (int64_t)s.N * 32 * ks * 2 <= kSkinnyPartFloats) ks *= 2;
+  while (nrt * ks < 512 && chunks / (ks * 2) >= 4 && (int64_t)s.N * 32 * ks * 2 <= kSkinnyPartFloats) ks *= 2;
   s.kslice = ((chunks + ks - 1) / ks) * kSkChunk;
   s.ksplit = (a.K + s.kslice - 1) / s.kslice;
   const bool q8 = a.weight_dtype == TDF_Q8_0;
@@ -328,6 +395,11 @@ hipError_t launch_linear_skinny(const LinearArgs& a, float* part, hipStream_t st
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.norm_out_g) {
+    if (!skinny_norm_supported(a)) return hipErrorInvalidValue;
+    skinny_residual_norm_kernel<<<a.T, kSkNormThreads, 0, st>>>(s);
+    return hipGetLastError();
+  }
   const int64_t n_thr = a.epi == EPI_SWIGLU ? (int64_t)a.T * a.n0 : (int64_t)a.T * ((s.N + 1) / 2);
   const unsigned blocks = (unsigned)((n_thr + 255) / 256);
   switch (a.epi) {

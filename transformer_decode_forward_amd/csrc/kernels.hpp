@@ -43,6 +43,13 @@ struct LinearArgs {
   float* next_u = nullptr;
   float* next_ssp = nullptr;
   int next_stride = 0;
+  // 9..32-token residual producer (launch_linear_skinny, EPI_RESIDUAL): when
+  // norm_out_g is set, the residual pass also writes the next RMSNorm's
+  // output g * x_new / sqrt(mean(x_new^2) + norm_out_eps) as a bf16 pair
+  const float* norm_out_g = nullptr;
+  uint16_t* norm_out_hi = nullptr;
+  uint16_t* norm_out_lo = nullptr;
+  float norm_out_eps = 0.f;
   const uint16_t* act_hi = nullptr;
   const uint16_t* act_lo = nullptr;
   // epilogue
@@ -71,6 +78,8 @@ bool gemm_supported(const LinearArgs& a);
 // then an epilogue pass); bf16 weights, hi/lo activations, K % 128 == 0
 constexpr int64_t kSkinnyPartFloats = 32ll * 65536;
 bool skinny_supported(const LinearArgs& a);
+// the residual pass can also write the next RMSNorm (norm_out_g)
+bool skinny_norm_supported(const LinearArgs& a);
 hipError_t launch_linear_skinny(const LinearArgs& a, float* part, hipStream_t s);
 
 // x[t][:] = E[token[t]][:] (to float32); with g set also u = g * x and

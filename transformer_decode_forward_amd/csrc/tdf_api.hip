@@ -554,6 +554,21 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
   // kernel that last wrote `cur` (embedding, residual GEMV, row gather) or by
   // an explicit pass when that kernel could not (matrix-core producer).
   int u_parts = 0;  // 0: not ready
+  // c->h_hi / h_lo already hold the next RMSNorm of `cur` (written by a
+  // 9..32-token residual projection's last pass)
+  bool h_ready = false;
+  auto on_skinny = [&](const LinearArgs& a, bool mfma) {
+    return mfma && a.T <= kDecodeMaxT && c->skinny_part && skinny_supported(a);
+  };
+  // a residual projection on the 9..32-token path also writes the next norm
+  // for a matrix-core consumer of the same rows
+  auto fuse_next_norm = [&](LinearArgs& a, bool mfma, const float* g) {
+    if (!on_skinny(a, mfma)) return;
+    LinearArgs t = a;
+    t.norm_out_g = g;
+    if (!skinny_norm_supported(t)) return;
+    a.norm_out_g = g; a.norm_out_hi = c->h_hi; a.norm_out_lo = c->h_lo; a.norm_out_eps = h.rms_eps;
+  };
   float* cur = c->x;  // residual rows being carried
   auto prep_norm = [&](const float* g, int rows) -> int {
     const int ps = prof_begin(c, TDF_OP_NORM, false);
@@ -576,11 +591,11 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     const tdf_layer_weights& W = m->layers[l];
     // attention block
     const bool big = use_mfma(T, d);
-    if (big) {
+    if (big && !h_ready) {
       ps = prof_begin(c, TDF_OP_NORM, big);
       TDF_HIP(launch_rmsnorm(cur, (const float*)W.attn_norm, T, d, h.rms_eps, nullptr, c->h_hi, c->h_lo, s));
       prof_end(c, ps);
-    } else if (!u_parts) {
+    } else if (!big && !u_parts) {
       if (int rc = prep_norm((const float*)W.attn_norm, T)) return rc;
     }
     LinearArgs qa;
@@ -678,8 +693,10 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     if (!wo_mfma && !bigm && !narrow) {
       oa.next_g = (const float*)W.ffn_norm; oa.next_u = c->u; oa.next_ssp = c->ssp; oa.next_stride = c->ssp_stride;
     }
+    if (bigm && !narrow) fuse_next_norm(oa, wo_mfma, (const float*)W.ffn_norm);
     if (int rc = run_linear(c, oa, wo_mfma, TDF_OP_WO)) return rc;
     u_parts = oa.next_g ? gemv_residual_parts(d) : 0;
+    h_ready = oa.norm_out_g != nullptr;
 
     if (last) {
       if (u.R == 0) return TDF_OK;
@@ -694,11 +711,11 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
       T = u.R;
     }
     // MLP block
-    if (bigm) {
+    if (bigm && !h_ready) {
       ps = prof_begin(c, TDF_OP_NORM, bigm);
       TDF_HIP(launch_rmsnorm(cur, (const float*)W.ffn_norm, T, d, h.rms_eps, nullptr, c->h_hi, c->h_lo, s));
       prof_end(c, ps);
-    } else if (!u_parts) {
+    } else if (!bigm && !u_parts) {
       if (int rc = prep_norm((const float*)W.ffn_norm, T)) return rc;
     }
     LinearArgs ga;
@@ -716,8 +733,11 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     if (!bigm && next_gemv) {
       da.next_g = attn_gain(l + 1); da.next_u = c->u; da.next_ssp = c->ssp; da.next_stride = c->ssp_stride;
     }
+    // the next consumer (next layer's QKV, or the LM head) reads the same rows
+    if (!next_gemv) fuse_next_norm(da, bigm, attn_gain(l + 1));
     if (int rc = run_linear(c, da, bigm, TDF_OP_DOWN)) return rc;
     u_parts = da.next_g ? gemv_residual_parts(d) : 0;
+    h_ready = da.norm_out_g != nullptr;
   }
   if (L == 0) {
     if (u.R == 0) return TDF_OK;
@@ -730,11 +750,11 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
   }
   // output norm + LM head into this ubatch's logits rows
   const bool bigo = use_mfma(T, d);
-  if (bigo) {
+  if (bigo && !h_ready) {
     ps = prof_begin(c, TDF_OP_NORM, bigo);
     TDF_HIP(launch_rmsnorm(cur, m->output_norm, T, d, h.rms_eps, nullptr, c->h_hi, c->h_lo, s));
     prof_end(c, ps);
-  } else if (!u_parts) {
+  } else if (!bigo && !u_parts) {
     if (int rc = prep_norm(m->output_norm, T)) return rc;
   }
   LinearArgs la;
