@@ -112,16 +112,23 @@ __global__ void __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(2))
   const float scale = rsqrtf((float)HD);
 
   typedef typename M::elem E;
-  // Q^T fragments (B operand), hi and lo: lane holds Q[query][ks*16 + qg*8 + 0..7]
+  // Q^T fragments (B operand), hi and lo: lane holds Q[query][ks*16 + qg*8 + 0..7],
+  // requested as two 16-byte pieces per ks (one 4-byte request per element
+  // put 64 scattered addresses in each of 64 requests: 8-15 us per block)
   vec qh[HD / 16], qlo[HD / 16];
+  {
+    const float* qrow = a.q + ((int64_t)max(t, 0) * a.H + h) * HD + qg * 8;
 #pragma unroll
-  for (int ks = 0; ks < HD / 16; ++ks) {
+    for (int ks = 0; ks < HD / 16; ++ks) {
+      const float4 x0 = *(const float4*)(qrow + ks * 16), x1 = *(const float4*)(qrow + ks * 16 + 4);
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = t >= 0 ? a.q[((int64_t)t * a.H + h) * HD + ks * 16 + qg * 8 + e] * scale : 0.f;
-      const E hi = (E)v;
-      qh[ks][e] = hi;
-      qlo[ks][e] = (E)(v - (float)hi);
+      for (int e = 0; e < 8; ++e) {
+        const float v = t >= 0 ? x[e] * scale : 0.f;
+        const E hi = (E)v;
+        qh[ks][e] = hi;
+        qlo[ks][e] = (E)(v - (float)hi);
+      }
     }
   }
 
