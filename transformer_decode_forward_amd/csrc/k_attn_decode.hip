@@ -791,9 +791,12 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
 // never multiplied: their memory holds stale values) and add up through
 // LDS.  Decode ubatches (many splits, few tokens) use 256 threads; larger
 // ubatches (few splits, many tokens) the smallest block.
-constexpr int kMergeBatch = 16;
-template <int HD, int NTH>
+// BATCH (the accumulators a thread requests at once) and R (the maxima and
+// sums per lane of wave 0, 64 splits each) are sized at launch from the
+// split count, so that a launch with few splits requests no clamped copies.
+template <int HD, int NTH, int BATCH, int R>
 __global__ void __launch_bounds__(NTH) attn_merge_kernel(AttnArgs a) {
+  constexpr int kMergeBatch = BATCH;
   constexpr int NP = NTH / HD;
   __shared__ float w_s[kMergeMaxSplits];
   __shared__ float part_s[NP][HD];
@@ -807,7 +810,6 @@ __global__ void __launch_bounds__(NTH) attn_merge_kernel(AttnArgs a) {
   float v[kMergeBatch];
 #pragma unroll
   for (int b = 0; b < kMergeBatch; ++b) v[b] = pa[(int64_t)min(part + b * NP, nc - 1) * HD];
-  constexpr int R = kMergeMaxSplits / 64;
   float2 ml[R];
   if (tid < 64) {
 #pragma unroll
@@ -900,6 +902,15 @@ static hipError_t attn_launch_hd(const AttnArgs& a, hipStream_t s) {
   return launch_attention_merge(a, s);
 }
 
+template <int HD, int NTH>
+static void merge_launch(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  const int per = (a.n_chunks + NTH / HD - 1) / (NTH / HD);  // splits per thread group
+  if (per <= 4 && a.n_chunks <= 64) attn_merge_kernel<HD, NTH, 4, 1><<<grid, NTH, 0, s>>>(a);
+  else if (per <= 8 && a.n_chunks <= 64) attn_merge_kernel<HD, NTH, 8, 1><<<grid, NTH, 0, s>>>(a);
+  else if (a.n_chunks <= 64) attn_merge_kernel<HD, NTH, 16, 1><<<grid, NTH, 0, s>>>(a);
+  else attn_merge_kernel<HD, NTH, 16, kMergeMaxSplits / 64><<<grid, NTH, 0, s>>>(a);
+}
+
 hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   if (a.n_chunks > kMergeMaxSplits) return hipErrorInvalidValue;
@@ -907,20 +918,20 @@ hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s) {
   const bool wide = a.n_chunks > 8;
   switch (a.hd) {
     case 16:
-      if (wide) attn_merge_kernel<16, 256><<<grid, 256, 0, s>>>(a);
-      else attn_merge_kernel<16, 64><<<grid, 64, 0, s>>>(a);
+      if (wide) merge_launch<16, 256>(a, grid, s);
+      else merge_launch<16, 64>(a, grid, s);
       break;
     case 32:
-      if (wide) attn_merge_kernel<32, 256><<<grid, 256, 0, s>>>(a);
-      else attn_merge_kernel<32, 64><<<grid, 64, 0, s>>>(a);
+      if (wide) merge_launch<32, 256>(a, grid, s);
+      else merge_launch<32, 64>(a, grid, s);
       break;
     case 64:
-      if (wide) attn_merge_kernel<64, 256><<<grid, 256, 0, s>>>(a);
-      else attn_merge_kernel<64, 64><<<grid, 64, 0, s>>>(a);
+      if (wide) merge_launch<64, 256>(a, grid, s);
+      else merge_launch<64, 64>(a, grid, s);
       break;
     case 128:
-      if (wide) attn_merge_kernel<128, 256><<<grid, 256, 0, s>>>(a);
-      else attn_merge_kernel<128, 128><<<grid, 128, 0, s>>>(a);
+      if (wide) merge_launch<128, 256>(a, grid, s);
+      else merge_launch<128, 128>(a, grid, s);
       break;
     default: return hipErrorInvalidValue;
   }
