@@ -45,6 +45,25 @@ def test_multi_sequence_steps():
     run_pair(cfg, w, dict(n_ctx=200, n_ubatch=40, n_seq_max=4), calls, TOL_BF16, "q8_0", "kvq8-multiseq")
 
 
+def test_lock_step_sequences_own_rows():
+    """12 sequences (prompts of 20..119 tokens, ubatches of 64), then three
+    lock-step steps of 12 tokens, one per sequence: no token sees another's
+    new cell, so the decode attention quantizes each token's own K/V rows
+    (9..32-token projections write them as float32).  Then a step whose two
+    tokens share a sequence (the separate quantization pass), and one more
+    lock-step step.  Every row's logits, cells and output rows checked."""
+    cfg, w = make_weights(SMALL64)
+    calls = [dict(tokens=tdf_synth.prompt(cfg, 50 + q, 20 + 9 * q), seq_ids=[[q]] * (20 + 9 * q)) for q in range(12)]
+    lock = lambda seed: dict(tokens=[int(x) for x in tdf_synth.prompt(cfg, seed, 12)], seq_ids=[[q] for q in range(12)],
+                             logits=np.ones(12, dtype=np.int8))
+    calls += [lock(70 + k) for k in range(3)]
+    calls.append(dict(tokens=[int(x) for x in tdf_synth.prompt(cfg, 80, 3)], seq_ids=[[4], [4], [9]],
+                      logits=np.ones(3, dtype=np.int8)))
+    calls.append(lock(81))
+    log("q8 cache lock-step own rows")
+    run_pair(cfg, w, dict(n_ctx=2048, n_ubatch=64, n_seq_max=16), calls, TOL_BF16, "q8_0", "kvq8-lockstep")
+
+
 def test_import_then_decode():
     """300 positions of float32 N(0,1) rows imported (quantized on both sides
     by the same rule from the same values), then decode steps."""
@@ -105,9 +124,9 @@ def test_llama8b_width_single_token_quantize():
     """8B-class widths (32 query heads, 8 KV heads of 128), two layers, Q8_0
     cache: a 600-token prompt in ubatches of 512 and 88 (the matrix-core
     projections write float32 rows that a separate pass quantizes), then four
-    single-token steps, whose QKV GEMV quantizes its own K/V rows in its
-    epilogue (192 blocks of 32 rows, each one 32-value block of a head's
-    row)."""
+    single-token steps, whose QKV GEMV writes the token's K/V rows as
+    float32 and whose decode attention quantizes them into the cell (the
+    block whose chunk holds the cell)."""
     cfg = dict(tdf_synth.CONFIGS["llama8b"])
     cfg, w = make_weights(cfg, layers=2)
     prompt = tdf_synth.prompt(cfg, 0, 600)

@@ -522,9 +522,29 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
     ksc = (const SRaw*)((const int8_t*)a.k_cache + (int64_t)a.Hkv * a.n_ctx * HD) + (int64_t)g * a.n_ctx;
     vsc = (const SRaw*)((const int8_t*)a.v_cache + (int64_t)a.Hkv * a.n_ctx * HD) + (int64_t)g * a.n_ctx;
   }
+  // Q8_0, tokens handing over their own K/V rows in float32: thread i takes
+  // element i of [K row | V row] of this head and token (requested with q),
+  // and the staging loop looks for the token's cell in this chunk
+  const bool own = Q8 && a.new_k != nullptr;  // block-uniform
+  int32_t slot = -1;
+  float xown = 0.f;
+  if (own) {
+    slot = a.new_slot[t];
+    const int i = min(tid, 2 * HD - 1);
+    const float* src = i < HD ? a.new_k + i : a.new_v + (i - HD);
+    xown = src[g * a.new_hs + (int64_t)t * HD];
+  }
+  int pos = -1;  // the cell's place in the chunk (at most one: a token sees a cell once)
   for (int e = tid; e < kCellStage; e += 256) {
     const int32_t v = cells[c_lo + min(e, span - 1)];
     cell_s[e] = v;  // entries past the span repeat its last cell
+    if (own && e < span && v == slot) pos = e;
+  }
+  __shared__ int pos_s[4];
+  if (own) {
+    const uint64_t hit = __ballot(pos >= 0);
+    const int p = __builtin_amdgcn_readlane(pos, hit ? (int)__builtin_ctzll(hit) : 0);
+    if (lane == 0) pos_s[wv] = hit ? p : -1;
   }
   // query operand: lane l holds head l % 16 (zero past G), dimensions
   // 32 kk + 8 (l / 16) .. + 8, scaled by 1/sqrt(HD), as a high part and the
@@ -548,6 +568,36 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
     }
   }
   __syncthreads();
+
+  // The chunk that holds the token's cell quantizes its rows by the Q8_0
+  // block rule (32 adjacent threads = one block), stores codes and scales in
+  // the cell, and keeps them in LDS for the tile that reads the cell: that
+  // tile takes them from there instead of from its loads.
+  __shared__ __attribute__((aligned(16))) int8_t oq_s[2][HD];      // K, V codes
+  __shared__ __attribute__((aligned(16))) uint16_t osc_s[2][NB];   // K, V scale bits
+  int otile = -1, orow = 0;  // tile and row of the cell in this chunk
+  if (own) {
+    const int p = max(max(pos_s[0], pos_s[1]), max(pos_s[2], pos_s[3]));
+    if (p >= 0) {  // block-uniform
+      otile = p >> 4;
+      orow = p & 15;
+      float amax = fabsf(xown);
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+      const uint16_t dbits = q8_scale_bits(amax);
+      const int8_t code = q8_code(xown, f16_to_f32(dbits));
+      if (tid < 2 * HD) {
+        const int which = tid / HD, i = tid % HD;
+        oq_s[which][i] = code;
+        if ((i & 31) == 0) osc_s[which][i / 32] = dbits;
+        int8_t* codes = (int8_t*)(which ? a.v_cache : a.k_cache);
+        const int64_t crow = (int64_t)g * a.n_ctx + slot;
+        codes[crow * HD + i] = code;
+        if ((i & 31) == 0) ((uint16_t*)(codes + (int64_t)a.Hkv * a.n_ctx * HD))[crow * NB + i / 32] = dbits;
+      }
+      __syncthreads();
+    }
+  }
 
   const int rg = lane / PR, pc = lane % PR;  // V loads: row group, 8-dimension piece
   const int hrow = (lane >> 4) * 4;          // heads hrow .. hrow + 3 in the score layout
@@ -588,6 +638,22 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
   }
   for (; tl < ntiles; tl += 4) {
     const int nt = min(tl + 4, ntiles - 1);  // next tile of this wave (clamped)
+    if constexpr (Q8) {
+      if (tl == otile) {  // wave-uniform: the token's own cell is row orow of this tile
+        const bool kr = (lane & 15) == orow;
+#pragma unroll
+        for (int kk = 0; kk < NKC; ++kk) {
+          const KRaw o = *(const KRaw*)&oq_s[0][kk * 32 + (lane >> 4) * 8];
+          kn[kk] = kr ? o : kn[kk];
+        }
+        const SRaw ko = *(const SRaw*)&osc_s[0][0], vo = *(const SRaw*)&osc_s[1][0];
+        ksr = kr ? ko : ksr;
+        vsr = kr ? vo : vsr;
+        const VRaw o = *(const VRaw*)&oq_s[1][pc * 8];
+#pragma unroll
+        for (int pi = 0; pi < CPL; ++pi) vn[pi] = rg * CPL + pi == orow ? o : vn[pi];
+      }
+    }
     // this tile's V rows into the wave's LDS tile (rows of VP elements), then
     // the next tile's V requested into the same registers
 #pragma unroll
@@ -876,6 +942,11 @@ static hipError_t attn_launch_hd(const AttnArgs& a, hipStream_t s) {
   // 16-bit and Q8_0 caches with head_dim 64 or 128: scores and value
   // products on the matrix cores (chunks of at most kCellStage cells)
   bool done = false;
+  // tokens' own rows handed over in float32: Q8_0 cache, the matrix-core
+  // kernel (the only one that quantizes them)
+  if (a.new_k && (!std::is_same<KvT, kv_q8>::value || !(HD == 64 || HD == 128) || a.chunk > kCellStage ||
+                  !a.new_v || !a.new_slot))
+    return hipErrorInvalidValue;
   if constexpr (!std::is_same<KvT, float>::value && (HD == 64 || HD == 128)) {
     if (a.chunk <= kCellStage) {
       switch (G) {

@@ -171,6 +171,15 @@ struct AttnArgs {
   float* out = nullptr;       // [T][H][hd] float32
   uint16_t* out_hi = nullptr; // optional bf16 pair
   uint16_t* out_lo = nullptr;
+  // Q8_0 cache on the matrix cores (optional): token t's own K and V rows
+  // arrive as float32 (head g at new_k / new_v + g * new_hs + t * hd) instead
+  // of in its cell new_slot[t]; the block whose chunk holds that cell
+  // quantizes them, stores them in the cell and uses them itself.  The caller
+  // guarantees that no token sees the cell of another token of the launch.
+  const float* new_k = nullptr;
+  const float* new_v = nullptr;
+  int64_t new_hs = 0;
+  const int32_t* new_slot = nullptr;
 };
 hipError_t launch_attention_decode(const AttnArgs& a, hipStream_t s);
 // Decode attention stages a block's cell indices in LDS; with 16-bit or Q8_0

@@ -163,7 +163,7 @@ struct tdf_context {
 
   // launch replay: one instantiated graph per decode ubatch shape
   bool use_graphs = true;
-  std::map<std::tuple<int, int, int, int, int, const void*, const void*, const void*, int, int, int, int>,
+  std::map<std::tuple<int, int, int, int, int, const void*, const void*, const void*, int, int, int, int, int>,
            hipGraphExec_t> graphs;
   int64_t n_graph_captures = 0, n_graph_replays = 0;
 
@@ -509,6 +509,9 @@ struct UbatchDev {
   const int32_t *tile_tokens = nullptr, *tile_off = nullptr, *tile_nvis = nullptr;
   int n_tiles = 0;
   bool sel_identity = false;  // selected rows are exactly 0..T-1
+  // the tokens' sequence sets are pairwise disjoint, so no token sees the
+  // cell of another token of the ubatch
+  bool own_rows = false;
   int attn_chunk = 64, attn_grid = 1;  // split-K decode attention: cells per split, splits launched
   int nvis_max = 0;
   // windowed layers: first visible list entry per token (n_lo), the shifted
@@ -609,20 +612,29 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     qa.k_cache = kv_k(c, l); qa.v_cache = kv_v(c, l);
     qa.kv_dtype = c->kv_dtype; qa.n_ctx = c->n_ctx; qa.head_dim = hd;
     qa.slots = u.slots; qa.pos = u.pos; qa.rope_cs = c->rope_cs;
-    // Q8_0 cache: a single token's GEMV quantizes its K/V blocks itself when
-    // its 32-row blocks fit on the compute units at once (each streams 32
-    // whole rows on one CU; measured decode 298.5 against 292.5 tok/s at 8B
-    // widths, 1048 against 1007 at 1B); otherwise float32 rows go to the
-    // staging area (row t of head h at [h][t]) and are quantized into their
-    // cells afterwards
-    const bool q8_fold = T == 1 && !big && (H + 2 * Hkv) * hd / 32 <= c->n_cu;
+    // Q8_0 cache: the projection writes float32 K/V rows to the staging area
+    // (row t of head h at [h][t]), and they are quantized into their cells
+    //  - with matrix-core decode attention, when no token sees another
+    //    token's cell (one token, or one token per sequence), by the
+    //    attention block whose chunk holds the cell (a single token's GEMV
+    //    keeps its 8-row blocks: 32-row quantizing blocks are 192 for 256 CUs
+    //    at 8B widths, 14.6 against 12.6 us; 32 lock-step sequences drop the
+    //    separate pass);
+    //  - for a single token otherwise, by the GEMV itself when its 32-row
+    //    blocks fit on the compute units at once (no staging);
+    //  - else by a separate pass.
+    const bool win = m->windowed[l] != 0;
+    const int dchunk = win ? u.attn_chunk_w : u.attn_chunk;
+    const bool q8_attn = c->kv_dtype == TDF_Q8_0 && T <= kDecodeMaxT && u.own_rows &&
+                         attn_decode_on_mfma(TDF_Q8_0, hd) && dchunk <= kDecodeCellStage;
+    const bool q8_fold = !q8_attn && T == 1 && !big && (H + 2 * Hkv) * hd / 32 <= c->n_cu;
     const bool kvq8 = c->kv_dtype == TDF_Q8_0 && !q8_fold;
     if (kvq8) {
       qa.k_cache = c->kv_stage; qa.v_cache = c->kv_stage + (size_t)Hkv * c->n_ubatch * hd;
       qa.kv_dtype = TDF_F32; qa.n_ctx = c->n_ubatch; qa.slots = c->iota;
     }
     if (int rc = run_linear(c, qa, big, TDF_OP_QKV)) return rc;
-    if (kvq8) {
+    if (kvq8 && !q8_attn) {
       ps = prof_begin(c, TDF_OP_QKV, big);
       TDF_HIP(launch_kv_quantize(c->kv_stage, c->kv_stage + (size_t)Hkv * c->n_ubatch * hd, hd,
                                  (int64_t)c->n_ubatch * hd, T, Hkv, hd, u.slots, kv_k(c, l), kv_v(c, l), c->n_ctx, s));
@@ -630,7 +642,6 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     }
     u_parts = 0;
 
-    const bool win = m->windowed[l] != 0;
     if (T > kDecodeMaxT && prefill_attention_supported(c->kv_dtype, hd)) {
       PrefillAttnArgs pa;
       pa.q = c->q;
@@ -669,8 +680,12 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
       at.list_off = win ? u.list_off_w : u.list_off;
       at.n_vis = win ? u.n_vis_w : u.n_vis;
       at.T = T; at.H = H; at.Hkv = Hkv; at.hd = hd; at.n_ctx = c->n_ctx;
-      at.chunk = win ? u.attn_chunk_w : u.attn_chunk;
+      at.chunk = dchunk;
       at.n_chunks = win ? u.attn_grid_w : u.attn_grid;
+      if (q8_attn) {
+        at.new_k = c->kv_stage; at.new_v = c->kv_stage + (size_t)Hkv * c->n_ubatch * hd;
+        at.new_hs = (int64_t)c->n_ubatch * hd; at.new_slot = u.slots;
+      }
       at.part_acc = c->part_acc; at.part_ml = c->part_ml;
       at.out = c->o;
       at.out_hi = big ? c->o_hi : nullptr;
@@ -776,7 +791,7 @@ static int run_graphed(tdf_context* c, const UbatchDev& u) {
   // part of the key as the integers' address is
   const auto key = std::make_tuple(u.T, u.R, u.n_list_writes, u.attn_chunk, u.attn_grid,
                                    (const void*)c->logits, (const void*)u.tokens, (const void*)u.list_writes,
-                                   u.out_row0, (int)u.sel_identity, u.attn_chunk_w, u.attn_grid_w);
+                                   u.out_row0, (int)u.sel_identity, u.attn_chunk_w, u.attn_grid_w, (int)u.own_rows);
   auto it = c->graphs.find(key);
   if (it == c->graphs.end()) {
     if (c->graphs.size() >= 64) {
@@ -952,6 +967,14 @@ extern "C" int32_t tdf_decode(tdf_context* c, const tdf_batch* b) {
     ud.T = T;
     ud.R = (int)sel.size();
     ud.sel_identity = ud.R == T;
+    {
+      uint64_t seen = 0;
+      ud.own_rows = true;
+      for (int i = 0; i < T; ++i) {
+        if (in.seq_mask[u0 + i] & seen) ud.own_rows = false;
+        seen |= in.seq_mask[u0 + i];
+      }
+    }
     ud.tokens = d32; ud.pos = d32 + T; ud.slots = d32 + 2 * T;
     ud.list_off = d32 + 3 * T; ud.n_vis = d32 + 4 * T; ud.sel = d32 + 5 * T;
     ud.list_writes = d64;
