@@ -325,7 +325,7 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(LinearArgs a, int M, int t
           }
         } else if (row_ok && col < Ntot) {
           float* o = a.out + (int64_t)row * a.ldo + col;
-          if (EPI == EPI_STORE) *o = y;
+          if (EPI == EPI_STORE) o[(int64_t)ks * M * a.ldo] = y;  // split ks: its own slab of M rows
           else if (ksplit == 1) *o += y;
           else atomicAdd(o, y);
         }
@@ -400,6 +400,17 @@ static hipError_t gemm_launch_t(const LinearArgs& a, hipStream_t s) {
     int ks = 1;
     while (ks < 8 && nkt % (ks * 2) == 0 && nkt / (ks * 2) >= 4 && b12 * ks < 512) ks *= 2;
     return gemm_launch_tile<EPI, KvT, 1, 2>(a, ks, s);
+  }
+  // QKV (RoPE and the cache write need whole sums, so no atomic adds): when
+  // 128x128 tiles are too few for the chip, K is split in two into float32
+  // slabs of the workspace and a second pass sums them and finishes
+  if (EPI == EPI_QKV && !q8 && a.split_ws && b22 < 384 && b22 * 2 >= 384 && nkt % 2 == 0 &&
+      (int64_t)2 * M * Ntot <= a.split_ws_floats) {
+    LinearArgs p = a;
+    p.epi = EPI_STORE; p.out = a.split_ws; p.ldo = Ntot;
+    const hipError_t e = gemm_launch_tile<EPI_STORE, float, 2, 2>(p, 2, s);
+    if (e != hipSuccess) return e;
+    return launch_split_epilogue(a, a.split_ws, 2, s);
   }
   if (b24 >= 384) return gemm_launch_tile<EPI, KvT, 2, 4>(a, 1, s);
   if (b22 >= 384) return gemm_launch_tile<EPI, KvT, 2, 2>(a, 1, s);

@@ -34,7 +34,8 @@ struct SkinnyArgs {
   LinearArgs a;
   int N = 0;        // stacked rows (SwiGLU: gate rows then up rows)
   int ksplit = 1, kslice = 0;
-  float* part = nullptr;  // [ksplit][32][N]
+  float* part = nullptr;  // [ksplit][tstride][N]
+  int tstride = 32;       // rows of one K slice's partials
 };
 
 // stacked row r: its matrix, row index in it and the matrix's row count
@@ -224,7 +225,7 @@ __global__ void __launch_bounds__(256) skinny_kernel(SkinnyArgs s) {
   // acc[r] <-> token (r/4)*8 + (lane/32)*4 + r%4, row rt*128 + w*32 + lane%32
   const int n = rt * 128 + w * 32 + (lane & 31);
   if (n >= s.N) return;
-  float* pp = s.part + (int64_t)ks * 32 * s.N + n;
+  float* pp = s.part + (int64_t)ks * s.tstride * s.N + n;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int t = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
@@ -244,7 +245,7 @@ __global__ void __launch_bounds__(256) skinny_epilogue_kernel(SkinnyArgs s) {
     for (int k0 = 0; k0 < s.ksplit; k0 += 8) {
       float v[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = s.part[((int64_t)min(k0 + k, s.ksplit - 1) * 32 + t) * s.N + n];
+      for (int k = 0; k < 8; ++k) v[k] = s.part[((int64_t)min(k0 + k, s.ksplit - 1) * s.tstride + t) * s.N + n];
 #pragma unroll
       for (int k = 0; k < 8; ++k) y = fmaf(v[k], k0 + k < s.ksplit ? 1.f : 0.f, y);
     }
@@ -323,7 +324,7 @@ __global__ void __launch_bounds__(kSkNormThreads) skinny_residual_norm_kernel(Sk
       for (int k0 = 0; k0 < s.ksplit; k0 += 8) {
         float4 v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = *(const float4*)&s.part[((int64_t)min(k0 + k, s.ksplit - 1) * 32 + t) * N + n];
+        for (int k = 0; k < 8; ++k) v[k] = *(const float4*)&s.part[((int64_t)min(k0 + k, s.ksplit - 1) * s.tstride + t) * N + n];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const float on = k0 + k < s.ksplit ? 1.f : 0.f;
@@ -369,6 +370,64 @@ bool skinny_supported(const LinearArgs& a) {
          (int64_t)N * 32 <= kSkinnyPartFloats && (a.epi != EPI_QKV || (a.n0 % 2 == 0 && a.n1 % 2 == 0));
 }
 
+// Pass 2 of a QKV GEMM split over K in two: one thread per 4 adjacent
+// columns of a token (two RoPE pairs inside one head), one float4 from each
+// slice, then the QKV epilogue of the other linear kernels
+template <typename KvT>
+__global__ void __launch_bounds__(256) split2_qkv_epilogue_kernel(SkinnyArgs s) {
+  const LinearArgs& a = s.a;
+  const int NQ = s.N / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.T * NQ) return;
+  const int t = (int)(i / NQ), n = 4 * (int)(i % NQ);
+  const float4 p0 = *(const float4*)&s.part[(int64_t)t * s.N + n];
+  const float4 p1 = *(const float4*)&s.part[((int64_t)s.tstride + t) * s.N + n];
+  const float y[4] = {p0.x + p1.x, p0.y + p1.y, p0.z + p1.z, p0.w + p1.w};
+  const int hd = a.head_dim;
+  if (n < a.n0 + a.n1) {
+    const int lr = n < a.n0 ? n : n - a.n0;
+    float z[4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float2 cs = a.rope_cs[(int64_t)t * (hd >> 1) + ((lr + 2 * q) % hd >> 1)];
+      z[2 * q] = y[2 * q] * cs.x - y[2 * q + 1] * cs.y;
+      z[2 * q + 1] = y[2 * q] * cs.y + y[2 * q + 1] * cs.x;
+    }
+    if (n < a.n0) {
+      *(float4*)&a.q_out[(int64_t)t * a.n0 + lr] = make_float4(z[0], z[1], z[2], z[3]);
+    } else {
+      const int64_t ci = ((int64_t)(lr / hd) * a.n_ctx + a.slots[t]) * hd + (lr % hd);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) KvStore<KvT>::store((typename KvStore<KvT>::T*)a.k_cache, ci + q, z[q]);
+    }
+  } else {
+    const int lr = n - a.n0 - a.n1;
+    const int64_t ci = ((int64_t)(lr / hd) * a.n_ctx + a.slots[t]) * hd + (lr % hd);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) KvStore<KvT>::store((typename KvStore<KvT>::T*)a.v_cache, ci + q, y[q]);
+  }
+}
+
+// Pass 2: sum the K slices of s.part and apply the layer's epilogue (one
+// thread per output, or per RoPE pair)
+static hipError_t slices_epilogue(const SkinnyArgs& s, hipStream_t st) {
+  const LinearArgs& a = s.a;
+  const int64_t n_thr = a.epi == EPI_SWIGLU ? (int64_t)a.T * a.n0 : (int64_t)a.T * ((s.N + 1) / 2);
+  const unsigned blocks = (unsigned)((n_thr + 255) / 256);
+  switch (a.epi) {
+    case EPI_STORE: skinny_epilogue_kernel<EPI_STORE, float><<<blocks, 256, 0, st>>>(s); break;
+    case EPI_RESIDUAL: skinny_epilogue_kernel<EPI_RESIDUAL, float><<<blocks, 256, 0, st>>>(s); break;
+    case EPI_SWIGLU: skinny_epilogue_kernel<EPI_SWIGLU, float><<<blocks, 256, 0, st>>>(s); break;
+    case EPI_QKV:
+      if (a.kv_dtype == TDF_BF16) skinny_epilogue_kernel<EPI_QKV, kv_bf16><<<blocks, 256, 0, st>>>(s);
+      else if (a.kv_dtype == TDF_F16) skinny_epilogue_kernel<EPI_QKV, kv_f16><<<blocks, 256, 0, st>>>(s);
+      else skinny_epilogue_kernel<EPI_QKV, float><<<blocks, 256, 0, st>>>(s);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_linear_skinny(const LinearArgs& a, float* part, hipStream_t st) {
   if (!skinny_supported(a)) return hipErrorInvalidValue;
   SkinnyArgs s;
@@ -400,20 +459,26 @@ hipError_t launch_linear_skinny(const LinearArgs& a, float* part, hipStream_t st
     skinny_residual_norm_kernel<<<a.T, kSkNormThreads, 0, st>>>(s);
     return hipGetLastError();
   }
-  const int64_t n_thr = a.epi == EPI_SWIGLU ? (int64_t)a.T * a.n0 : (int64_t)a.T * ((s.N + 1) / 2);
-  const unsigned blocks = (unsigned)((n_thr + 255) / 256);
-  switch (a.epi) {
-    case EPI_STORE: skinny_epilogue_kernel<EPI_STORE, float><<<blocks, 256, 0, st>>>(s); break;
-    case EPI_RESIDUAL: skinny_epilogue_kernel<EPI_RESIDUAL, float><<<blocks, 256, 0, st>>>(s); break;
-    case EPI_SWIGLU: skinny_epilogue_kernel<EPI_SWIGLU, float><<<blocks, 256, 0, st>>>(s); break;
-    case EPI_QKV:
-      if (a.kv_dtype == TDF_BF16) skinny_epilogue_kernel<EPI_QKV, kv_bf16><<<blocks, 256, 0, st>>>(s);
-      else if (a.kv_dtype == TDF_F16) skinny_epilogue_kernel<EPI_QKV, kv_f16><<<blocks, 256, 0, st>>>(s);
-      else skinny_epilogue_kernel<EPI_QKV, float><<<blocks, 256, 0, st>>>(s);
-      break;
-    default: return hipErrorInvalidValue;
+  return slices_epilogue(s, st);
+}
+
+hipError_t launch_split_epilogue(const LinearArgs& a, float* part, int ksplit, hipStream_t st) {
+  if (a.T <= 0 || ksplit < 1 || a.norm_out_g || (a.epi == EPI_QKV && (a.n0 % 2 || a.n1 % 2)))
+    return hipErrorInvalidValue;
+  SkinnyArgs s;
+  s.a = a;
+  s.N = a.epi == EPI_SWIGLU ? 2 * a.n0 : a.n0 + a.n1 + a.n2;
+  s.part = part;
+  s.ksplit = ksplit;
+  s.tstride = a.T;
+  if (a.epi == EPI_QKV && ksplit == 2 && a.n0 % 4 == 0 && a.n1 % 4 == 0 && a.n2 % 4 == 0 && a.head_dim % 4 == 0) {
+    const unsigned blocks = (unsigned)(((int64_t)a.T * (s.N / 4) + 255) / 256);
+    if (a.kv_dtype == TDF_BF16) split2_qkv_epilogue_kernel<kv_bf16><<<blocks, 256, 0, st>>>(s);
+    else if (a.kv_dtype == TDF_F16) split2_qkv_epilogue_kernel<kv_f16><<<blocks, 256, 0, st>>>(s);
+    else split2_qkv_epilogue_kernel<float><<<blocks, 256, 0, st>>>(s);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  return slices_epilogue(s, st);
 }
 
 }  // namespace tdf

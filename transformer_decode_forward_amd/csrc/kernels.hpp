@@ -68,6 +68,10 @@ struct LinearArgs {
   const int32_t* slots = nullptr;  // [T] cell of each token
   const int32_t* pos = nullptr;    // [T] position of each token
   const float2* rope_cs = nullptr; // [T][head_dim/2] (cos, sin) of pos * theta^(-2i/head_dim)
+  // optional float32 workspace of the matrix-core GEMM (K-split partials of
+  // an epilogue that needs whole sums)
+  float* split_ws = nullptr;
+  int64_t split_ws_floats = 0;
 };
 
 hipError_t launch_linear_gemv(const LinearArgs& a, hipStream_t s);
@@ -81,6 +85,8 @@ bool skinny_supported(const LinearArgs& a);
 // the residual pass can also write the next RMSNorm (norm_out_g)
 bool skinny_norm_supported(const LinearArgs& a);
 hipError_t launch_linear_skinny(const LinearArgs& a, float* part, hipStream_t s);
+// the epilogue of `a` over K-split partials part[ksplit][a.T][N] (their sum)
+hipError_t launch_split_epilogue(const LinearArgs& a, float* part, int ksplit, hipStream_t s);
 
 // x[t][:] = E[token[t]][:] (to float32); with g set also u = g * x and
 // ssp[t * stride] = sum x^2 (one partial per row).  n_rows: rows of the

@@ -140,6 +140,8 @@ struct tdf_context {
   float* logits = nullptr;          // [cap][V]
   int32_t* d_tok = nullptr;         // [cap]
   float* skinny_part = nullptr;     // K-split partials of the 9..32-token linear layers
+  float* qkv_split = nullptr;       // K-split partials of the ubatch QKV GEMM [2][n_ubatch][(H + 2 Hkv) hd]
+  int64_t qkv_split_floats = 0;
   float* amax_v = nullptr;          // [cap][argmax_splits(V)] partial maxima
   int32_t* amax_i = nullptr;        // [cap][argmax_splits(V)] their indices
   int32_t* h_tok = nullptr;         // pinned [cap]
@@ -454,6 +456,10 @@ extern "C" tdf_context* tdf_context_create(const tdf_model* m, const tdf_context
   A((void**)&c->part_acc, c->part_rows * hd * 4);
   A((void**)&c->part_ml, c->part_rows * 2 * 4);
   if (U > kGemvMaxT) A((void**)&c->skinny_part, (size_t)kSkinnyPartFloats * 4);
+  if (U > kDecodeMaxT && m->hp.weight_dtype == TDF_BF16) {
+    c->qkv_split_floats = (int64_t)2 * U * (H + 2 * Hkv) * hd;
+    A((void**)&c->qkv_split, (size_t)c->qkv_split_floats * 4);
+  }
   if (c->kv_dtype == TDF_Q8_0) {
     A((void**)&c->kv_stage, (size_t)2 * Hkv * U * hd * 4);
     A((void**)&c->iota, (size_t)U * 4);
@@ -612,6 +618,7 @@ static int forward_ubatch(tdf_context* c, const UbatchDev& u) {
     qa.k_cache = kv_k(c, l); qa.v_cache = kv_v(c, l);
     qa.kv_dtype = c->kv_dtype; qa.n_ctx = c->n_ctx; qa.head_dim = hd;
     qa.slots = u.slots; qa.pos = u.pos; qa.rope_cs = c->rope_cs;
+    qa.split_ws = c->qkv_split; qa.split_ws_floats = c->qkv_split_floats;
     // Q8_0 cache: the projection writes float32 K/V rows to the staging area
     // (row t of head h at [h][t]), and they are quantized into their cells
     //  - with matrix-core decode attention, when no token sees another
