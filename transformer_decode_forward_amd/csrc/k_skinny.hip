@@ -370,42 +370,110 @@ bool skinny_supported(const LinearArgs& a) {
          (int64_t)N * 32 <= kSkinnyPartFloats && (a.epi != EPI_QKV || (a.n0 % 2 == 0 && a.n1 % 2 == 0));
 }
 
-// Pass 2 of a QKV GEMM split over K in two: one thread per 4 adjacent
-// columns of a token (two RoPE pairs inside one head), one float4 from each
-// slice, then the QKV epilogue of the other linear kernels
-template <typename KvT>
-__global__ void __launch_bounds__(256) split2_qkv_epilogue_kernel(SkinnyArgs s) {
+// Pass 2 with four adjacent columns of a token per thread (16-byte loads of
+// every K slice's partials in batches of KB, clamped and weighted 0 past the
+// last slice; the same sum order as skinny_epilogue_kernel), then the
+// layer's epilogue: SwiGLU on columns f..f+3 of gate and up, or two RoPE
+// pairs inside one head, or store / residual add.
+template <int EPI, typename KvT, int KB>
+__global__ void __launch_bounds__(256) slices4_epilogue_kernel(SkinnyArgs s) {
   const LinearArgs& a = s.a;
-  const int NQ = s.N / 4;
+  const int NC = EPI == EPI_SWIGLU ? a.n0 : s.N;  // output columns
+  const int NQ = NC / 4;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)a.T * NQ) return;
   const int t = (int)(i / NQ), n = 4 * (int)(i % NQ);
-  const float4 p0 = *(const float4*)&s.part[(int64_t)t * s.N + n];
-  const float4 p1 = *(const float4*)&s.part[((int64_t)s.tstride + t) * s.N + n];
-  const float y[4] = {p0.x + p1.x, p0.y + p1.y, p0.z + p1.z, p0.w + p1.w};
-  const int hd = a.head_dim;
-  if (n < a.n0 + a.n1) {
-    const int lr = n < a.n0 ? n : n - a.n0;
-    float z[4];
+  auto total4 = [&](int c, float* y) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const float2 cs = a.rope_cs[(int64_t)t * (hd >> 1) + ((lr + 2 * q) % hd >> 1)];
-      z[2 * q] = y[2 * q] * cs.x - y[2 * q + 1] * cs.y;
-      z[2 * q + 1] = y[2 * q] * cs.y + y[2 * q + 1] * cs.x;
+    for (int q = 0; q < 4; ++q) y[q] = 0.f;
+    for (int k0 = 0; k0 < s.ksplit; k0 += KB) {
+      float4 v[KB];
+#pragma unroll
+      for (int k = 0; k < KB; ++k)
+        v[k] = *(const float4*)&s.part[((int64_t)min(k0 + k, s.ksplit - 1) * s.tstride + t) * s.N + c];
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const float w = k0 + k < s.ksplit ? 1.f : 0.f;
+        y[0] = fmaf(v[k].x, w, y[0]); y[1] = fmaf(v[k].y, w, y[1]);
+        y[2] = fmaf(v[k].z, w, y[2]); y[3] = fmaf(v[k].w, w, y[3]);
+      }
     }
-    if (n < a.n0) {
-      *(float4*)&a.q_out[(int64_t)t * a.n0 + lr] = make_float4(z[0], z[1], z[2], z[3]);
+  };
+  float y[4];
+  total4(n, y);
+  if (EPI == EPI_SWIGLU) {
+    float u[4], v[4];
+    total4(a.n0 + n, u);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = silu(y[q]) * u[q];
+    const int64_t o = (int64_t)t * a.ldo + n;
+    if (a.out) *(float4*)&a.out[o] = make_float4(v[0], v[1], v[2], v[3]);
+    if (a.out_hi) {
+      uint16_t hi[4], lo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) split_bf16(v[q], hi[q], lo[q]);
+      *(uint2*)&a.out_hi[o] = make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+      *(uint2*)&a.out_lo[o] = make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+    }
+  } else if (EPI == EPI_STORE) {
+    *(float4*)&a.out[(int64_t)t * a.ldo + n] = make_float4(y[0], y[1], y[2], y[3]);
+  } else if (EPI == EPI_RESIDUAL) {
+    float4* xo = (float4*)&a.out[(int64_t)t * a.ldo + n];
+    const float4 x = *xo;
+    *xo = make_float4(x.x + y[0], x.y + y[1], x.z + y[2], x.w + y[3]);
+  } else if (EPI == EPI_QKV) {
+    const int hd = a.head_dim;
+    if (n < a.n0 + a.n1) {
+      const int lr = n < a.n0 ? n : n - a.n0;
+      float z[4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float2 cs = a.rope_cs[(int64_t)t * (hd >> 1) + (((lr + 2 * q) % hd) >> 1)];
+        z[2 * q] = y[2 * q] * cs.x - y[2 * q + 1] * cs.y;
+        z[2 * q + 1] = y[2 * q] * cs.y + y[2 * q + 1] * cs.x;
+      }
+      if (n < a.n0) {
+        *(float4*)&a.q_out[(int64_t)t * a.n0 + lr] = make_float4(z[0], z[1], z[2], z[3]);
+      } else {
+        const int64_t ci = ((int64_t)(lr / hd) * a.n_ctx + a.slots[t]) * hd + (lr % hd);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) KvStore<KvT>::store((typename KvStore<KvT>::T*)a.k_cache, ci + q, z[q]);
+      }
     } else {
+      const int lr = n - a.n0 - a.n1;
       const int64_t ci = ((int64_t)(lr / hd) * a.n_ctx + a.slots[t]) * hd + (lr % hd);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) KvStore<KvT>::store((typename KvStore<KvT>::T*)a.k_cache, ci + q, z[q]);
+      for (int q = 0; q < 4; ++q) KvStore<KvT>::store((typename KvStore<KvT>::T*)a.v_cache, ci + q, y[q]);
     }
-  } else {
-    const int lr = n - a.n0 - a.n1;
-    const int64_t ci = ((int64_t)(lr / hd) * a.n_ctx + a.slots[t]) * hd + (lr % hd);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) KvStore<KvT>::store((typename KvStore<KvT>::T*)a.v_cache, ci + q, y[q]);
   }
+}
+
+// four columns per thread fit: every column count, the row pitch and (QKV)
+// the head size are multiples of 4
+static bool slices4_fit(const SkinnyArgs& s) {
+  const LinearArgs& a = s.a;
+  if (a.epi == EPI_QKV) return a.n0 % 4 == 0 && a.n1 % 4 == 0 && a.n2 % 4 == 0 && a.head_dim % 4 == 0;
+  if (a.epi == EPI_SWIGLU) return a.n0 % 4 == 0 && a.ldo % 4 == 0;
+  return s.N % 4 == 0 && a.ldo % 4 == 0;
+}
+
+template <int KB>
+static hipError_t slices4_epilogue(const SkinnyArgs& s, hipStream_t st) {
+  const LinearArgs& a = s.a;
+  const int NC = a.epi == EPI_SWIGLU ? a.n0 : s.N;
+  const unsigned blocks = (unsigned)(((int64_t)a.T * (NC / 4) + 255) / 256);
+  switch (a.epi) {
+    case EPI_STORE: slices4_epilogue_kernel<EPI_STORE, float, KB><<<blocks, 256, 0, st>>>(s); break;
+    case EPI_RESIDUAL: slices4_epilogue_kernel<EPI_RESIDUAL, float, KB><<<blocks, 256, 0, st>>>(s); break;
+    case EPI_SWIGLU: slices4_epilogue_kernel<EPI_SWIGLU, float, KB><<<blocks, 256, 0, st>>>(s); break;
+    case EPI_QKV:
+      if (a.kv_dtype == TDF_BF16) slices4_epilogue_kernel<EPI_QKV, kv_bf16, KB><<<blocks, 256, 0, st>>>(s);
+      else if (a.kv_dtype == TDF_F16) slices4_epilogue_kernel<EPI_QKV, kv_f16, KB><<<blocks, 256, 0, st>>>(s);
+      else slices4_epilogue_kernel<EPI_QKV, float, KB><<<blocks, 256, 0, st>>>(s);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // Pass 2: sum the K slices of s.part and apply the layer's epilogue (one
@@ -459,6 +527,7 @@ hipError_t launch_linear_skinny(const LinearArgs& a, float* part, hipStream_t st
     skinny_residual_norm_kernel<<<a.T, kSkNormThreads, 0, st>>>(s);
     return hipGetLastError();
   }
+  if (slices4_fit(s)) return slices4_epilogue<8>(s, st);
   return slices_epilogue(s, st);
 }
 
@@ -471,13 +540,7 @@ hipError_t launch_split_epilogue(const LinearArgs& a, float* part, int ksplit, h
   s.part = part;
   s.ksplit = ksplit;
   s.tstride = a.T;
-  if (a.epi == EPI_QKV && ksplit == 2 && a.n0 % 4 == 0 && a.n1 % 4 == 0 && a.n2 % 4 == 0 && a.head_dim % 4 == 0) {
-    const unsigned blocks = (unsigned)(((int64_t)a.T * (s.N / 4) + 255) / 256);
-    if (a.kv_dtype == TDF_BF16) split2_qkv_epilogue_kernel<kv_bf16><<<blocks, 256, 0, st>>>(s);
-    else if (a.kv_dtype == TDF_F16) split2_qkv_epilogue_kernel<kv_f16><<<blocks, 256, 0, st>>>(s);
-    else split2_qkv_epilogue_kernel<float><<<blocks, 256, 0, st>>>(s);
-    return hipGetLastError();
-  }
+  if (slices4_fit(s)) return ksplit <= 2 ? slices4_epilogue<2>(s, st) : slices4_epilogue<8>(s, st);
   return slices_epilogue(s, st);
 }
 
