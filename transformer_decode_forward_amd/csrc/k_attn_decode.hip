@@ -503,16 +503,26 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
   const int g = blockIdx.x % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int t, j;
-  if (!decode_item(a.n_vis, a.T, a.chunk, blockIdx.x / a.Hkv, lane, t, j)) return;
-  t = __builtin_amdgcn_readfirstlane(t);
-  j = __builtin_amdgcn_readfirstlane(j);
+  if (a.T == 1) {
+    // one token: the dense list is the chunk order itself, so the token's
+    // count and list offset are requested together below (one round trip
+    // fewer before the cell indices)
+    t = 0;
+    j = blockIdx.x / a.Hkv;
+  } else {
+    if (!decode_item(a.n_vis, a.T, a.chunk, blockIdx.x / a.Hkv, lane, t, j)) return;
+    t = __builtin_amdgcn_readfirstlane(t);
+    j = __builtin_amdgcn_readfirstlane(j);
+  }
   if (j >= a.n_chunks) return;  // cells past the launch's split count are not covered
   const int nvis = a.n_vis[t];
+  const int loff = a.list_off[t];
   const int c_lo = j * a.chunk;
+  if (c_lo >= nvis) return;  // a chunk past the token's cells (one token)
   const int c_hi = min(nvis, c_lo + a.chunk);
   const int span = c_hi - c_lo;  // 1 .. kCellStage (checked at launch)
   const int ntiles = (span + 15) >> 4;
-  const int32_t* cells = a.cell_list + a.list_off[t];
+  const int32_t* cells = a.cell_list + loff;
   const ST* kc = (const ST*)a.k_cache + (int64_t)g * a.n_ctx * HD;
   const ST* vc = (const ST*)a.v_cache + (int64_t)g * a.n_ctx * HD;
   // Q8_0 scale rows of this kv head (NB fp16 per cell)
