@@ -356,8 +356,9 @@ static hipError_t gemm_launch_tile(const LinearArgs& a, int ksplit, hipStream_t 
   return hipGetLastError();
 }
 
-// Tile choice.  Plain epilogues: the largest of 128x256, 128x128, 64x128
-// that gives at least 384 blocks (1.5 per CU).  Residual epilogue: the
+// Tile choice.  Plain epilogues: 64x128 for at most 64 rows, else the
+// largest of 128x256, 128x128, 64x128 that gives at least 384 blocks (1.5
+// per CU).  Residual epilogue: the
 // largest tile that reaches 512 blocks with a K split (2, 4) that still
 // leaves each split at least 48 K tiles; failing that, the smallest K split
 // (1, 2, 4, 8) for which some tile reaches 512 blocks, with the largest such
@@ -412,6 +413,11 @@ static hipError_t gemm_launch_t(const LinearArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     return launch_split_epilogue(a, a.split_ws, 2, s);
   }
+  // at most 64 rows (the 32-row LM head of a multi-sequence step, small
+  // ubatches): 64-row tiles, so that 128-row tiles do not spend three
+  // quarters of their matrix-core work on padding rows (LM head of 32 rows
+  // at 8B widths: 32 sequences 3745-3752 -> 3756-3763 tok/s on one box)
+  if (M <= 64 && b12 >= 384) return gemm_launch_tile<EPI, KvT, 1, 2>(a, 1, s);
   if (b24 >= 384) return gemm_launch_tile<EPI, KvT, 2, 4>(a, 1, s);
   if (b22 >= 384) return gemm_launch_tile<EPI, KvT, 2, 2>(a, 1, s);
   return gemm_launch_tile<EPI, KvT, 1, 2>(a, 1, s);
