@@ -87,6 +87,33 @@ def test_import_then_decode():
         check_token(gc.argmax_ith(0), ro.logits[0], "kvq8 import")
 
 
+def test_import_long_context_own_rows():
+    """20000 imported positions (8 KV heads of 128, 2 query heads each),
+    then three single-token steps: 1024-cell chunks (the largest a block
+    stages), the token's own K/V rows quantized by the block whose partial
+    last chunk holds its cell, 20 chunks merged."""
+    import transformer_decode_forward_amd as tdf
+    from transformer_decode_forward_amd.device import to_device
+    cfg0 = dict(SMALL, n_embd=256, n_head=16, n_head_kv=8, head_dim=128, n_ff=256, seed=77)
+    cfg, w = make_weights(cfg0)
+    L, P, n_ctx = cfg["n_layer"], 20000, 20480
+    ks = [tdf_synth.kv_fill(cfg, l, "k", 0, P, "f32") for l in range(L)]
+    vs = [tdf_synth.kv_fill(cfg, l, "v", 0, P, "f32") for l in range(L)]
+    gc = tdf.Context(device_model(cfg, w), n_ctx=n_ctx, kv_dtype="q8_0")
+    kd = [to_device(k) for k in ks]
+    vd = [to_device(v) for v in vs]
+    assert gc.kv_import(0, 0, P, [t.data_ptr() for t in kd], [t.data_ptr() for t in vd]) == 0
+    oc = OracleContext(oracle_model(cfg, w), n_ctx=n_ctx, kv_dtype="q8_0")
+    assert oc.kv_import(0, 0, P, ks, vs) == 0
+    log("q8 cache 20k imported cells, single-token steps")
+    for k, t in enumerate(tdf_synth.prompt(cfg, 5, 3)):
+        assert gc.decode([int(t)]) == 0, tdf.tdf_last_error()
+        ro = oc.decode([int(t)])
+        assert gc.last_slots() == ro.slots
+        check_logits(gc.logits_ith(0), ro.logits[0], TOL_BF16, f"kvq8 long own rows step {k}")
+        check_token(gc.argmax_ith(0), ro.logits[0], f"kvq8 long own rows step {k}")
+
+
 def test_drop_and_shift_then_decode():
     """Drop positions [0, 30) of a 100-token prompt, shift the rest down by 30
     (the stored keys rotated and re-quantized), then 5 steps."""
