@@ -421,12 +421,14 @@ __device__ __forceinline__ float row16_sum(float v) { return group_sum<16>(v); }
 // it; items of (nearly) equal size in dispatch order keep the engines evenly
 // loaded, and the shorter partial chunks fill the end of the launch.  Every
 // wave of a block computes the same result; false past the last item.
-__device__ __forceinline__ bool decode_item(const int32_t* n_vis, int T, int chunk, int item, int lane,
-                                            int& t_out, int& j_out) {
+__device__ __forceinline__ bool decode_item(const int32_t* n_vis, const int32_t* list_off, int T, int chunk,
+                                            int item, int lane, int& t_out, int& j_out, int& off_out) {
   int base = 0;  // whole chunks of the tokens before this group of 64
 #pragma unroll 1
   for (int t0 = 0; t0 < T; t0 += 64) {
+    // the tokens' list offsets ride with their counts (one round trip)
     const int nv = t0 + lane < T ? n_vis[t0 + lane] : 0;
+    const int lo = list_off[min(t0 + lane, T - 1)];
     const int full = nv / chunk;
     int incl = full;
 #pragma unroll
@@ -439,6 +441,7 @@ __device__ __forceinline__ bool decode_item(const int32_t* n_vis, int T, int chu
       const int tl = __builtin_ctzll(__ballot(base + incl > item));
       t_out = t0 + tl;
       j_out = item - base - __shfl(incl - full, tl);
+      off_out = __shfl(lo, tl);
       return true;
     }
     base += tot;
@@ -447,6 +450,7 @@ __device__ __forceinline__ bool decode_item(const int32_t* n_vis, int T, int chu
 #pragma unroll 1
   for (int t0 = 0; t0 < T; t0 += 64) {
     const int nv = t0 + lane < T ? n_vis[t0 + lane] : 0;
+    const int lo = list_off[min(t0 + lane, T - 1)];
     const int part = nv % chunk != 0 ? 1 : 0;
     int incl = part;
 #pragma unroll
@@ -459,6 +463,7 @@ __device__ __forceinline__ bool decode_item(const int32_t* n_vis, int T, int chu
       const int tl = __builtin_ctzll(__ballot(incl > rel));
       t_out = t0 + tl;
       j_out = __shfl(nv / chunk, tl);
+      off_out = __shfl(lo, tl);
       return true;
     }
     rel -= tot;
@@ -502,21 +507,22 @@ __global__ void __launch_bounds__(256) attn_decode_mfma_kernel(AttnArgs a) {
   // work item
   const int g = blockIdx.x % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int t, j;
+  int t, j, loff;
   if (a.T == 1) {
     // one token: the dense list is the chunk order itself, so the token's
     // count and list offset are requested together below (one round trip
     // fewer before the cell indices)
     t = 0;
     j = blockIdx.x / a.Hkv;
+    loff = a.list_off[0];
   } else {
-    if (!decode_item(a.n_vis, a.T, a.chunk, blockIdx.x / a.Hkv, lane, t, j)) return;
+    if (!decode_item(a.n_vis, a.list_off, a.T, a.chunk, blockIdx.x / a.Hkv, lane, t, j, loff)) return;
     t = __builtin_amdgcn_readfirstlane(t);
     j = __builtin_amdgcn_readfirstlane(j);
+    loff = __builtin_amdgcn_readfirstlane(loff);
   }
   if (j >= a.n_chunks) return;  // cells past the launch's split count are not covered
   const int nvis = a.n_vis[t];
-  const int loff = a.list_off[t];
   const int c_lo = j * a.chunk;
   if (c_lo >= nvis) return;  // a chunk past the token's cells (one token)
   const int c_hi = min(nvis, c_lo + a.chunk);
