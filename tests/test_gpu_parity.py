@@ -230,3 +230,45 @@ def test_mid_size_ubatches_matrix_cores_streaming(kv_dtype):
         calls.append(dict(tokens=tdf_synth.prompt(cfg, 50 + k, n), seq_ids=[[j % 3] for j in range(n)],
                           logits=np.ones(n, dtype=np.int8)))
     run_pair(cfg, w, dict(n_ctx=512, n_ubatch=64, n_seq_max=3), calls, TOL_BF16, kv_dtype, "mid ubatch")
+
+
+def _lock_step_calls(cfg, n_seq, seed, base_len, step_len):
+    """n_seq sequences prefilled in their own calls, then two lock-step steps
+    of one token per sequence, a step whose three tokens share sequences, and
+    one more lock-step step; every row's logits in the steps."""
+    calls = [dict(tokens=tdf_synth.prompt(cfg, seed + q, base_len + step_len * q), seq_ids=[[q]] * (base_len + step_len * q))
+             for q in range(n_seq)]
+    lock = lambda k: dict(tokens=[int(x) for x in tdf_synth.prompt(cfg, seed + 100 + k, n_seq)],
+                          seq_ids=[[q] for q in range(n_seq)], logits=np.ones(n_seq, dtype=np.int8))
+    calls += [lock(0), lock(1)]
+    calls.append(dict(tokens=[int(x) for x in tdf_synth.prompt(cfg, seed + 150, 3)], seq_ids=[[1], [1], [n_seq - 1]],
+                      logits=np.ones(3, dtype=np.int8)))
+    calls.append(lock(2))
+    return calls
+
+
+@pytest.mark.parametrize("kv_dtype,hd", [("bf16", 64), ("f16", 64), ("bf16", 128)], ids=["bf16-hd64", "f16-hd64", "bf16-hd128"])
+def test_lock_step_one_token_per_sequence(kv_dtype, hd):
+    """12 sequences (prompts of 20..119 tokens, ubatches of 64), then
+    lock-step steps of 12 tokens, one per sequence (the 9..32-token
+    matrix-core projections with their K-split epilogue passes, the decode
+    attention over 12 separate cell lists), with a step whose tokens share a
+    sequence between them; every row's logits."""
+    from test_gpu_swa import SMALL64
+    cfg0 = SMALL64 if hd == 64 else dict(SMALL, n_embd=256, n_head=8, n_head_kv=2, head_dim=128, n_ff=256, seed=41)
+    cfg, w = make_weights(cfg0)
+    log(f"lock-step, one token per sequence: {kv_dtype} cache, head_dim {hd}")
+    run_pair(cfg, w, dict(n_ctx=2048, n_ubatch=64, n_seq_max=16), _lock_step_calls(cfg, 12, 300, 20, 9), TOL_BF16,
+             kv_dtype, f"lockstep-{kv_dtype}-hd{hd}")
+
+
+def test_llama8b_width_lock_step_one_token_per_sequence():
+    """8B widths (32 query heads, 8 KV heads of 128), two layers: 16
+    sequences of 40..115 tokens, then lock-step steps of 16 tokens, one per
+    sequence (the 9..32-token projections at full width), with a
+    shared-sequence step between them; every row's logits."""
+    cfg = dict(tdf_synth.CONFIGS["llama8b"])
+    cfg, w = make_weights(cfg, layers=2)
+    log("8B widths, 16 lock-step sequences")
+    run_pair(cfg, w, dict(n_ctx=2560, n_ubatch=512, n_seq_max=16), _lock_step_calls(cfg, 16, 400, 40, 5), TOL_BF16,
+             "bf16", "lockstep-8b-2L")
