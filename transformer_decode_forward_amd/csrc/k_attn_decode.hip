@@ -989,6 +989,59 @@ static hipError_t attn_launch_hd(const AttnArgs& a, hipStream_t s) {
   return launch_attention_merge(a, s);
 }
 
+// Merge of at most 8 splits with one wave per (token, head) pair, four
+// pairs per block (the prefill's many pairs: half the waves of the block
+// form, no LDS or barrier).  Lane i takes dimensions DPL i .. + DPL; the
+// splits' maxima and sums sit in lanes 0 .. nch-1.  The same operations in
+// the same order as attn_merge_kernel (wave reductions of the maxima and of
+// the l w products, then the weighted sum split by split).
+template <int HD>
+__global__ void __launch_bounds__(256) attn_merge_wave_kernel(AttnArgs a) {
+  constexpr int DPL = HD / 64;  // 1 or 2
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= a.T * a.H) return;  // wave-uniform
+  const int t = pair / a.H, h = pair % a.H;
+  const int nc = a.n_chunks;  // splits launched (>= the token's count), at most 8
+  const int64_t base = ((int64_t)t * a.H + h) * nc;
+  // every split's accumulators and the maxima / sums, requested together
+  float v[8][DPL];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float* p = a.part_acc + (base + min(j, nc - 1)) * HD + lane * DPL;
+    if constexpr (DPL == 2) {
+      const float2 x = *(const float2*)p;
+      v[j][0] = x.x; v[j][1] = x.y;
+    } else {
+      v[j][0] = *p;
+    }
+  }
+  const float2 ml = *(const float2*)&a.part_ml[(base + min(lane, nc - 1)) * 2];
+  const int nch = (a.n_vis[t] + a.chunk - 1) / a.chunk;
+  const bool in = lane < nch;
+  const float M = wave_max(in ? ml.x : -INFINITY);
+  const float w = in ? __expf(ml.x - M) : 0.f;
+  const float L = wave_sum(in ? fmaf(ml.y, w, 0.f) : 0.f);
+  const float inv_l = 1.f / L;
+  float o[DPL];
+#pragma unroll
+  for (int q = 0; q < DPL; ++q) o[q] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= nch) break;  // wave-uniform
+    const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+#pragma unroll
+    for (int q = 0; q < DPL; ++q) o[q] = fmaf(v[j][q], wj, o[q]);
+  }
+  const int64_t oi = ((int64_t)t * a.H + h) * HD + lane * DPL;
+#pragma unroll
+  for (int q = 0; q < DPL; ++q) {
+    const float r = (0.f + o[q]) * inv_l;
+    if (a.out) a.out[oi + q] = r;
+    if (a.out_hi) split_bf16(r, a.out_hi[oi + q], a.out_lo[oi + q]);
+  }
+}
+
 template <int HD, int NTH>
 static void merge_launch(const AttnArgs& a, dim3 grid, hipStream_t s) {
   const int per = (a.n_chunks + NTH / HD - 1) / (NTH / HD);  // splits per thread group
@@ -1003,6 +1056,13 @@ hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s) {
   if (a.n_chunks > kMergeMaxSplits) return hipErrorInvalidValue;
   const dim3 grid(a.H, a.T);
   const bool wide = a.n_chunks > 8;
+  // many pairs, few splits, every token merged (the prefill): one wave per pair
+  if (a.merge_single && a.n_chunks <= 8 && (a.hd == 64 || a.hd == 128) && (int64_t)a.T * a.H >= 1024) {
+    const unsigned blocks = (unsigned)(((int64_t)a.T * a.H + 3) / 4);
+    if (a.hd == 128) attn_merge_wave_kernel<128><<<blocks, 256, 0, s>>>(a);
+    else attn_merge_wave_kernel<64><<<blocks, 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
   switch (a.hd) {
     case 16:
       if (wide) merge_launch<16, 256>(a, grid, s);
