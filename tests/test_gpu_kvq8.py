@@ -89,9 +89,9 @@ def test_import_then_decode():
 
 def test_import_long_context_own_rows():
     """20000 imported positions (8 KV heads of 128, 2 query heads each),
-    then three single-token steps: 1024-cell chunks (the largest a block
-    stages), the token's own K/V rows quantized by the block whose partial
-    last chunk holds its cell, 20 chunks merged."""
+    then three single-token steps: 1024-cell chunks, the token's own K/V
+    rows quantized by the block whose partial last chunk holds its cell, 20
+    chunks merged."""
     import transformer_decode_forward_amd as tdf
     from transformer_decode_forward_amd.device import to_device
     cfg0 = dict(SMALL, n_embd=256, n_head=16, n_head_kv=8, head_dim=128, n_ff=256, seed=77)

@@ -1010,7 +1010,7 @@ extern "C" int32_t tdf_decode(tdf_context* c, const tdf_batch* b) {
         chunk = std::max(64, (chunk + 63) / 64 * 64);
         const int64_t heads = (int64_t)T * c->m->hp.n_head_kv;
         if (attn_decode_on_mfma(c->kv_dtype, c->m->hp.head_dim)) {
-          // matrix-core kernel: about 256 blocks in all, 128..1024 cells each
+          // matrix-core kernel: about 256 blocks in all, 128..2048 cells each
           // (measured best from one sequence at 2k to 32 sequences at 8k)
           const int64_t want = (nmax * heads + 255) / 256;
           int ch = 128;
