@@ -64,6 +64,27 @@ def test_lock_step_sequences_own_rows():
     run_pair(cfg, w, dict(n_ctx=2048, n_ubatch=64, n_seq_max=16), calls, TOL_BF16, "q8_0", "kvq8-lockstep")
 
 
+def test_graph_key_tracks_own_rows():
+    """Steps of the same shape (3 tokens, every row's logits, three list
+    writes) that alternate between one token per sequence (the decode
+    attention quantizes the tokens' own rows) and two tokens of one sequence
+    (the separate quantization pass): replayed launch sequences must follow
+    the difference."""
+    cfg, w = make_weights(SMALL64)
+    calls = [dict(tokens=tdf_synth.prompt(cfg, 60 + q, 30 + 10 * q), seq_ids=[[q]] * (30 + 10 * q)) for q in range(3)]
+    for k in range(6):
+        seqs = [[0], [1], [2]] if k % 2 == 0 else [[0], [0], [1]]
+        calls.append(dict(tokens=[int(x) for x in tdf_synth.prompt(cfg, 90 + k, 3)], seq_ids=seqs,
+                          logits=np.ones(3, dtype=np.int8)))
+    log("q8 cache: alternating own-row and shared-sequence steps")
+    gc, _ = run_pair(cfg, w, dict(n_ctx=512, n_ubatch=64, n_seq_max=4), calls, TOL_BF16, "q8_0", "kvq8-graph-own-rows")
+    # captured: the 30-token prompt, the first step of each kind; replayed:
+    # the other four steps (one key per kind: without the own-row flag in
+    # the key a shared-sequence step would replay the own-row graph, and
+    # there would be 2 captures)
+    assert gc.graph_counts() == (3, 4), gc.graph_counts()
+
+
 def test_import_then_decode():
     """300 positions of float32 N(0,1) rows imported (quantized on both sides
     by the same rule from the same values), then decode steps."""
