@@ -116,6 +116,7 @@ hipError_t launch_embed(const void* table, int weight_dtype, int n_rows, const i
   return hipGetLastError();
 }
 
+template <int P>
 __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ x,
                                                       const float* __restrict__ g, int d, float eps,
                                                       float* __restrict__ out_f32,
@@ -125,16 +126,17 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
   const int t = blockIdx.x;
   const float* xr = x + (int64_t)t * d;
   const int64_t ro = (int64_t)t * d;
-  if ((d & 3) == 0 && d <= 8 * 1024) {
-    // rows of up to 8192: the row stays in registers between the two passes;
-    // loads are clamped and masked by a multiply (no loads under branches)
-    constexpr int P = 8;  // float4 per thread
-    float4 xv[P];
+  if ((d & 3) == 0 && d <= P * 1024) {
+    // rows of up to 1024 P: the row stays in registers between the two
+    // passes, and the gains are requested with it; loads are clamped and
+    // masked by a multiply (no loads under branches)
+    float4 xv[P], gv[P];
     float ss = 0.f;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int k = threadIdx.x * 4 + p * 1024;
       const float4 v = *(const float4*)(xr + min(k, d - 4));
+      gv[p] = *(const float4*)(g + min(k, d - 4));
       const float on = k < d ? 1.f : 0.f;
       xv[p] = make_float4(v.x * on, v.y * on, v.z * on, v.w * on);
       ss += xv[p].x * xv[p].x + xv[p].y * xv[p].y + xv[p].z * xv[p].z + xv[p].w * xv[p].w;
@@ -148,8 +150,7 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float* __restrict__ 
     for (int p = 0; p < P; ++p) {
       const int k = threadIdx.x * 4 + p * 1024;
       if (k >= d) break;
-      const float4 gv = *(const float4*)(g + k);
-      const float v[4] = {xv[p].x * r * gv.x, xv[p].y * r * gv.y, xv[p].z * r * gv.z, xv[p].w * r * gv.w};
+      const float v[4] = {xv[p].x * r * gv[p].x, xv[p].y * r * gv[p].y, xv[p].z * r * gv[p].z, xv[p].w * r * gv[p].w};
       if (out_f32) *(float4*)(out_f32 + ro + k) = make_float4(v[0], v[1], v[2], v[3]);
       if (out_hi) {
         uint16_t h[4], l[4];
@@ -179,7 +180,10 @@ hipError_t launch_rmsnorm(const float* x, const float* g, int T, int d, float ep
                           uint16_t* out_hi, uint16_t* out_lo, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if ((out_hi == nullptr) != (out_lo == nullptr)) return hipErrorInvalidValue;
-  rmsnorm_kernel<<<T, 256, 0, s>>>(x, g, d, eps, out_f32, out_hi, out_lo);
+  // float4 per thread: 4 for rows of up to 4096 (no clamped duplicate
+  // requests), else 8
+  if (d <= 4 * 1024) rmsnorm_kernel<4><<<T, 256, 0, s>>>(x, g, d, eps, out_f32, out_hi, out_lo);
+  else rmsnorm_kernel<8><<<T, 256, 0, s>>>(x, g, d, eps, out_f32, out_hi, out_lo);
   return hipGetLastError();
 }
 
